@@ -1,0 +1,224 @@
+"""Benchmark of the Beam MoE block on one MI355X.
+
+A step is one forward of the whole block (router, permutation, experts,
+combine) over one batch of synthetic tokens already resident in HBM.  The
+default workload is the Beam-shape decode layer (64 bf16 tokens, hidden 5120,
+256 experts in 8 groups of 32, top-4 groups, top-8 experts, SwiGLU 2560).
+
+Prints one JSON line: throughput (tokens/s), the dominant kernel's roofline
+(its average duration from HIP events recorded around it on its own stream
+inside the timed region) and the CPU oracle timed on a bounded sample of the
+same workload on this host's cores.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + % of roofline (MFMA prefill, HBM GB/s decode), 1 GPU"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5033.2        # MI355X dense fp8 MFMA
+FP32_PEAK_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode64")
+    ap.add_argument("--path", choices=["auto", "stream", "grouped"], default="auto")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_bytes_flops(name, T, S, H, I, E, touched, wbytes):
+    """Algorithmic bytes and flops of one launch of a kernel.  Weights of
+    touched experts are read once; activations once; outputs written once."""
+    if name in ("stream_gate_up_bf16", "grouped_gate_up_bf16", "gate_up_fp8"):
+        return (touched * 2 * I * H * wbytes + T * H * 2 + S * I * 2,
+                2.0 * S * 2 * I * H)
+    if name in ("stream_down_bf16", "grouped_down_bf16", "down_fp8"):
+        ybytes = 4 if name.startswith("stream") else 2
+        return (touched * H * I * wbytes + S * I * 2 + S * H * ybytes,
+                2.0 * S * H * I)
+    return None, None
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src):
+        return None
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    return rec["bytes_per_launch"] if h == rec["source_sha256"] else None
+
+
+def cpu_baseline(inp, shape, seconds):
+    """The oracle (logits, routing, experts, combine in binary64) on a bounded
+    sample of the workload's tokens, all host threads."""
+    import numpy as np
+    import torch
+    import oracle
+
+    T = inp.x.shape[0]
+    rng = np.random.default_rng(0)
+
+    def run(tokens):
+        t0 = time.perf_counter()
+        xs = inp.x[torch.as_tensor(tokens, device=inp.x.device)].cpu()
+        lg = oracle.logits(shape, xs, inp.w_router).astype(np.float32)
+        idx, w, _ = oracle.route(shape, lg, inp.bias.cpu().numpy())
+        need = np.unique(idx)
+        remap = np.full(shape.n_experts, -1, np.int64)
+        remap[need] = np.arange(need.size)
+        sel = torch.as_tensor(need, device=inp.x.device)
+        wgu = inp.w_gate_up.index_select(0, sel).cpu()
+        wd = inp.w_down.index_select(0, sel).cpu()
+        sgu = sd = None
+        if inp.s_gate_up is not None:
+            sgu = inp.s_gate_up.index_select(0, sel).cpu()
+            sd = inp.s_down.index_select(0, sel).cpu()
+        t1 = time.perf_counter()
+        oracle.forward_tokens(shape, np.arange(len(tokens)), xs,
+                              remap[idx].astype(np.int32), w, wgu, wd, sgu, sd,
+                              act_quant=sgu is not None)
+        t2 = time.perf_counter()
+        return (t1 - t0) + (t2 - t1), t1 - t0
+
+    threads = oracle.max_threads()
+    probe = rng.choice(T, min(T, threads), replace=False)
+    t_probe, _ = run(probe)
+    per_tok = t_probe / len(probe)
+    n = int(max(len(probe), min(T, seconds / max(per_tok, 1e-9))))
+    n = max(threads, (n // threads) * threads) if n >= threads else n
+    toks = rng.choice(T, min(n, T), replace=False)
+    t, t_copy = run(toks)
+    return {"value": len(toks) / t, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(toks)} of {T} tokens (random, seed 0): binary64 "
+                      f"logits, routing, {shape.top_k} SwiGLU experts and "
+                      f"combine per token; {t:.1f} s wall incl. {t_copy:.1f} s "
+                      f"of host copies of the touched experts"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported: "
+              "this build has no multi-GPU path (the block runs whole on one "
+              "MI355X).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import group_limited_routing_sigmoid_amd as gl
+    from synth import WORKLOADS, make_inputs, FP8
+
+    w = WORKLOADS[a.workload]
+    sh = w.shape
+    dev = torch.device("cuda:0")
+    inp = make_inputs(w, device=dev)
+    T, H, I, E, K = inp.x.shape[0], sh.hidden, sh.intermediate, sh.n_experts, sh.top_k
+    S = T * K
+    flags = {"auto": 0, "stream": gl.PATH_STREAM, "grouped": gl.PATH_GROUPED}[a.path]
+    wdt = gl.FP8_E4M3 if w.weight_dtype == FP8 else (
+        gl.F32 if w.weight_dtype == "f32" else gl.BF16)
+    act = gl.F32 if w.act_dtype == "f32" else gl.BF16
+    d = gl.make_desc(sh, act, wdt, flags)
+    ws = gl.Workspace(dev)
+    out = torch.empty(T, H, dtype=inp.x.dtype, device=dev)
+
+    def step(timer=None):
+        gl.forward(d, inp.x, inp.w_router, inp.bias, inp.w_gate_up, inp.w_down,
+                   inp.s_gate_up, inp.s_down, out=out, workspace=ws, timer=timer)
+
+    # routing statistics of this batch (touched experts set the byte count)
+    idx, _, _ = gl.route(d, inp.x, inp.w_router, inp.bias, workspace=ws)
+    counts = torch.bincount(idx.flatten().long(), minlength=E).cpu().numpy()
+    touched = int((counts > 0).sum())
+    for _ in range(a.warmup):
+        step()
+    timer = gl.Timer(capacity=64 * max(a.steps, 1))
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(a.steps):
+        step(timer)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / a.steps
+    per = {}
+    for name, kms in timer.records():
+        per.setdefault(name, []).append(kms)
+    kern_ms = {k: sum(v) / len(v) for k, v in per.items()}
+    launches = {k: len(v) / a.steps for k, v in per.items()}
+    dom = max(kern_ms, key=lambda k: kern_ms[k] * launches[k])
+    wbytes = 1 if w.weight_dtype == FP8 else (4 if w.weight_dtype == "f32" else 2)
+    kb, kf = kernel_bytes_flops(dom, T, S, H, I, E, touched, wbytes)
+    mem_bound = S <= 16 * E
+    if mem_bound or kf is None:
+        ach = kb / (kern_ms[dom] * 1e-3) / 1e9 if kb else None
+        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS if ach else None,
+                "traffic": traffic_for(dom, a.workload), "kernel": dom,
+                "kernel_ms": kern_ms[dom], "algorithmic_bytes": kb}
+    else:
+        peak = FP8_PEAK_TFLOPS if w.weight_dtype == FP8 else BF16_PEAK_TFLOPS
+        ach = kf / (kern_ms[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                "frac": ach / peak, "traffic": traffic_for(dom, a.workload),
+                "kernel": dom, "kernel_ms": kern_ms[dom], "algorithmic_flops": kf}
+    layer_bytes = touched * 3 * H * I * wbytes + E * H * 4 + 2 * T * H * inp.x.element_size()
+    layer_flops = 2.0 * S * 3 * H * I
+    res = {
+        "metric": METRIC,
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"fp8": "fp8", "f32": "f32"}.get(w.weight_dtype, "bf16"),
+        "data": "synthetic",
+        "config": {"workload": a.workload, "tokens": T, "hidden": H,
+                   "intermediate": I, "experts": E, "groups": sh.n_groups,
+                   "topk_groups": sh.topk_groups, "top_k": K,
+                   "routed_scale": sh.routed_scale, "path": a.path,
+                   "weights": w.weight_dtype, "bias": w.bias, "seed": w.seed},
+        "roofline": roof,
+        "layer": {"hbm_GBps": layer_bytes / (ms * 1e-3) / 1e9,
+                  "hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                  "mfma_TFLOPs": layer_flops / (ms * 1e-3) / 1e12,
+                  "mfma_frac": layer_flops / (ms * 1e-3) / 1e12 / (
+                      FP8_PEAK_TFLOPS if w.weight_dtype == FP8 else BF16_PEAK_TFLOPS),
+                  "algorithmic_bytes": layer_bytes, "expert_flops": layer_flops},
+        "routing": {"touched_experts": touched,
+                    "max_over_mean_load": float(counts.max() / counts.mean())},
+        "kernels_ms": kern_ms,
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, sh, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,350 @@
+// C ABI of the Beam MoE block library: host-side validation, workspace plan,
+// path choice and kernel launch order.  See include/beam_moe.h for the
+// contract of every entry point.
+#include <math.h>
+#include <string.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace beam {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? BEAM_OK : BEAM_ERR_HIP; }
+
+}  // namespace
+
+struct Timer {
+  int32_t capacity = 0, count = 0;
+  bool open = false;         // a begin without its end yet
+  hipEvent_t* ev = nullptr;  // 2 * capacity events: start, stop pairs
+  const char** names = nullptr;
+};
+
+void timer_begin(Timer* t, const char* name, hipStream_t s) {
+  if (!t || t->count >= t->capacity) return;
+  t->names[t->count] = name;
+  hipEventRecord(t->ev[2 * t->count], s);
+  t->open = true;
+}
+
+void timer_end(Timer* t, hipStream_t s) {
+  if (!t || !t->open) return;
+  hipEventRecord(t->ev[2 * t->count + 1], s);
+  t->open = false;
+  ++t->count;
+}
+
+int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
+  const int st = beam_moe_validate(d, T);
+  if (st != BEAM_OK) return st;
+  memset(p, 0, sizeof(*p));
+  p->H = d->hidden;
+  p->I = d->intermediate;
+  p->E = d->n_experts;
+  p->G = d->n_groups;
+  p->TG = d->topk_groups;
+  p->K = d->top_k;
+  p->topn = d->group_score_topn;
+  p->scale = d->routed_scale;
+  p->act = d->act_dtype;
+  p->wdt = d->weight_dtype;
+  p->flags = d->flags;
+  p->T = T;
+  p->S = T * d->top_k;
+  p->nb = ceil_div(T, kPermBlock);
+  // Router reduction split: enough waves to spread W_r over the chip when
+  // there are few tokens; each split must cover a multiple of 16 columns.
+  p->ks = 1;
+  if (p->act == BEAM_BF16 && p->E % 64 == 0) {
+    const int64_t waves = ceil_div(T, 32) * (p->E / 64);
+    while (p->ks < 16 && waves * p->ks < 1024 && (p->H / 16) % (2 * p->ks) == 0)
+      p->ks *= 2;
+  }
+  // Few tokens per expert: stream each touched expert's weights once.
+  if (p->flags & BEAM_PATH_STREAM)
+    p->stream_path = true;
+  else if (p->flags & BEAM_PATH_GROUPED)
+    p->stream_path = false;
+  else
+    p->stream_path = p->S <= 16 * static_cast<int64_t>(p->E);
+  if (p->wdt == BEAM_F32) p->stream_path = false;
+  const int64_t S = p->S, E = p->E, H = p->H, I = p->I;
+  p->max_tiles = S / kGemmBM + (S < E ? S : E) + 1;
+  const bool f32 = p->wdt == BEAM_F32;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  p->off_part = take(static_cast<size_t>(p->ks) * T * E * 4);
+  p->off_idx = take(S * 4);
+  p->off_w = take(S * 4);
+  p->off_hist = take(p->nb * E * 4);
+  p->off_base = take(p->nb * E * 4);
+  p->off_rank = take(S * 4);
+  p->off_counts = take(E * 4);
+  p->off_offsets = take((E + 1) * 4);
+  p->off_slot_token = take(S * 4);
+  p->off_slot_of = take(S * 4);
+  p->off_tile_expert = take(p->max_tiles * 4);
+  p->off_tile_row0 = take(p->max_tiles * 4);
+  p->off_meta = take(kMetaWords * 4);
+  p->off_active = take(E * 4);
+  p->off_h = take(S * I * (f32 ? 4 : 2));
+  p->off_y = take(S * H * ((f32 || p->stream_path) ? 4 : 2));
+  if (p->wdt == BEAM_FP8_E4M3) {
+    p->off_xq = take(T * H);
+    p->off_xs = take(T * (H / 128) * 4);
+    p->off_hq = take(S * I);
+    p->off_hs = take(S * (I / 128) * 4);
+  }
+  p->total = o;
+  return BEAM_OK;
+}
+
+}  // namespace beam
+
+using namespace beam;
+
+extern "C" {
+
+const char* beam_status_string(int status) {
+  switch (status) {
+    case BEAM_OK: return "ok";
+    case BEAM_ERR_INVALID_ARG: return "invalid argument";
+    case BEAM_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case BEAM_ERR_WORKSPACE: return "workspace missing or too small";
+    case BEAM_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int beam_moe_validate(const beam_moe_desc* d, int64_t T) {
+  if (!d || T < 0) return BEAM_ERR_INVALID_ARG;
+  const uint32_t known = BEAM_ROUTE_LOGITS_IN | BEAM_PATH_STREAM | BEAM_PATH_GROUPED;
+  if (d->flags & ~known) return BEAM_ERR_INVALID_ARG;
+  if ((d->flags & BEAM_PATH_STREAM) && (d->flags & BEAM_PATH_GROUPED))
+    return BEAM_ERR_INVALID_ARG;
+  if (d->act_dtype != BEAM_F32 && d->act_dtype != BEAM_BF16) return BEAM_ERR_INVALID_ARG;
+  if (d->weight_dtype != BEAM_F32 && d->weight_dtype != BEAM_BF16 &&
+      d->weight_dtype != BEAM_FP8_E4M3)
+    return BEAM_ERR_INVALID_ARG;
+  if (!(d->routed_scale > 0.0f) || !isfinite(d->routed_scale)) return BEAM_ERR_INVALID_ARG;
+  const int E = d->n_experts, G = d->n_groups;
+  if (E < 1 || E > 1024 || G < 1 || G > 64 || E % G) return BEAM_ERR_UNSUPPORTED;
+  const int gs = E / G;
+  if (gs > 64) return BEAM_ERR_UNSUPPORTED;
+  if (d->topk_groups < 1 || d->topk_groups > G) return BEAM_ERR_UNSUPPORTED;
+  if (d->top_k < 1 || d->top_k > 16 || d->top_k > d->topk_groups * gs)
+    return BEAM_ERR_UNSUPPORTED;
+  if (d->group_score_topn < 1 || d->group_score_topn > 2 || d->group_score_topn > gs)
+    return BEAM_ERR_UNSUPPORTED;
+  if (d->hidden < 128 || d->hidden % 128 || d->intermediate < 128 ||
+      d->intermediate % 128)
+    return BEAM_ERR_UNSUPPORTED;
+  if (d->weight_dtype == BEAM_F32 && d->act_dtype != BEAM_F32) return BEAM_ERR_UNSUPPORTED;
+  if (d->weight_dtype != BEAM_F32 && d->act_dtype != BEAM_BF16) return BEAM_ERR_UNSUPPORTED;
+  if (T * static_cast<int64_t>(d->top_k) > 0x7FFFFFFF) return BEAM_ERR_UNSUPPORTED;
+  return BEAM_OK;
+}
+
+int beam_moe_workspace_bytes(const beam_moe_desc* d, int64_t T, size_t* bytes) {
+  if (!bytes) return BEAM_ERR_INVALID_ARG;
+  Plan p;
+  const int st = make_plan(d, T, &p);
+  if (st != BEAM_OK) return st;
+  *bytes = T == 0 ? 0 : p.total;
+  return BEAM_OK;
+}
+
+int beam_moe_route(const beam_moe_desc* d, int64_t T, const void* x,
+                   const float* w_router, const float* bias, float* logits,
+                   int32_t* topk_idx, float* topk_w, void* workspace,
+                   size_t ws_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(d, T, &p);
+  if (st != BEAM_OK) return st;
+  if (T == 0) return BEAM_OK;
+  const bool lin = d->flags & BEAM_ROUTE_LOGITS_IN;
+  if (!topk_idx || !topk_w) return BEAM_ERR_INVALID_ARG;
+  if (lin ? !logits : (!x || !w_router)) return BEAM_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(bias) ||
+      !aligned16(logits) || !aligned16(topk_idx) || !aligned16(topk_w))
+    return BEAM_ERR_INVALID_ARG;
+  if (!lin) {
+    if (!workspace || ws_bytes < p.total) return BEAM_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256) return BEAM_ERR_INVALID_ARG;
+  }
+  return hip_status(launch_router(p, x, w_router, bias, lin ? nullptr : logits,
+                                  lin ? logits : nullptr, topk_idx, topk_w,
+                                  workspace, static_cast<hipStream_t>(stream),
+                                  nullptr));
+}
+
+int beam_moe_permute(const beam_moe_desc* d, int64_t T, const int32_t* topk_idx,
+                     int32_t* counts, int32_t* offsets, int32_t* slot_token,
+                     int32_t* slot_of, void* workspace, size_t ws_bytes,
+                     void* stream) {
+  Plan p;
+  int st = make_plan(d, T, &p);
+  if (st != BEAM_OK) return st;
+  if (T == 0) return BEAM_OK;
+  if (!topk_idx || !counts || !offsets || !slot_token || !slot_of)
+    return BEAM_ERR_INVALID_ARG;
+  if (!aligned16(topk_idx) || !aligned16(counts) || !aligned16(offsets) ||
+      !aligned16(slot_token) || !aligned16(slot_of))
+    return BEAM_ERR_INVALID_ARG;
+  if (!workspace || ws_bytes < p.total) return BEAM_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return BEAM_ERR_INVALID_ARG;
+  return hip_status(launch_permute(p, topk_idx, counts, offsets, slot_token,
+                                   slot_of, workspace, static_cast<hipStream_t>(stream),
+                                   nullptr));
+}
+
+int beam_moe_quant_e4m3(int64_t rows, int64_t cols, int32_t dtype,
+                        const void* v, uint8_t* q, float* scales, void* stream) {
+  if (rows < 0 || cols < 0 || (dtype != BEAM_F32 && dtype != BEAM_BF16))
+    return BEAM_ERR_INVALID_ARG;
+  if (cols % 128) return BEAM_ERR_UNSUPPORTED;
+  if (rows == 0 || cols == 0) return BEAM_OK;
+  if (!v || !q || !scales || !aligned16(v) || !aligned16(q) || !aligned16(scales))
+    return BEAM_ERR_INVALID_ARG;
+  return hip_status(launch_quant_e4m3(rows, cols, dtype, v, q, scales,
+                                      static_cast<hipStream_t>(stream), nullptr));
+}
+
+static int forward_impl(const beam_moe_desc* d, int64_t T, const void* x,
+                        const float* w_router, const float* bias,
+                        const void* w_gate_up, const float* s_gate_up,
+                        const void* w_down, const float* s_down, void* out,
+                        int32_t* topk_idx, float* topk_w, float* logits,
+                        void* workspace, size_t ws_bytes, void* stream,
+                        Timer* tm) {
+  Plan p;
+  int st = make_plan(d, T, &p);
+  if (st != BEAM_OK) return st;
+  if (T == 0) return BEAM_OK;
+  const bool lin = d->flags & BEAM_ROUTE_LOGITS_IN;
+  const bool fp8 = d->weight_dtype == BEAM_FP8_E4M3;
+  if (!x || !w_gate_up || !w_down || !out) return BEAM_ERR_INVALID_ARG;
+  if (lin ? !logits : !w_router) return BEAM_ERR_INVALID_ARG;
+  if (fp8 && (!s_gate_up || !s_down)) return BEAM_ERR_INVALID_ARG;
+  if (fp8 && !fp8_experts_built()) return BEAM_ERR_UNSUPPORTED;
+  const void* ptrs[] = {x, w_router, bias, w_gate_up, s_gate_up, w_down,
+                        s_down, out, topk_idx, topk_w, logits};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return BEAM_ERR_INVALID_ARG;
+  if (!workspace || ws_bytes < p.total) return BEAM_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return BEAM_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* idx = topk_idx ? topk_idx : ws_at<int32_t>(workspace, p.off_idx);
+  float* w = topk_w ? topk_w : ws_at<float>(workspace, p.off_w);
+  hipError_t e = launch_router(p, x, w_router, bias, lin ? nullptr : logits,
+                               lin ? logits : nullptr, idx, w, workspace, s, tm);
+  if (e != hipSuccess) return BEAM_ERR_HIP;
+  int32_t* slot_of = ws_at<int32_t>(workspace, p.off_slot_of);
+  e = launch_permute(p, idx, ws_at<int32_t>(workspace, p.off_counts),
+                     ws_at<int32_t>(workspace, p.off_offsets),
+                     ws_at<int32_t>(workspace, p.off_slot_token), slot_of,
+                     workspace, s, tm);
+  if (e != hipSuccess) return BEAM_ERR_HIP;
+  if (p.wdt == BEAM_F32)
+    e = launch_experts_f32(p, static_cast<const float*>(x),
+                           static_cast<const float*>(w_gate_up),
+                           static_cast<const float*>(w_down), workspace, s, tm);
+  else if (fp8)
+    e = launch_experts_fp8(p, x, static_cast<const uint8_t*>(w_gate_up), s_gate_up,
+                           static_cast<const uint8_t*>(w_down), s_down, workspace, s, tm);
+  else if (p.stream_path)
+    e = launch_stream_bf16(p, x, w_gate_up, w_down, workspace, s, tm);
+  else
+    e = launch_grouped_bf16(p, x, w_gate_up, w_down, workspace, s, tm);
+  if (e != hipSuccess) return BEAM_ERR_HIP;
+  return hip_status(launch_combine(p, slot_of, w, out, workspace, s, tm));
+}
+
+int beam_moe_forward(const beam_moe_desc* d, int64_t T, const void* x,
+                     const float* w_router, const float* bias,
+                     const void* w_gate_up, const float* s_gate_up,
+                     const void* w_down, const float* s_down, void* out,
+                     int32_t* topk_idx, float* topk_w, float* logits,
+                     void* workspace, size_t ws_bytes, void* stream) {
+  return forward_impl(d, T, x, w_router, bias, w_gate_up, s_gate_up, w_down,
+                      s_down, out, topk_idx, topk_w, logits, workspace,
+                      ws_bytes, stream, nullptr);
+}
+
+int beam_moe_forward_timed(const beam_moe_desc* d, int64_t T, const void* x,
+                           const float* w_router, const float* bias,
+                           const void* w_gate_up, const float* s_gate_up,
+                           const void* w_down, const float* s_down, void* out,
+                           int32_t* topk_idx, float* topk_w, float* logits,
+                           void* workspace, size_t ws_bytes, void* stream,
+                           beam_moe_timer* timer) {
+  return forward_impl(d, T, x, w_router, bias, w_gate_up, s_gate_up, w_down,
+                      s_down, out, topk_idx, topk_w, logits, workspace,
+                      ws_bytes, stream, reinterpret_cast<Timer*>(timer));
+}
+
+int beam_moe_timer_create(int32_t capacity, beam_moe_timer** out) {
+  if (!out) return BEAM_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (capacity < 1) return BEAM_ERR_INVALID_ARG;
+  Timer* t = new Timer;
+  t->capacity = capacity;
+  t->ev = new hipEvent_t[2 * static_cast<size_t>(capacity)]();
+  t->names = new const char*[capacity]();
+  for (int32_t i = 0; i < 2 * capacity; ++i)
+    if (hipEventCreate(&t->ev[i]) != hipSuccess) {
+      for (int32_t j = 0; j < i; ++j) hipEventDestroy(t->ev[j]);
+      delete[] t->ev;
+      delete[] t->names;
+      delete t;
+      return BEAM_ERR_HIP;
+    }
+  *out = reinterpret_cast<beam_moe_timer*>(t);
+  return BEAM_OK;
+}
+
+void beam_moe_timer_destroy(beam_moe_timer* timer) {
+  Timer* t = reinterpret_cast<Timer*>(timer);
+  if (!t) return;
+  for (int32_t i = 0; i < 2 * t->capacity; ++i) hipEventDestroy(t->ev[i]);
+  delete[] t->ev;
+  delete[] t->names;
+  delete t;
+}
+
+void beam_moe_timer_reset(beam_moe_timer* timer) {
+  Timer* t = reinterpret_cast<Timer*>(timer);
+  if (t) {
+    t->count = 0;
+    t->open = false;
+  }
+}
+
+int32_t beam_moe_timer_count(const beam_moe_timer* timer) {
+  const Timer* t = reinterpret_cast<const Timer*>(timer);
+  return t ? t->count : 0;
+}
+
+int beam_moe_timer_read(beam_moe_timer* timer, int32_t i, const char** name,
+                        float* ms) {
+  Timer* t = reinterpret_cast<Timer*>(timer);
+  if (!t || i < 0 || i >= t->count || !name || !ms) return BEAM_ERR_INVALID_ARG;
+  if (hipEventSynchronize(t->ev[2 * i + 1]) != hipSuccess) return BEAM_ERR_HIP;
+  if (hipEventElapsedTime(ms, t->ev[2 * i], t->ev[2 * i + 1]) != hipSuccess)
+    return BEAM_ERR_HIP;
+  *name = t->names[i];
+  return BEAM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,172 @@
+// Expert MLPs for decode-sized batches: each touched expert sees only a few
+// tokens, so the work is bound by reading its weights once from HBM.  The
+// weights are the 16-row A side of 16x16x32 bf16 MFMA and up to 16 tokens
+// are the B side; the reduction over the hidden (or intermediate) dimension
+// is split over the 4 waves of a workgroup and summed in LDS in a fixed
+// order.  Experts with more than 16 tokens are handled in chunks of 16.
+//
+// Same SwiGLU expert as the grouped path ("Hugging Face releases Beam ..."
+// MoE paragraph): h = silu(x W_g^T) * (x W_u^T) for gate/up, y = h W_d^T for
+// down.  h is kept in bf16 (the down product's input); y in fp32.
+//
+// Work items: (active expert j, 16-channel block) for gate/up and (active
+// expert j, 32-row block of W_d) for down.  The grid covers every expert
+// that could be active; items past the device-side count exit at once, so
+// the host never waits for the routing result.
+#include "common.h"
+#include "internal.h"
+
+namespace beam {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kUnroll = 8;   // k-steps of 32 in flight per wave
+
+// grid (max_active * I/16), block 256
+__global__ __launch_bounds__(kThreads) void stream_gate_up(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_gu,
+    uint16_t* __restrict__ h, const int32_t* __restrict__ slot_token,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ active, const int32_t* __restrict__ meta,
+    int H, int I) {
+  __shared__ f32x4 red[kWaves][2][kWave];
+  const int n_cb = I / 16;
+  const int j = blockIdx.x / n_cb;
+  const int cb = blockIdx.x % n_cb;
+  if (j >= meta[kMetaActive]) return;
+  const int e = active[j];
+  const int off = offsets[e], cnt = counts[e];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int kw = H / kWaves;  // columns per wave
+  const int kofs = wave * kw + 8 * (lane / 16);
+  const uint16_t* wg = w_gu + (static_cast<int64_t>(e) * 2 * I + cb * 16 + lane % 16) * H + kofs;
+  const uint16_t* wu = wg + static_cast<int64_t>(I) * H;
+
+  for (int c0 = 0; c0 < cnt; c0 += 16) {
+    const int ntok = min(16, cnt - c0);
+    const bool has_tok = (lane % 16) < ntok;
+    const uint16_t* xr = x + (has_tok ? static_cast<int64_t>(slot_token[off + c0 + lane % 16]) * H : 0) + kofs;
+    f32x4 ag = {}, au = {};
+    for (int k = 0; k < kw; k += 32 * kUnroll) {
+      u32x4 ga[kUnroll], ua[kUnroll], xb[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const bool in = k + 32 * u < kw;
+        ga[u] = in ? ld16(wg + k + 32 * u) : u32x4{0, 0, 0, 0};
+        ua[u] = in ? ld16(wu + k + 32 * u) : u32x4{0, 0, 0, 0};
+        xb[u] = (in && has_tok) ? ld16(xr + k + 32 * u) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        ag = mfma16x16x32(as_bf16x8(ga[u]), as_bf16x8(xb[u]), ag);
+        au = mfma16x16x32(as_bf16x8(ua[u]), as_bf16x8(xb[u]), au);
+      }
+    }
+    red[wave][0][lane] = ag;
+    red[wave][1][lane] = au;
+    __syncthreads();
+    if (wave == 0) {
+      f32x4 g = red[0][0][lane], u = red[0][1][lane];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) {
+        g += red[w][0][lane];
+        u += red[w][1][lane];
+      }
+      if (has_tok) {
+        // element r: channel cb*16 + 4*(lane/16) + r, token lane%16
+        uint16_t* hr = h + static_cast<int64_t>(off + c0 + lane % 16) * I + cb * 16 + 4 * (lane / 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hr[r] = f32_to_bf16_bits(silu(g[r]) * u[r]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// grid (max_active * H/32), block 256
+__global__ __launch_bounds__(kThreads) void stream_down(
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ w_d,
+    float* __restrict__ y, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
+    const int32_t* __restrict__ meta, int H, int I) {
+  __shared__ f32x4 red[kWaves][2][kWave];
+  const int n_ob = H / 32;
+  const int j = blockIdx.x / n_ob;
+  const int ob = blockIdx.x % n_ob;
+  if (j >= meta[kMetaActive]) return;
+  const int e = active[j];
+  const int off = offsets[e], cnt = counts[e];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int kw = I / kWaves;
+  const int kofs = wave * kw + 8 * (lane / 16);
+  const uint16_t* w0 = w_d + (static_cast<int64_t>(e) * H + ob * 32 + lane % 16) * I + kofs;
+  const uint16_t* w1 = w0 + static_cast<int64_t>(16) * I;
+
+  for (int c0 = 0; c0 < cnt; c0 += 16) {
+    const int ntok = min(16, cnt - c0);
+    const bool has_tok = (lane % 16) < ntok;
+    const uint16_t* hr = h + static_cast<int64_t>(off + c0 + (has_tok ? lane % 16 : 0)) * I + kofs;
+    f32x4 a0 = {}, a1 = {};
+    for (int k = 0; k < kw; k += 32 * kUnroll) {
+      u32x4 wa[kUnroll], wb[kUnroll], hb[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const bool in = k + 32 * u < kw;
+        wa[u] = in ? ld16(w0 + k + 32 * u) : u32x4{0, 0, 0, 0};
+        wb[u] = in ? ld16(w1 + k + 32 * u) : u32x4{0, 0, 0, 0};
+        hb[u] = (in && has_tok) ? ld16(hr + k + 32 * u) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        a0 = mfma16x16x32(as_bf16x8(wa[u]), as_bf16x8(hb[u]), a0);
+        a1 = mfma16x16x32(as_bf16x8(wb[u]), as_bf16x8(hb[u]), a1);
+      }
+    }
+    red[wave][0][lane] = a0;
+    red[wave][1][lane] = a1;
+    __syncthreads();
+    if (wave == 0) {
+      f32x4 r0 = red[0][0][lane], r1 = red[0][1][lane];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) {
+        r0 += red[w][0][lane];
+        r1 += red[w][1][lane];
+      }
+      if (has_tok) {
+        float* yr = y + static_cast<int64_t>(off + c0 + lane % 16) * H + ob * 32 + 4 * (lane / 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          yr[r] = r0[r];
+          yr[16 + r] = r1[r];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_stream_bf16(const Plan& p, const void* x,
+                              const void* w_gate_up, const void* w_down,
+                              void* ws, hipStream_t s, Timer* tm) {
+  const int32_t* slot_token = ws_at<int32_t>(ws, p.off_slot_token);
+  const int32_t* counts = ws_at<int32_t>(ws, p.off_counts);
+  const int32_t* offsets = ws_at<int32_t>(ws, p.off_offsets);
+  const int32_t* active = ws_at<int32_t>(ws, p.off_active);
+  const int32_t* meta = ws_at<int32_t>(ws, p.off_meta);
+  uint16_t* h = ws_at<uint16_t>(ws, p.off_h);
+  float* y = ws_at<float>(ws, p.off_y);
+  const int64_t max_active = p.S < p.E ? p.S : p.E;
+  BEAM_LAUNCH(tm, "stream_gate_up_bf16", stream_gate_up, dim3(static_cast<unsigned>(max_active * (p.I / 16))),
+                     dim3(kThreads), 0, s, static_cast<const uint16_t*>(x),
+                     static_cast<const uint16_t*>(w_gate_up), h, slot_token,
+                     counts, offsets, active, meta, p.H, p.I);
+  BEAM_LAUNCH(tm, "stream_down_bf16", stream_down, dim3(static_cast<unsigned>(max_active * (p.H / 32))),
+                     dim3(kThreads), 0, s, h, static_cast<const uint16_t*>(w_down),
+                     y, counts, offsets, active, meta, p.H, p.I);
+  return hipGetLastError();
+}
+
+}  // namespace beam

@@ -1,0 +1,146 @@
+// Token permutation between the router and the experts: every token goes to
+// K of the E experts ("Beam Turns Frontier-Scale Openness Into an
+// Infrastructure Decision", section "Sparse compute still requires dense
+// planning"), so the T*K (token, expert) assignments are grouped by expert
+// before the expert matrix products.  Integer work only; the result is a
+// stable counting sort (slots of one expert in increasing token order), so it
+// is identical on every run.
+//
+//   perm_rank     per block of 256 tokens: a [E x 256] bit matrix in LDS
+//                 (bit t of row e set when token t chose e); per-block expert
+//                 histogram = row popcounts; rank of (t, e) inside the block
+//                 = popcount of row e below bit t.
+//   perm_scan     one block: per-expert prefix over blocks, counts, offsets,
+//                 grouped-GEMM M-tile list and the list of active experts.
+//   perm_scatter  slot = offsets[e] + block base + rank.
+#include "common.h"
+#include "internal.h"
+
+namespace beam {
+namespace {
+
+constexpr int kMaxE = 1024;
+constexpr int kWords = kPermBlock / 32;
+
+__global__ __launch_bounds__(kPermBlock) void perm_rank(
+    const int32_t* __restrict__ idx, int64_t T, int K, int E,
+    int32_t* __restrict__ hist, int32_t* __restrict__ rank) {
+  __shared__ uint32_t bits[kMaxE * kWords];
+  const int lt = threadIdx.x;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kPermBlock + lt;
+  for (int i = lt; i < E * kWords; i += kPermBlock) bits[i] = 0;
+  __syncthreads();
+  if (t < T)
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[t * K + k];
+      atomicOr(&bits[e * kWords + lt / 32], 1u << (lt % 32));
+    }
+  __syncthreads();
+  for (int e = lt; e < E; e += kPermBlock) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kWords; ++w) c += __popc(bits[e * kWords + w]);
+    hist[static_cast<int64_t>(blockIdx.x) * E + e] = c;
+  }
+  if (t < T)
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[t * K + k];
+      int r = __popc(bits[e * kWords + lt / 32] & ((1u << (lt % 32)) - 1u));
+      for (int w = 0; w < lt / 32; ++w) r += __popc(bits[e * kWords + w]);
+      rank[t * K + k] = r;
+    }
+}
+
+// Inclusive scan of v over the 1024 threads of the block (Hillis-Steele).
+__device__ int block_scan_incl(int v, int* sh) {
+  const int i = threadIdx.x;
+  sh[i] = v;
+  __syncthreads();
+  for (int off = 1; off < kMaxE; off <<= 1) {
+    const int a = (i >= off) ? sh[i - off] : 0;
+    __syncthreads();
+    sh[i] += a;
+    __syncthreads();
+  }
+  const int r = sh[i];
+  __syncthreads();
+  return r;
+}
+
+// one block of 1024 threads; thread e handles expert e
+__global__ __launch_bounds__(kMaxE) void perm_scan(
+    const int32_t* __restrict__ hist, int64_t nb, int E, int bm,
+    int32_t* __restrict__ base, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ tile_expert,
+    int32_t* __restrict__ tile_row0, int32_t* __restrict__ meta,
+    int32_t* __restrict__ active) {
+  __shared__ int sh[kMaxE];
+  const int e = threadIdx.x;
+  int c = 0;
+  if (e < E)
+    for (int64_t b = 0; b < nb; ++b) {
+      base[b * E + e] = c;
+      c += hist[b * E + e];
+    }
+  const int incl = block_scan_incl(c, sh);
+  const int off = incl - c;
+  const int nt = (c + bm - 1) / bm;
+  const int tincl = block_scan_incl(nt, sh);
+  const int toff = tincl - nt;
+  const int act = c > 0;
+  const int aincl = block_scan_incl(act, sh);
+  if (e < E) {
+    counts[e] = c;
+    offsets[e] = off;
+    for (int i = 0; i < nt; ++i) {
+      tile_expert[toff + i] = e;
+      tile_row0[toff + i] = off + i * bm;
+    }
+    if (act) active[aincl - 1] = e;
+  }
+  if (e == E - 1) {
+    offsets[E] = incl;
+    meta[kMetaTiles] = tincl;
+    meta[kMetaActive] = aincl;
+  }
+}
+
+__global__ __launch_bounds__(kPermBlock) void perm_scatter(
+    const int32_t* __restrict__ idx, int64_t T, int K, int E,
+    const int32_t* __restrict__ base, const int32_t* __restrict__ rank,
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ slot_token,
+    int32_t* __restrict__ slot_of) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kPermBlock + threadIdx.x;
+  if (t >= T) return;
+  for (int k = 0; k < K; ++k) {
+    const int e = idx[t * K + k];
+    const int slot = offsets[e] + base[static_cast<int64_t>(blockIdx.x) * E + e] +
+                     rank[t * K + k];
+    slot_token[slot] = static_cast<int32_t>(t);
+    slot_of[t * K + k] = slot;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const Plan& p, const int32_t* idx, int32_t* counts,
+                          int32_t* offsets, int32_t* slot_token,
+                          int32_t* slot_of, void* ws, hipStream_t s, Timer* tm) {
+  int32_t* hist = ws_at<int32_t>(ws, p.off_hist);
+  int32_t* base = ws_at<int32_t>(ws, p.off_base);
+  int32_t* rank = ws_at<int32_t>(ws, p.off_rank);
+  const unsigned nb = static_cast<unsigned>(p.nb);
+  BEAM_LAUNCH(tm, "perm_rank", perm_rank, dim3(nb), dim3(kPermBlock), 0, s, idx, p.T,
+                     p.K, p.E, hist, rank);
+  BEAM_LAUNCH(tm, "perm_scan", perm_scan, dim3(1), dim3(kMaxE), 0, s, hist, p.nb, p.E,
+                     kGemmBM, base, counts, offsets,
+                     ws_at<int32_t>(ws, p.off_tile_expert),
+                     ws_at<int32_t>(ws, p.off_tile_row0),
+                     ws_at<int32_t>(ws, p.off_meta),
+                     ws_at<int32_t>(ws, p.off_active));
+  BEAM_LAUNCH(tm, "perm_scatter", perm_scatter, dim3(nb), dim3(kPermBlock), 0, s, idx, p.T,
+                     p.K, p.E, base, rank, offsets, slot_token, slot_of);
+  return hipGetLastError();
+}
+
+}  // namespace beam

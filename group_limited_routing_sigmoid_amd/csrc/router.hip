@@ -1,0 +1,305 @@
+// Router of the Beam MoE block on gfx950.
+//
+// The router computes sigmoid scores over the experts, adds a per-expert bias
+// used only to choose experts, keeps the best groups, picks the top-K experts
+// inside them and normalises their unbiased scores to sum to the routed scale
+// ("Reflection Releases Beam: An Open 501B-Parameter MoE Model Under Apache
+// 2.0", section "Where Beam Saves and Where the Memory Bill Comes In";
+// "Hugging Face releases Beam ..." MoE paragraph; bias from the
+// load-balancing paragraph of "Reflection AI Introduces Beam ...").  The
+// group score is the sum of a group's best two biased scores, DeepSeek-V3's
+// rule (arXiv 2412.19437, section 2.1.2), which the pages invoke.
+//
+// Two kernels:
+//   router_logits_*  logits = x W_r^T in fp32.  With bf16 activations the
+//                    fp32 router weights are split exactly into three bf16
+//                    terms (hi + mid + lo), so every product is exact and the
+//                    matrix cores accumulate in fp32.  The reduction over H
+//                    may be split into `ks` partial sums for parallelism.
+//   router_select    one wavefront per token: sums the partials in a fixed
+//                    order, then routes in binary32 exactly as specified
+//                    (sigmoid from a fixed binary64 evaluation, ties to the
+//                    lower index), so indices and weights are bitwise
+//                    reproducible from the fp32 logits.
+//
+// This translation unit is compiled with -ffp-contract=off.
+#include "common.h"
+#include "internal.h"
+
+namespace beam {
+namespace {
+
+// ---- logits: bf16 activations, bf16x3 split of fp32 weights, MFMA -------
+
+__device__ __forceinline__ void split3(const float* w, bf16x8& hi, bf16x8& mid,
+                                       bf16x8& lo) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float v = w[j];
+    const bf16 h = static_cast<bf16>(v);
+    const float r1 = v - static_cast<float>(h);
+    const bf16 m = static_cast<bf16>(r1);
+    const float r2 = r1 - static_cast<float>(m);
+    hi[j] = h;
+    mid[j] = m;
+    lo[j] = static_cast<bf16>(r2);
+  }
+}
+
+// grid (ceil(T/32), E/64, ks), one wave: 32 tokens x 64 experts over
+// columns [z*kchunk, (z+1)*kchunk) of H.
+__global__ __launch_bounds__(64) void router_logits_mfma(
+    const uint16_t* __restrict__ x, const float* __restrict__ wr,
+    float* __restrict__ part, int64_t T, int H, int E, int kchunk) {
+  const int lane = threadIdx.x;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 32;
+  const int e0 = blockIdx.y * 64;
+  const int z = blockIdx.z;
+  const int kb = z * kchunk + 8 * (lane / 32);
+  int64_t tr = t0 + (lane % 32);
+  if (tr > T - 1) tr = T - 1;
+  const uint16_t* xp = x + tr * H + kb;
+  const float* wp0 = wr + static_cast<int64_t>(e0 + lane % 32) * H + kb;
+  const float* wp1 = wp0 + static_cast<int64_t>(32) * H;
+  f32x16 acc0 = {}, acc1 = {};
+#pragma unroll 2
+  for (int k = 0; k < kchunk; k += 16) {
+    const bf16x8 a = as_bf16x8(ld16(xp + k));
+    float w0[8], w1[8];
+    *reinterpret_cast<u32x4*>(w0) = ld16(wp0 + k);
+    *reinterpret_cast<u32x4*>(w0 + 4) = ld16(wp0 + k + 4);
+    *reinterpret_cast<u32x4*>(w1) = ld16(wp1 + k);
+    *reinterpret_cast<u32x4*>(w1 + 4) = ld16(wp1 + k + 4);
+    bf16x8 h0, m0, l0, h1, m1, l1;
+    split3(w0, h0, m0, l0);
+    split3(w1, h1, m1, l1);
+    acc0 = mfma32x32x16(a, l0, acc0);
+    acc1 = mfma32x32x16(a, l1, acc1);
+    acc0 = mfma32x32x16(a, m0, acc0);
+    acc1 = mfma32x32x16(a, m1, acc1);
+    acc0 = mfma32x32x16(a, h0, acc0);
+    acc1 = mfma32x32x16(a, h1, acc1);
+  }
+  float* out = part + static_cast<int64_t>(z) * T * E;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t t = t0 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+    if (t < T) {
+      out[t * E + e0 + lane % 32] = acc0[r];
+      out[t * E + e0 + 32 + lane % 32] = acc1[r];
+    }
+  }
+}
+
+// ---- logits: generic fp32 dot products (fp32 activations, small layers) --
+
+__global__ __launch_bounds__(256) void router_logits_valu(
+    const void* __restrict__ x, int x_bf16, const float* __restrict__ wr,
+    float* __restrict__ part, int64_t T, int H, int E, int kchunk) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int z = blockIdx.y;
+  if (i >= T * E) return;
+  const int64_t t = i / E;
+  const int e = static_cast<int>(i % E);
+  const int k0 = z * kchunk;
+  float acc = 0.0f;
+  for (int k = k0; k < k0 + kchunk; ++k) {
+    const float xv = x_bf16
+        ? bf16_bits_to_f32(static_cast<const uint16_t*>(x)[t * H + k])
+        : static_cast<const float*>(x)[t * H + k];
+    acc = __builtin_fmaf(xv, wr[static_cast<int64_t>(e) * H + k], acc);
+  }
+  part[static_cast<int64_t>(z) * T * E + i] = acc;
+}
+
+// ---- routing --------------------------------------------------------------
+
+// sigmoid32(l) = 1/(1+e^-l) evaluated in binary64 and rounded once to
+// binary32.  e^z: Cody & Waite reduction z = n ln2 + r (ln2 as a 32-bit head
+// plus a tail), then the degree-13 Taylor polynomial of e^r in Horner form
+// with fused multiply-adds; coefficients are the binary64 roundings of 1/j!.
+// Every step is an IEEE-exact binary64 operation, so any conforming
+// evaluation of this sequence returns the same bits.
+__device__ __forceinline__ float sigmoid32(float l) {
+  if (l <= -104.0f) return 0.0f;
+  if (l >= 40.0f) return 1.0f;
+  const double z = -static_cast<double>(l);
+  const double n = __builtin_rint(z * 0x1.71547652b82fep+0);
+  double r = __builtin_fma(-n, 0x1.62e42feep-1, z);
+  r = __builtin_fma(-n, 0x1.a39ef35793c76p-33, r);
+  double p = 0x1.6124613a86d09p-33;          // 1/13!
+  p = __builtin_fma(p, r, 0x1.1eed8eff8d898p-29);  // 1/12!
+  p = __builtin_fma(p, r, 0x1.ae64567f544e4p-26);  // 1/11!
+  p = __builtin_fma(p, r, 0x1.27e4fb7789f5cp-22);  // 1/10!
+  p = __builtin_fma(p, r, 0x1.71de3a556c734p-19);  // 1/9!
+  p = __builtin_fma(p, r, 0x1.a01a01a01a01ap-16);  // 1/8!
+  p = __builtin_fma(p, r, 0x1.a01a01a01a01ap-13);  // 1/7!
+  p = __builtin_fma(p, r, 0x1.6c16c16c16c17p-10);  // 1/6!
+  p = __builtin_fma(p, r, 0x1.1111111111111p-7);   // 1/5!
+  p = __builtin_fma(p, r, 0x1.5555555555555p-5);   // 1/4!
+  p = __builtin_fma(p, r, 0x1.5555555555555p-3);   // 1/3!
+  p = __builtin_fma(p, r, 0x1.0p-1);               // 1/2!
+  p = __builtin_fma(p, r, 1.0);                    // 1/1!
+  p = __builtin_fma(p, r, 1.0);                    // 1/0!
+  const double ez = __builtin_ldexp(p, static_cast<int>(n));
+  const double q = 1.0 / (1.0 + ez);
+  return static_cast<float>(q);
+}
+
+// Order-preserving map of a finite binary32 to uint32 (larger float, larger
+// key); +0 and -0 map to the same key after canonicalisation.
+__device__ __forceinline__ uint32_t ordered(float v) {
+  const uint32_t b = __float_as_uint(v + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Rank key: larger value first, then lower expert id.  0 means "not a
+// candidate" and is below every real key.
+__device__ __forceinline__ uint64_t rank_key(float u, int e) {
+  return (static_cast<uint64_t>(ordered(u)) << 32) |
+         static_cast<uint64_t>(0xFFFFFFFFu - static_cast<uint32_t>(e));
+}
+
+constexpr int kSelWaves = 4;
+constexpr int kMaxE = 1024;
+constexpr int kMaxG = 64;
+
+// grid ceil(T/4), block 256: wave w routes token 4*blockIdx.x + w.
+template <int EPL>
+__global__ __launch_bounds__(256) void router_select(
+    const float* __restrict__ part, int ks, int64_t T, int E, int G, int TG,
+    int K, int topn, float scale, const float* __restrict__ bias,
+    float* __restrict__ logits_out, int32_t* __restrict__ idx_out,
+    float* __restrict__ w_out) {
+  __shared__ float s_sh[kSelWaves][kMaxE];
+  __shared__ float u_sh[kSelWaves][kMaxE];
+  __shared__ float g_sh[kSelWaves][kMaxG];
+  __shared__ int keep_sh[kSelWaves][kMaxG];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kSelWaves + wave;
+  const bool valid = t < T;
+  const int gs = E / G;
+
+  // 1. logits (fixed-order sum of partials), scores, biased scores
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane * EPL + j;
+    if (valid && e < E) {
+      float l = part[t * E + e];
+      for (int z = 1; z < ks; ++z) l = l + part[(static_cast<int64_t>(z) * T + t) * E + e];
+      if (logits_out) logits_out[t * E + e] = l;
+      const float s = sigmoid32(l);
+      s_sh[wave][e] = s;
+      u_sh[wave][e] = s + (bias ? bias[e] : 0.0f);
+    }
+  }
+  __syncthreads();
+  // 2. group scores: sum of the topn (1 or 2) largest biased scores
+  if (valid && lane < G) {
+    float t1 = -__builtin_huge_valf(), t2 = -__builtin_huge_valf();
+    for (int j = 0; j < gs; ++j) {
+      const float v = u_sh[wave][lane * gs + j];
+      if (v > t1) {
+        t2 = t1;
+        t1 = v;
+      } else if (v > t2) {
+        t2 = v;
+      }
+    }
+    g_sh[wave][lane] = (topn == 1) ? t1 : t1 + t2;
+  }
+  __syncthreads();
+  // 3. keep the TG best groups (ties: lower group id)
+  if (valid && lane < G) {
+    const float mine = g_sh[wave][lane];
+    int rank = 0;
+    for (int g = 0; g < G; ++g) {
+      const float o = g_sh[wave][g];
+      rank += (o > mine) || (o == mine && g < lane);
+    }
+    keep_sh[wave][lane] = rank < TG;
+  }
+  __syncthreads();
+  if (!valid) return;
+  // 4. top-K of the eligible experts by biased score, rank order
+  uint64_t key[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane * EPL + j;
+    key[j] = (e < E && keep_sh[wave][e / gs]) ? rank_key(u_sh[wave][e], e) : 0;
+  }
+  float D = 0.0f, my_s = 0.0f;
+  int my_e = 0;
+  for (int k = 0; k < K; ++k) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) best = key[j] > best ? key[j] : best;
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) {
+      const uint64_t o = __shfl_xor(best, off);
+      best = o > best ? o : best;
+    }
+    // K <= TG*E/G eligible experts always remain, so best != 0; the clamp
+    // only keeps the LDS read below in bounds.
+    int e = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best));
+    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (lane * EPL + j == e) key[j] = 0;
+    const float sk = s_sh[wave][e];
+    D = (k == 0) ? sk : D + sk;
+    if (lane == k) {
+      my_e = e;
+      my_s = sk;
+    }
+  }
+  // 5. weights: (s / D) * scale, two binary32 roundings
+  if (lane < K) {
+    const float q = my_s / D;
+    idx_out[t * K + lane] = my_e;
+    w_out[t * K + lane] = q * scale;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_router(const Plan& p, const void* x, const float* w_router,
+                         const float* bias, float* logits_out,
+                         const float* logits_in, int32_t* idx, float* w,
+                         void* ws, hipStream_t s, Timer* tm) {
+  const float* part = logits_in;
+  int ks = 1;
+  if (!logits_in) {
+    ks = p.ks;
+    float* buf = ws_at<float>(ws, p.off_part);
+    const int kchunk = p.H / ks;
+    if (p.act == BEAM_BF16 && p.E % 64 == 0) {
+      dim3 grid(static_cast<unsigned>(ceil_div(p.T, 32)), p.E / 64, ks);
+      BEAM_LAUNCH(tm, "router_logits_mfma", router_logits_mfma, grid, dim3(64), 0, s,
+                         static_cast<const uint16_t*>(x), w_router, buf, p.T,
+                         p.H, p.E, kchunk);
+    } else {
+      dim3 grid(static_cast<unsigned>(ceil_div(p.T * p.E, 256)), ks);
+      BEAM_LAUNCH(tm, "router_logits_valu", router_logits_valu, grid, dim3(256), 0, s, x,
+                         p.act == BEAM_BF16 ? 1 : 0, w_router, buf, p.T, p.H,
+                         p.E, kchunk);
+    }
+    part = buf;
+  }
+  const float* lo = logits_in ? nullptr : logits_out;
+  dim3 grid(static_cast<unsigned>(ceil_div(p.T, kSelWaves)));
+#define BEAM_SEL(EPL)                                                          \
+  BEAM_LAUNCH(tm, "router_select", router_select<EPL>, grid, dim3(256), 0, s, part, ks, p.T, \
+                     p.E, p.G, p.TG, p.K, p.topn, p.scale, bias,              \
+                     const_cast<float*>(lo), idx, w)
+  const int epl = static_cast<int>(ceil_div(p.E, kWave));
+  if (epl <= 1) BEAM_SEL(1);
+  else if (epl <= 2) BEAM_SEL(2);
+  else if (epl <= 4) BEAM_SEL(4);
+  else if (epl <= 8) BEAM_SEL(8);
+  else BEAM_SEL(16);
+#undef BEAM_SEL
+  return hipGetLastError();
+}
+
+}  // namespace beam

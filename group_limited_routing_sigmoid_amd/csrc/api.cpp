@@ -74,7 +74,8 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
     p->stream_path = false;
   else
     p->stream_path = p->S <= 16 * static_cast<int64_t>(p->E);
-  if (p->wdt == BEAM_F32) p->stream_path = false;
+  // streaming kernels exist for bf16 weights only
+  if (p->wdt != BEAM_BF16) p->stream_path = false;
   const int64_t S = p->S, E = p->E, H = p->H, I = p->I;
   p->max_tiles = S / kGemmBM + (S < E ? S : E) + 1;
   const bool f32 = p->wdt == BEAM_F32;
@@ -98,6 +99,7 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
   p->off_tile_row0 = take(p->max_tiles * 4);
   p->off_meta = take(kMetaWords * 4);
   p->off_active = take(E * 4);
+  p->off_tile_off = take((E + 1) * 4);
   p->off_h = take(S * I * (f32 ? 4 : 2));
   p->off_y = take(S * H * ((f32 || p->stream_path) ? 4 : 2));
   if (p->wdt == BEAM_FP8_E4M3) {
@@ -152,7 +154,10 @@ int beam_moe_validate(const beam_moe_desc* d, int64_t T) {
     return BEAM_ERR_UNSUPPORTED;
   if (d->weight_dtype == BEAM_F32 && d->act_dtype != BEAM_F32) return BEAM_ERR_UNSUPPORTED;
   if (d->weight_dtype != BEAM_F32 && d->act_dtype != BEAM_BF16) return BEAM_ERR_UNSUPPORTED;
-  if (T * static_cast<int64_t>(d->top_k) > 0x7FFFFFFF) return BEAM_ERR_UNSUPPORTED;
+  // slot indices and per-slot element offsets are 32-bit
+  const int64_t S = T * static_cast<int64_t>(d->top_k);
+  const int64_t wide = d->hidden > d->intermediate ? d->hidden : d->intermediate;
+  if (S * wide > 0x7FFFFFFF) return BEAM_ERR_UNSUPPORTED;
   return BEAM_OK;
 }
 

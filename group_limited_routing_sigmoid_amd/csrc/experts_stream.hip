@@ -1,9 +1,10 @@
 // Expert MLPs for decode-sized batches: each touched expert sees only a few
 // tokens, so the work is bound by reading its weights once from HBM.  The
 // weights are the 16-row A side of 16x16x32 bf16 MFMA and up to 16 tokens
-// are the B side; the reduction over the hidden (or intermediate) dimension
-// is split over the 4 waves of a workgroup and summed in LDS in a fixed
-// order.  Experts with more than 16 tokens are handled in chunks of 16.
+// are the B side.  Gate/up: one wave streams 32 rows over the whole hidden
+// dimension.  Down (rows half as long): the reduction over the intermediate
+// dimension is split over the 4 waves of a workgroup and summed in LDS in a
+// fixed order.  Experts with more than 16 tokens are handled in chunks of 16.
 //
 // Same SwiGLU expert as the grouped path ("Hugging Face releases Beam ..."
 // MoE paragraph): h = silu(x W_g^T) * (x W_u^T) for gate/up, y = h W_d^T for
@@ -23,23 +24,27 @@ constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kUnroll = 8;   // k-steps of 32 in flight per wave
 
-// grid (max_active * I/16), block 256
+// One wave per (active expert j, 16-channel block): it streams the 16 gate
+// and 16 up rows over the whole hidden dimension with two independent
+// accumulator chains per half, so no cross-wave reduction is needed.
+// grid ceil(max_active * I/16 / 4), block 256 (4 work items per workgroup)
+constexpr int kGuUnroll = 16;  // k-steps of 32 in flight per wave
+
 __global__ __launch_bounds__(kThreads) void stream_gate_up(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_gu,
     uint16_t* __restrict__ h, const int32_t* __restrict__ slot_token,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ active, const int32_t* __restrict__ meta,
     int H, int I) {
-  __shared__ f32x4 red[kWaves][2][kWave];
   const int n_cb = I / 16;
-  const int j = blockIdx.x / n_cb;
-  const int cb = blockIdx.x % n_cb;
+  const int item = blockIdx.x * kWaves + threadIdx.x / kWave;
+  const int j = item / n_cb;
+  const int cb = item % n_cb;
   if (j >= meta[kMetaActive]) return;
   const int e = active[j];
   const int off = offsets[e], cnt = counts[e];
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int kw = H / kWaves;  // columns per wave
-  const int kofs = wave * kw + 8 * (lane / 16);
+  const int lane = threadIdx.x % kWave;
+  const int kofs = 8 * (lane / 16);
   const uint16_t* wg = w_gu + (static_cast<int64_t>(e) * 2 * I + cb * 16 + lane % 16) * H + kofs;
   const uint16_t* wu = wg + static_cast<int64_t>(I) * H;
 
@@ -47,40 +52,31 @@ __global__ __launch_bounds__(kThreads) void stream_gate_up(
     const int ntok = min(16, cnt - c0);
     const bool has_tok = (lane % 16) < ntok;
     const uint16_t* xr = x + (has_tok ? static_cast<int64_t>(slot_token[off + c0 + lane % 16]) * H : 0) + kofs;
-    f32x4 ag = {}, au = {};
-    for (int k = 0; k < kw; k += 32 * kUnroll) {
-      u32x4 ga[kUnroll], ua[kUnroll], xb[kUnroll];
+    f32x4 ag0 = {}, au0 = {}, ag1 = {}, au1 = {};
+    for (int k = 0; k < H; k += 32 * kGuUnroll) {
+      u32x4 ga[kGuUnroll], ua[kGuUnroll], xb[kGuUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const bool in = k + 32 * u < kw;
+      for (int u = 0; u < kGuUnroll; ++u) {
+        const bool in = k + 32 * u < H;
         ga[u] = in ? ld16(wg + k + 32 * u) : u32x4{0, 0, 0, 0};
         ua[u] = in ? ld16(wu + k + 32 * u) : u32x4{0, 0, 0, 0};
         xb[u] = (in && has_tok) ? ld16(xr + k + 32 * u) : u32x4{0, 0, 0, 0};
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        ag = mfma16x16x32(as_bf16x8(ga[u]), as_bf16x8(xb[u]), ag);
-        au = mfma16x16x32(as_bf16x8(ua[u]), as_bf16x8(xb[u]), au);
+      for (int u = 0; u < kGuUnroll; u += 2) {
+        ag0 = mfma16x16x32(as_bf16x8(ga[u]), as_bf16x8(xb[u]), ag0);
+        au0 = mfma16x16x32(as_bf16x8(ua[u]), as_bf16x8(xb[u]), au0);
+        ag1 = mfma16x16x32(as_bf16x8(ga[u + 1]), as_bf16x8(xb[u + 1]), ag1);
+        au1 = mfma16x16x32(as_bf16x8(ua[u + 1]), as_bf16x8(xb[u + 1]), au1);
       }
     }
-    red[wave][0][lane] = ag;
-    red[wave][1][lane] = au;
-    __syncthreads();
-    if (wave == 0) {
-      f32x4 g = red[0][0][lane], u = red[0][1][lane];
+    const f32x4 g = ag0 + ag1, u = au0 + au1;
+    if (has_tok) {
+      // element r: channel cb*16 + 4*(lane/16) + r, token lane%16
+      uint16_t* hr = h + static_cast<int64_t>(off + c0 + lane % 16) * I + cb * 16 + 4 * (lane / 16);
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) {
-        g += red[w][0][lane];
-        u += red[w][1][lane];
-      }
-      if (has_tok) {
-        // element r: channel cb*16 + 4*(lane/16) + r, token lane%16
-        uint16_t* hr = h + static_cast<int64_t>(off + c0 + lane % 16) * I + cb * 16 + 4 * (lane / 16);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hr[r] = f32_to_bf16_bits(silu(g[r]) * u[r]);
-      }
+      for (int r = 0; r < 4; ++r) hr[r] = f32_to_bf16_bits(silu(g[r]) * u[r]);
     }
-    __syncthreads();
   }
 }
 
@@ -159,7 +155,8 @@ hipError_t launch_stream_bf16(const Plan& p, const void* x,
   uint16_t* h = ws_at<uint16_t>(ws, p.off_h);
   float* y = ws_at<float>(ws, p.off_y);
   const int64_t max_active = p.S < p.E ? p.S : p.E;
-  BEAM_LAUNCH(tm, "stream_gate_up_bf16", stream_gate_up, dim3(static_cast<unsigned>(max_active * (p.I / 16))),
+  BEAM_LAUNCH(tm, "stream_gate_up_bf16", stream_gate_up,
+              dim3(static_cast<unsigned>(ceil_div(max_active * (p.I / 16), kWaves))),
                      dim3(kThreads), 0, s, static_cast<const uint16_t*>(x),
                      static_cast<const uint16_t*>(w_gate_up), h, slot_token,
                      counts, offsets, active, meta, p.H, p.I);

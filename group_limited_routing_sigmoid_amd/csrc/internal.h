@@ -11,7 +11,7 @@
 namespace beam {
 
 // Grouped-GEMM row tile: rows (slots) per M tile of one expert.
-constexpr int kGemmBM = 128;
+constexpr int kGemmBM = 256;
 // Tokens routed per workgroup by the permutation kernels.
 constexpr int kPermBlock = 256;
 
@@ -28,7 +28,8 @@ struct Plan {
   // byte offsets into the workspace
   size_t off_part, off_idx, off_w, off_hist, off_base, off_rank, off_counts,
       off_offsets, off_slot_token, off_slot_of, off_tile_expert, off_tile_row0,
-      off_meta, off_active, off_h, off_y, off_xq, off_xs, off_hq, off_hs;
+      off_meta, off_active, off_tile_off, off_h, off_y, off_xq, off_xs,
+      off_hq, off_hs;
   size_t total;
 };
 

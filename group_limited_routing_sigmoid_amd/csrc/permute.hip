@@ -11,7 +11,8 @@
 //                 histogram = row popcounts; rank of (t, e) inside the block
 //                 = popcount of row e below bit t.
 //   perm_scan     one block: per-expert prefix over blocks, counts, offsets,
-//                 grouped-GEMM M-tile list and the list of active experts.
+//                 grouped-GEMM M-tile list (with each expert's first tile)
+//                 and the list of active experts.
 //   perm_scatter  slot = offsets[e] + block base + rank.
 #include "common.h"
 #include "internal.h"
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(kMaxE) void perm_scan(
     int32_t* __restrict__ base, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ tile_expert,
     int32_t* __restrict__ tile_row0, int32_t* __restrict__ meta,
-    int32_t* __restrict__ active) {
+    int32_t* __restrict__ active, int32_t* __restrict__ tile_off) {
   __shared__ int sh[kMaxE];
   const int e = threadIdx.x;
   int c = 0;
@@ -97,9 +98,11 @@ __global__ __launch_bounds__(kMaxE) void perm_scan(
       tile_row0[toff + i] = off + i * bm;
     }
     if (act) active[aincl - 1] = e;
+    tile_off[e] = toff;
   }
   if (e == E - 1) {
     offsets[E] = incl;
+    tile_off[E] = tincl;
     meta[kMetaTiles] = tincl;
     meta[kMetaActive] = aincl;
   }
@@ -137,7 +140,8 @@ hipError_t launch_permute(const Plan& p, const int32_t* idx, int32_t* counts,
                      ws_at<int32_t>(ws, p.off_tile_expert),
                      ws_at<int32_t>(ws, p.off_tile_row0),
                      ws_at<int32_t>(ws, p.off_meta),
-                     ws_at<int32_t>(ws, p.off_active));
+                     ws_at<int32_t>(ws, p.off_active),
+                     ws_at<int32_t>(ws, p.off_tile_off));
   BEAM_LAUNCH(tm, "perm_scatter", perm_scatter, dim3(nb), dim3(kPermBlock), 0, s, idx, p.T,
                      p.K, p.E, base, rank, offsets, slot_token, slot_of);
   return hipGetLastError();

@@ -89,7 +89,7 @@ const char* beam_status_string(int status);
  * Supported: 1 <= E <= 1024, E % G == 0, E/G <= 64, 1 <= TG <= G,
  * 1 <= K <= min(16, TG*E/G), group_score_topn in {1,2} and <= E/G,
  * H % 128 == 0 and I % 128 == 0, routed_scale finite and > 0, T >= 0,
- * T*K < 2^31.  Returns BEAM_OK or the first error found. */
+ * T*K*max(H, I) < 2^31 (52,428 tokens for the Beam layer).   Returns BEAM_OK or the first error found. */
 int beam_moe_validate(const beam_moe_desc* desc, int64_t T);
 
 /* Bytes of workspace beam_moe_forward / beam_moe_route need for T tokens.

@@ -39,6 +39,14 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
 
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's bytes land at lds + 16*l, where lds must be the same for the
+// whole wave.  Completion is tracked by the wave's vector-memory counter.
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
 // D = A(32x16) * B(16x32) + C on the matrix cores, bf16 inputs, fp32 sums.
 // Lane l supplies A row (l % 32) and B column (l % 32), k-block (l / 32).
 // Accumulator element r of lane l is C[8*(r/4) + 4*(l/32) + r%4][l % 32].

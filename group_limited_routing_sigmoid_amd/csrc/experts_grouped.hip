@@ -11,16 +11,18 @@
 // permutation kernels, crossed with 256-wide N tiles.  A gate/up N tile holds
 // 128 gate rows of W_gu and the 128 matching up rows, so every wave owns both
 // halves of its channels and applies silu(g)*u in registers; x rows are
-// gathered by slot inside the A loads (no permuted copy of x).  Tiles are
-// staged in LDS, double buffered, 16-byte chunks XOR-swizzled by row so the
-// MFMA operand reads are bank-conflict free.  8 waves (2 per SIMD) each
-// compute 128x64 with 32x32x16 bf16 MFMA.
+// gathered by slot inside the A loads (no permuted copy of x).  Tiles move
+// from global memory straight into LDS (global_load_lds_dwordx4), double
+// buffered, 16-byte chunks XOR-swizzled by row so the MFMA operand reads are
+// bank-conflict free; operand fragments are double buffered in registers.
+// 8 waves (2 per SIMD) each compute 128x64 with 32x32x16 bf16 MFMA.
 //
 // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, each with
 // its own L2.  Workgroup b takes logical tile (b % 8) * ceil(n/8) + b / 8, so
-// every XCD walks a contiguous stretch of the logical order (expert, N tile,
-// M tile) and the M tiles that share a weight N tile run together on one
-// XCD and hit its L2.
+// every XCD walks a contiguous stretch of the logical order: expert, then
+// groups of 4 M tiles, then N tile, then M tile inside the group.  The ~32
+// workgroups an XCD runs at once then cover about 4 M tiles x 8 N tiles of
+// one expert and share both operands' current k-slices in its L2.
 #include "common.h"
 #include "internal.h"
 
@@ -34,6 +36,10 @@ constexpr int kThreads = 512;
 constexpr int kRowBytes = BK * 2;        // 128 bytes per tile row in LDS
 constexpr int kTileBytes = BM * kRowBytes;  // 32 KiB per operand tile
 constexpr int kXcds = 8;
+#ifndef BEAM_GROUP_M
+#define BEAM_GROUP_M 4
+#endif
+constexpr int kGroupM = BEAM_GROUP_M;  // M tiles per rasterisation group
 constexpr int kLoads = (BM * BK * 2) / (16 * kThreads);  // 16-byte chunks per thread per operand
 
 enum Mode { kGateUp = 0, kDown = 1 };
@@ -72,9 +78,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(
   if (local >= per_xcd || L >= n_log) return;
   const int e = find_expert(tile_off, E, n_nt, L);
   const int t0 = tile_off[e], nt_e = tile_off[e + 1] - t0;
+  // Within an expert, groups of kGroupM M tiles walk the N tiles together,
+  // so the workgroups resident on one XCD share A and B k-slices in its L2.
   const int j = L - t0 * n_nt;
-  const int nt = j / nt_e;
-  const int row0 = offsets[e] + (j % nt_e) * BM;
+  const int g = j / (kGroupM * n_nt);
+  const int gm = min(kGroupM, nt_e - g * kGroupM);
+  const int jj = j - g * kGroupM * n_nt;
+  const int nt = jj / gm;
+  const int row0 = offsets[e] + (g * kGroupM + jj % gm) * BM;
   const int row_end = offsets[e] + counts[e];  // first slot past this expert
   const int K = (MODE == kGateUp) ? H : I;
 
@@ -82,44 +93,35 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(
   const int lane = tid % kWave, wave = tid / kWave;
   const int wm = wave / 4, wn = wave % 4;
 
-  // ---- this thread's global chunks: rows tid/8 + 64*i, 16-byte chunk tid%8
-  const int chunk = tid % 8;
-  // 32-bit element offsets from wave-uniform bases (the caller guarantees
-  // S * max(H, I) < 2^31; one expert's weights are far below that).
+  // ---- direct-to-LDS loads: one instruction fills 1 KiB = 8 tile rows, lane
+  // l writing physical chunk l % 8 of row l / 8; it fetches the logical chunk
+  // the swizzle maps there.  Wave w fills A regions w + 8i and B regions
+  // w + 8i (i = 0..3) of each stage.
   const uint16_t* wbase = (MODE == kGateUp) ? w + static_cast<int64_t>(e) * 2 * I * H
                                             : w + static_cast<int64_t>(e) * H * I;
   uint32_t a_off[kLoads], b_off[kLoads];
-  int lds_off[kLoads];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
-    const int r = tid / 8 + (kThreads / 8) * i;
+    const int r = 8 * (wave + 8 * i) + lane / 8;            // tile row
+    const int c = (lane % 8) ^ ((r ^ (r >> 3)) & 7);         // logical chunk
     int slot = row0 + r;
-    if (slot > row_end - 1) slot = row_end - 1;  // padded rows: any valid row
+    if (slot > row_end - 1) slot = row_end - 1;              // padded rows: any valid row
     if (MODE == kGateUp) {
-      a_off[i] = static_cast<uint32_t>(slot_token[slot]) * H + chunk * 8;
+      a_off[i] = static_cast<uint32_t>(slot_token[slot]) * H + c * 8;
       // rows 0..127: gate channels nt*128 + r; rows 128..255: up channels
       const int wrow = (r < 128) ? (nt * 128 + r) : (I + nt * 128 + (r - 128));
-      b_off[i] = static_cast<uint32_t>(wrow) * H + chunk * 8;
+      b_off[i] = static_cast<uint32_t>(wrow) * H + c * 8;
     } else {
-      a_off[i] = static_cast<uint32_t>(slot) * I + chunk * 8;
-      b_off[i] = static_cast<uint32_t>(nt * BN + r) * I + chunk * 8;
+      a_off[i] = static_cast<uint32_t>(slot) * I + c * 8;
+      b_off[i] = static_cast<uint32_t>(nt * BN + r) * I + c * 8;
     }
-    lds_off[i] = swz(r, chunk);
   }
-
-  u32x4 ra[kLoads], rb[kLoads];
-  auto gload = [&](int k0) {
+  auto dma = [&](int buf, int k0) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      ra[i] = ld16(a_src + (a_off[i] + k0));
-      rb[i] = ld16(wbase + (b_off[i] + k0));
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      *reinterpret_cast<u32x4*>(&lds[buf][lds_off[i]]) = ra[i];
-      *reinterpret_cast<u32x4*>(&lds[buf][kTileBytes + lds_off[i]]) = rb[i];
+      const int region = wave + 8 * i;
+      dma16(a_src + (a_off[i] + k0), &lds[buf][region * 1024]);
+      dma16(wbase + (b_off[i] + k0), &lds[buf][kTileBytes + region * 1024]);
     }
   };
 
@@ -140,35 +142,54 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(
     brow[n] = (MODE == kGateUp) ? (n * 128 + wn * 32 + lane % 32)
                                 : (wn * 64 + n * 32 + lane % 32);
 
+  struct Frags {
+    bf16x8 a[4], b[2];
+  };
+  auto load_frags = [&](Frags& f, int buf, int kk) {
+    const int c = kk * 2 + lane / 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      f.a[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&lds[buf][swz(arow[i], c)]));
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+      f.b[n] = as_bf16x8(*reinterpret_cast<const u32x4*>(&lds[buf][kTileBytes + swz(brow[n], c)]));
+  };
+  auto mfmas = [&](const Frags& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int n = 0; n < 2; ++n) acc[i][n] = mfma32x32x16(f.a[i], f.b[n], acc[i][n]);
+  };
+  // fragments of k16 step kk+1 are read while the 8 products of step kk run
+  // (scheduling fences keep the compiler from folding the two fragment sets
+  // into one and waiting on LDS before every product)
   auto compute = [&](int buf) {
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = kk * 2 + lane / 32;
-      bf16x8 af[4], bfr[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&lds[buf][swz(arow[i], c)]));
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-        bfr[n] = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(&lds[buf][kTileBytes + swz(brow[n], c)]));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int n = 0; n < 2; ++n) acc[i][n] = mfma32x32x16(af[i], bfr[n], acc[i][n]);
-    }
+    Frags f0, f1;
+    load_frags(f0, buf, 0);
+    load_frags(f1, buf, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(f0, buf, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(f1, buf, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f1);
   };
 
   const int nk = K / BK;
-  gload(0);
-  sstore(0);
+  dma(0, 0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+    // buffer buf^1 was last read before the barrier that ended step kt-1
+    if (kt + 1 < nk) dma(buf ^ 1, (kt + 1) * BK);
     compute(buf);
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
+    __syncthreads();  // waits for this wave's loads, then for every wave
   }
 
   // ---- epilogue -------------------------------------------------------------

@@ -28,7 +28,10 @@ constexpr int kUnroll = 8;   // k-steps of 32 in flight per wave
 // and 16 up rows over the whole hidden dimension with two independent
 // accumulator chains per half, so no cross-wave reduction is needed.
 // grid ceil(max_active * I/16 / 4), block 256 (4 work items per workgroup)
-constexpr int kGuUnroll = 16;  // k-steps of 32 in flight per wave
+#ifndef BEAM_GU_UNROLL
+#define BEAM_GU_UNROLL 16
+#endif
+constexpr int kGuUnroll = BEAM_GU_UNROLL;  // k-steps of 32 in flight per wave
 
 __global__ __launch_bounds__(kThreads) void stream_gate_up(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_gu,
@@ -80,62 +83,89 @@ __global__ __launch_bounds__(kThreads) void stream_gate_up(
   }
 }
 
-// grid (max_active * H/32), block 256
+// Down: a work item is (active expert j, 16*kDnTiles rows of W_d); its
+// reduction over I is split over kDnSplit waves and summed in LDS in a fixed
+// order.  A workgroup of 4 waves holds 4 / kDnSplit items.
+#ifndef BEAM_DN_TILES
+#define BEAM_DN_TILES 2
+#endif
+#ifndef BEAM_DN_SPLIT
+#define BEAM_DN_SPLIT 4
+#endif
+#ifndef BEAM_DN_UNROLL
+#define BEAM_DN_UNROLL 8
+#endif
+constexpr int kDnTiles = BEAM_DN_TILES;
+constexpr int kDnSplit = BEAM_DN_SPLIT;
+constexpr int kDnUnroll = BEAM_DN_UNROLL;
+constexpr int kDnRows = 16 * kDnTiles;
+constexpr int kDnItems = kWaves / kDnSplit;
+
 __global__ __launch_bounds__(kThreads) void stream_down(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ w_d,
     float* __restrict__ y, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
     const int32_t* __restrict__ meta, int H, int I) {
-  __shared__ f32x4 red[kWaves][2][kWave];
-  const int n_ob = H / 32;
-  const int j = blockIdx.x / n_ob;
-  const int ob = blockIdx.x % n_ob;
-  if (j >= meta[kMetaActive]) return;
-  const int e = active[j];
-  const int off = offsets[e], cnt = counts[e];
+  __shared__ f32x4 red[kWaves][kDnTiles][kWave];
+  const int n_ob = H / kDnRows;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int kw = I / kWaves;
-  const int kofs = wave * kw + 8 * (lane / 16);
-  const uint16_t* w0 = w_d + (static_cast<int64_t>(e) * H + ob * 32 + lane % 16) * I + kofs;
-  const uint16_t* w1 = w0 + static_cast<int64_t>(16) * I;
+  const int item = blockIdx.x * kDnItems + wave / kDnSplit;
+  const int part = wave % kDnSplit;
+  const int j = item / n_ob;
+  const int ob = item % n_ob;
+  // every wave of the workgroup reaches the barriers below, valid or not
+  const bool valid = j < meta[kMetaActive];
+  const int e = valid ? active[j] : 0;
+  const int off = valid ? offsets[e] : 0, cnt = valid ? counts[e] : 0;
+  const int kw = I / kDnSplit;
+  const int kofs = part * kw + 8 * (lane / 16);
+  const uint16_t* w0 = w_d + (static_cast<int64_t>(e) * H + ob * kDnRows + lane % 16) * I + kofs;
 
-  for (int c0 = 0; c0 < cnt; c0 += 16) {
-    const int ntok = min(16, cnt - c0);
+  // all items of a workgroup loop the same number of 16-token chunks
+  __shared__ int chunk_cnt[kDnItems];
+  if (lane == 0 && part == 0) chunk_cnt[wave / kDnSplit] = cnt;
+  __syncthreads();
+  int loops = 0;
+#pragma unroll
+  for (int o = 0; o < kDnItems; ++o) loops = max(loops, chunk_cnt[o]);
+
+  for (int c0 = 0; c0 < loops; c0 += 16) {
+    const int ntok = max(0, min(16, cnt - c0));
     const bool has_tok = (lane % 16) < ntok;
     const uint16_t* hr = h + static_cast<int64_t>(off + c0 + (has_tok ? lane % 16 : 0)) * I + kofs;
-    f32x4 a0 = {}, a1 = {};
-    for (int k = 0; k < kw; k += 32 * kUnroll) {
-      u32x4 wa[kUnroll], wb[kUnroll], hb[kUnroll];
+    f32x4 a[kDnTiles];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const bool in = k + 32 * u < kw;
-        wa[u] = in ? ld16(w0 + k + 32 * u) : u32x4{0, 0, 0, 0};
-        wb[u] = in ? ld16(w1 + k + 32 * u) : u32x4{0, 0, 0, 0};
-        hb[u] = (in && has_tok) ? ld16(hr + k + 32 * u) : u32x4{0, 0, 0, 0};
-      }
+    for (int t = 0; t < kDnTiles; ++t) a[t] = f32x4{};
+    if (ntok > 0) {
+      for (int k = 0; k < kw; k += 32 * kDnUnroll) {
+        u32x4 wv[kDnTiles][kDnUnroll], hb[kDnUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        a0 = mfma16x16x32(as_bf16x8(wa[u]), as_bf16x8(hb[u]), a0);
-        a1 = mfma16x16x32(as_bf16x8(wb[u]), as_bf16x8(hb[u]), a1);
+        for (int u = 0; u < kDnUnroll; ++u) {
+          const bool in = k + 32 * u < kw;
+#pragma unroll
+          for (int t = 0; t < kDnTiles; ++t)
+            wv[t][u] = in ? ld16(w0 + static_cast<int64_t>(16 * t) * I + k + 32 * u) : u32x4{0, 0, 0, 0};
+          hb[u] = (in && has_tok) ? ld16(hr + k + 32 * u) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < kDnUnroll; ++u)
+#pragma unroll
+          for (int t = 0; t < kDnTiles; ++t)
+            a[t] = mfma16x16x32(as_bf16x8(wv[t][u]), as_bf16x8(hb[u]), a[t]);
       }
     }
-    red[wave][0][lane] = a0;
-    red[wave][1][lane] = a1;
+#pragma unroll
+    for (int t = 0; t < kDnTiles; ++t) red[wave][t][lane] = a[t];
     __syncthreads();
-    if (wave == 0) {
-      f32x4 r0 = red[0][0][lane], r1 = red[0][1][lane];
+    if (part == 0 && has_tok) {
+      float* yr = y + static_cast<int64_t>(off + c0 + lane % 16) * H + ob * kDnRows + 4 * (lane / 16);
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) {
-        r0 += red[w][0][lane];
-        r1 += red[w][1][lane];
-      }
-      if (has_tok) {
-        float* yr = y + static_cast<int64_t>(off + c0 + lane % 16) * H + ob * 32 + 4 * (lane / 16);
+      for (int t = 0; t < kDnTiles; ++t) {
+        f32x4 r = red[wave][t][lane];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          yr[r] = r0[r];
-          yr[16 + r] = r1[r];
-        }
+        for (int w = 1; w < kDnSplit; ++w) r += red[wave + w][t][lane];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) yr[16 * t + q] = r[q];
       }
     }
     __syncthreads();
@@ -160,7 +190,8 @@ hipError_t launch_stream_bf16(const Plan& p, const void* x,
                      dim3(kThreads), 0, s, static_cast<const uint16_t*>(x),
                      static_cast<const uint16_t*>(w_gate_up), h, slot_token,
                      counts, offsets, active, meta, p.H, p.I);
-  BEAM_LAUNCH(tm, "stream_down_bf16", stream_down, dim3(static_cast<unsigned>(max_active * (p.H / 32))),
+  BEAM_LAUNCH(tm, "stream_down_bf16", stream_down,
+              dim3(static_cast<unsigned>(ceil_div(max_active * (p.H / kDnRows), kDnItems))),
                      dim3(kThreads), 0, s, h, static_cast<const uint16_t*>(w_down),
                      y, counts, offsets, active, meta, p.H, p.I);
   return hipGetLastError();

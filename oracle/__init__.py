@@ -26,6 +26,11 @@ What each oracle function follows, and what pins it (tests/test_oracle_*.py):
                       experts (2.5 x one expert), experts differing only by a
                       down-projection factor (checks which weight goes with
                       which expert), and token-permutation invariance.
+  * bias_update    -- aux-loss-free balancing step (load-balancing paragraph
+                      of "Reflection AI Introduces Beam ..."; rule of
+                      DeepSeek-V3).  Pinned by a closed form on crafted loads
+                      and by repeated route/update rounds driving the expert
+                      load towards balance (a flipped sign diverges).
   * e4m3 codec     -- pinned against torch.float8_e4m3fn on all 256 codes and
                       on random values.  The FP8 activation recipe (per-128
                       amax/448 scales) is a reading the pages do not fix:
@@ -85,6 +90,10 @@ def lib():
         L.bo_forward_tokens.argtypes = [ctypes.POINTER(Shape), i64, vp, vp, i32,
                                         vp, vp, vp, vp, vp, vp, i32, i32, vp, i32]
         L.bo_forward_tokens.restype = i32
+        L.bo_bias_update.argtypes = [i32, i64, i32, vp, ctypes.c_float, vp]
+        L.bo_bias_update.restype = None
+        L.bo_bias_gamma.argtypes = [i64, i64, ctypes.c_float, ctypes.c_float]
+        L.bo_bias_gamma.restype = ctypes.c_float
         L.bo_max_threads.argtypes = []
         L.bo_max_threads.restype = i32
         _lib = L
@@ -218,3 +227,17 @@ def forward_tokens(shape, tokens, x, idx, w, w_gate_up, w_down,
     if rc:
         raise ValueError("oracle forward: unsupported shape")
     return out
+
+
+def bias_update(n_experts, idx, gamma, bias):
+    """Aux-loss-free balancing step: returns the updated fp32 bias."""
+    idx = np.ascontiguousarray(_np(idx), np.int32)
+    b = np.array(_np(bias), dtype=np.float32, copy=True)
+    T, K = idx.shape
+    lib().bo_bias_update(n_experts, T, K, _ptr(idx), float(gamma), _ptr(b))
+    return b
+
+
+def bias_gamma(t, n, g0, g1):
+    """Cosine-decayed update speed for step t of n."""
+    return lib().bo_bias_gamma(t, n, g0, g1)

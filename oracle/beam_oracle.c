@@ -372,6 +372,34 @@ int bo_forward_tokens(const bo_shape* sh, int64_t n, const int64_t* tokens,
   return 0;
 }
 
+/* Auxiliary-loss-free load balancing ([P4]: DeepSeek-V3's bias-update
+ * balancing with a cosine-decayed update speed; rule from [DSV3] section
+ * 2.1.2): after a batch, every expert's bias moves by gamma towards balance,
+ *   b_e = b_e + gamma * sign(mean_load - load_e),  mean_load = T*K/E,
+ * with sign(0) = 0 and one binary32 addition.  load_e counts the (token,
+ * expert) assignments of the batch; the sign is decided exactly in integers
+ * (load_e * E against T * K). */
+void bo_bias_update(int E, int64_t T, int K, const int32_t* idx, float gamma,
+                    float* bias) {
+  int64_t* load = (int64_t*)calloc(E, sizeof(int64_t));
+  for (int64_t i = 0; i < T * K; ++i) load[idx[i]] += 1;
+  for (int e = 0; e < E; ++e) {
+    const int64_t lhs = load[e] * E, rhs = T * K;
+    const float step = (lhs < rhs) ? gamma : ((lhs > rhs) ? -gamma : 0.0f);
+    bias[e] = bias[e] + step;
+  }
+  free(load);
+}
+
+/* Cosine decay of the update speed over a schedule of n steps ([P4] names a
+ * cosine decay; the endpoints are inputs): gamma_t = g1 + (g0 - g1) * (1 +
+ * cos(pi * t / n)) / 2, in binary64, rounded to binary32. */
+float bo_bias_gamma(int64_t t, int64_t n, float g0, float g1) {
+  const double pi = 3.14159265358979323846;
+  const double c = 0.5 * (1.0 + cos(pi * (double)t / (double)n));
+  return (float)((double)g1 + ((double)g0 - (double)g1) * c);
+}
+
 int bo_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -26,7 +26,7 @@ SYMBOLS = ("beam_status_string", "beam_moe_validate", "beam_moe_workspace_bytes"
            "beam_moe_route", "beam_moe_permute", "beam_moe_quant_e4m3",
            "beam_moe_forward", "beam_moe_timer_create", "beam_moe_timer_destroy",
            "beam_moe_timer_reset", "beam_moe_timer_count", "beam_moe_timer_read",
-           "beam_moe_forward_timed")
+           "beam_moe_forward_timed", "beam_moe_bias_update", "beam_moe_bias_gamma")
 
 
 class Desc(ctypes.Structure):
@@ -76,9 +76,13 @@ def lib():
         L.beam_moe_timer_count.argtypes = [vp]
         L.beam_moe_timer_read.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_char_p),
                                           ctypes.POINTER(ctypes.c_float)]
+        L.beam_moe_bias_update.argtypes = [D, i64, vp, ctypes.c_float, vp, vp]
+        L.beam_moe_bias_gamma.argtypes = [i64, i64, ctypes.c_float, ctypes.c_float]
+        L.beam_moe_bias_gamma.restype = ctypes.c_float
         for f in SYMBOLS[1:]:
             if getattr(L, f).restype is ctypes.c_int or f in (
-                    "beam_moe_timer_destroy", "beam_moe_timer_reset"):
+                    "beam_moe_timer_destroy", "beam_moe_timer_reset",
+                    "beam_moe_bias_gamma"):
                 continue
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -201,6 +205,20 @@ def permute(desc: Desc, topk_idx: torch.Tensor,
     out["slot_token"] = out["slot_token"][:S]
     out["slot_of"] = out["slot_of"][:S].view(T, desc.top_k)
     return out
+
+
+def bias_update(desc: Desc, topk_idx: torch.Tensor, gamma: float,
+                bias: torch.Tensor, stream=None):
+    """beam_moe_bias_update: one balancing step on `bias` (in place)."""
+    _check(lib().beam_moe_bias_update(ctypes.byref(desc), topk_idx.shape[0],
+                                      _p(topk_idx), float(gamma), _p(bias),
+                                      _stream(stream)), "beam_moe_bias_update")
+    return bias
+
+
+def bias_gamma(t: int, n: int, g0: float, g1: float) -> float:
+    """beam_moe_bias_gamma: cosine-decayed update speed (host only)."""
+    return lib().beam_moe_bias_gamma(t, n, g0, g1)
 
 
 def quant_e4m3(v: torch.Tensor, stream=None):

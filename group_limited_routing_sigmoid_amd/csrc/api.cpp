@@ -62,7 +62,16 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
   // Router reduction split: enough waves to spread W_r over the chip when
   // there are few tokens; each split must cover a multiple of 16 columns.
   p->ks = 1;
-  if (p->act == BEAM_BF16 && p->E % 64 == 0) {
+  p->router_gemm = p->act == BEAM_BF16 && p->E % 256 == 0 && T >= 1024;
+  if (p->router_gemm) {
+    // dense tile GEMM of x against W3 = the three bf16 terms of W_r side by
+    // side (depth 3H); split the depth until about one workgroup per
+    // compute unit
+    const int64_t tiles = ceil_div(T, kGemmBM) * (p->E / 256);
+    p->ks = 1;
+    while (p->ks < 16 && tiles * p->ks < 256 && (3 * p->H / 64) % (2 * p->ks) == 0)
+      p->ks *= 2;
+  } else if (p->act == BEAM_BF16 && p->E % 64 == 0) {
     const int64_t waves = ceil_div(T, 32) * (p->E / 64);
     while (p->ks < 16 && waves * p->ks < 1024 && (p->H / 16) % (2 * p->ks) == 0)
       p->ks *= 2;
@@ -86,6 +95,7 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
     return at;
   };
   p->off_part = take(static_cast<size_t>(p->ks) * T * E * 4);
+  p->off_w3 = p->router_gemm ? take(3 * E * H * 2) : 0;
   p->off_idx = take(S * 4);
   p->off_w = take(S * 4);
   p->off_hist = take(p->nb * E * 4);
@@ -212,6 +222,27 @@ int beam_moe_permute(const beam_moe_desc* d, int64_t T, const int32_t* topk_idx,
   return hip_status(launch_permute(p, topk_idx, counts, offsets, slot_token,
                                    slot_of, workspace, static_cast<hipStream_t>(stream),
                                    nullptr));
+}
+
+int beam_moe_bias_update(const beam_moe_desc* d, int64_t T, const int32_t* topk_idx,
+                         float gamma, float* bias, void* stream) {
+  Plan p;
+  int st = make_plan(d, T, &p);
+  if (st != BEAM_OK) return st;
+  if (!(gamma >= 0.0f) || !isfinite(gamma)) return BEAM_ERR_INVALID_ARG;
+  if (T == 0) return BEAM_OK;
+  if (!topk_idx || !bias || !aligned16(topk_idx) || !aligned16(bias))
+    return BEAM_ERR_INVALID_ARG;
+  return hip_status(launch_bias_update(p, topk_idx, gamma, bias,
+                                       static_cast<hipStream_t>(stream), nullptr));
+}
+
+float beam_moe_bias_gamma(int64_t t, int64_t n, float g0, float g1) {
+  if (n <= 0) return g1;
+  if (t < 0) t = 0;
+  if (t > n) t = n;
+  const double c = 0.5 * (1.0 + cos(M_PI * static_cast<double>(t) / static_cast<double>(n)));
+  return static_cast<float>(static_cast<double>(g1) + (static_cast<double>(g0) - g1) * c);
 }
 
 int beam_moe_quant_e4m3(int64_t rows, int64_t cols, int32_t dtype,

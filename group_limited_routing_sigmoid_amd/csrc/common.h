@@ -47,6 +47,12 @@ __device__ __forceinline__ void dma16(const void* g, void* lds) {
                                    (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
+// As dma16 with 4 bytes per lane (lane l's dword lands at lds + 4*l).
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+
 // D = A(32x16) * B(16x32) + C on the matrix cores, bf16 inputs, fp32 sums.
 // Lane l supplies A row (l % 32) and B column (l % 32), k-block (l / 32).
 // Accumulator element r of lane l is C[8*(r/4) + 4*(l/32) + r%4][l % 32].

@@ -1,5 +1,6 @@
 // Expert MLPs as grouped matrix products on the gfx950 matrix cores (bf16
-// inputs, fp32 sums), for batches where each expert sees many tokens.
+// inputs, fp32 sums), for batches where each expert sees many tokens, and the
+// router's logits for such batches.
 //
 // Each expert is a SwiGLU MLP, hidden 5,120 -> intermediate 2,560 -> hidden
 // ("Hugging Face releases Beam ..." MoE paragraph; "Reflection Releases Beam
@@ -23,26 +24,32 @@
 // groups of 4 M tiles, then N tile, then M tile inside the group.  The ~32
 // workgroups an XCD runs at once then cover about 4 M tiles x 8 N tiles of
 // one expert and share both operands' current k-slices in its L2.
+//
+// Router logits for many tokens use the same tile loop as a dense product:
+// the fp32 router matrix is split exactly into three bf16 matrices, laid side
+// by side along k (W3 [E, 3H]) and multiplied with x repeated three times
+// (its column index wraps modulo H), so every product is exact and the sums
+// are fp32.  The reduction is split into ks slices; the router's selection
+// kernel adds the ks partial logits in a fixed order.
 #include "common.h"
 #include "internal.h"
 
 namespace beam {
 namespace {
 
-constexpr int BM = kGemmBM;  // 256 slots
+constexpr int BM = kGemmBM;  // 256 rows
 constexpr int BN = 256;
 constexpr int BK = 64;
 constexpr int kThreads = 512;
-constexpr int kRowBytes = BK * 2;        // 128 bytes per tile row in LDS
+constexpr int kRowBytes = BK * 2;           // 128 bytes per tile row in LDS
 constexpr int kTileBytes = BM * kRowBytes;  // 32 KiB per operand tile
 constexpr int kXcds = 8;
-#ifndef BEAM_GROUP_M
-#define BEAM_GROUP_M 4
-#endif
-constexpr int kGroupM = BEAM_GROUP_M;  // M tiles per rasterisation group
-constexpr int kLoads = (BM * BK * 2) / (16 * kThreads);  // 16-byte chunks per thread per operand
+constexpr int kGroupM = 4;                  // M tiles per rasterisation group
+constexpr int kLoads = (BM * BK * 2) / (16 * kThreads);  // DMA regions per wave per operand
 
 enum Mode { kGateUp = 0, kDown = 1 };
+
+typedef unsigned char TileLds[2][2 * kTileBytes];
 
 __device__ __forceinline__ int swz(int row, int chunk) {
   // the 8 chunks of any 8 consecutive rows land on distinct bank groups,
@@ -50,98 +57,36 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kRowBytes + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
 }
 
-// Largest e with tile_off[e] * n_nt <= L (tile_off is non-decreasing).
-__device__ __forceinline__ int find_expert(const int32_t* tile_off, int E, int n_nt, int L) {
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tile_off[mid] * n_nt <= L) lo = mid; else hi = mid - 1;
-  }
-  return lo;
+// Tile row and logical 16-byte chunk that lane `lane` of wave `wave` loads in
+// DMA region i: one region = 1 KiB = 8 tile rows, lane l writing physical
+// chunk l % 8 of row l / 8; wave w fills regions w + 8i.
+__device__ __forceinline__ int dma_row(int wave, int lane, int i) {
+  return 8 * (wave + 8 * i) + lane / 8;
+}
+__device__ __forceinline__ int dma_chunk(int row, int lane) {
+  return (lane % 8) ^ ((row ^ (row >> 3)) & 7);
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(
-    const uint16_t* __restrict__ a_src,   // gate/up: x [T,H]; down: h [S,I]
-    const uint16_t* __restrict__ w,       // W_gu [E,2I,H] or W_d [E,H,I]
-    uint16_t* __restrict__ out,           // gate/up: h [S,I]; down: y [S,H]
-    const int32_t* __restrict__ slot_token, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off,
-    const int32_t* __restrict__ meta, int E, int H, int I, int n_nt) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2][2 * kTileBytes];
-
-  // ---- logical tile of this workgroup -------------------------------------
-  const int n_log = meta[kMetaTiles] * n_nt;
-  const int per_xcd = (n_log + kXcds - 1) / kXcds;
-  const int local = blockIdx.x / kXcds;
-  const int L = (blockIdx.x % kXcds) * per_xcd + local;
-  if (local >= per_xcd || L >= n_log) return;
-  const int e = find_expert(tile_off, E, n_nt, L);
-  const int t0 = tile_off[e], nt_e = tile_off[e + 1] - t0;
-  // Within an expert, groups of kGroupM M tiles walk the N tiles together,
-  // so the workgroups resident on one XCD share A and B k-slices in its L2.
-  const int j = L - t0 * n_nt;
-  const int g = j / (kGroupM * n_nt);
-  const int gm = min(kGroupM, nt_e - g * kGroupM);
-  const int jj = j - g * kGroupM * n_nt;
-  const int nt = jj / gm;
-  const int row0 = offsets[e] + (g * kGroupM + jj % gm) * BM;
-  const int row_end = offsets[e] + counts[e];  // first slot past this expert
-  const int K = (MODE == kGateUp) ? H : I;
-
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave, wave = tid / kWave;
-  const int wm = wave / 4, wn = wave % 4;
-
-  // ---- direct-to-LDS loads: one instruction fills 1 KiB = 8 tile rows, lane
-  // l writing physical chunk l % 8 of row l / 8; it fetches the logical chunk
-  // the swizzle maps there.  Wave w fills A regions w + 8i and B regions
-  // w + 8i (i = 0..3) of each stage.
-  const uint16_t* wbase = (MODE == kGateUp) ? w + static_cast<int64_t>(e) * 2 * I * H
-                                            : w + static_cast<int64_t>(e) * H * I;
-  uint32_t a_off[kLoads], b_off[kLoads];
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const int r = 8 * (wave + 8 * i) + lane / 8;            // tile row
-    const int c = (lane % 8) ^ ((r ^ (r >> 3)) & 7);         // logical chunk
-    int slot = row0 + r;
-    if (slot > row_end - 1) slot = row_end - 1;              // padded rows: any valid row
-    if (MODE == kGateUp) {
-      a_off[i] = static_cast<uint32_t>(slot_token[slot]) * H + c * 8;
-      // rows 0..127: gate channels nt*128 + r; rows 128..255: up channels
-      const int wrow = (r < 128) ? (nt * 128 + r) : (I + nt * 128 + (r - 128));
-      b_off[i] = static_cast<uint32_t>(wrow) * H + c * 8;
-    } else {
-      a_off[i] = static_cast<uint32_t>(slot) * I + c * 8;
-      b_off[i] = static_cast<uint32_t>(nt * BN + r) * I + c * 8;
-    }
-  }
-  auto dma = [&](int buf, int k0) {
+// acc[i][n] += A[arow_i] . B[brow_n] over columns [k0, k0 + nk*BK) of B;
+// A's column is the same index modulo a_period (a_period >= k0 + nk*BK when
+// A is as wide as B).  a_off / b_off: this lane's element offsets (from
+// a_base / b_base) of its kLoads A and B rows, chunk included.  arow / brow:
+// tile rows whose fragments this lane feeds to the MFMAs.  Ends with a
+// barrier.
+__device__ __forceinline__ void tile_mainloop(
+    const uint16_t* __restrict__ a_base, const uint32_t* a_off, int a_period,
+    const uint16_t* __restrict__ b_base, const uint32_t* b_off, int k0, int nk,
+    TileLds& lds, f32x16 (&acc)[4][2], const int* arow, const int* brow) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  auto dma = [&](int buf, int k) {
+    const int ka = k % a_period;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int region = wave + 8 * i;
-      dma16(a_src + (a_off[i] + k0), &lds[buf][region * 1024]);
-      dma16(wbase + (b_off[i] + k0), &lds[buf][kTileBytes + region * 1024]);
+      dma16(a_base + (a_off[i] + ka), &lds[buf][region * 1024]);
+      dma16(b_base + (b_off[i] + k), &lds[buf][kTileBytes + region * 1024]);
     }
   };
-
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int n = 0; n < 2; ++n) acc[i][n] = f32x16{};
-
-  // A rows of this wave: wm*128 + mi*32 + lane%32.
-  // B rows: gate/up -> gate wn*32 + lane%32 and up 128 + wn*32 + lane%32;
-  //         down    -> wn*64 + ni*32 + lane%32.
-  int arow[4], brow[2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) arow[i] = wm * 128 + i * 32 + lane % 32;
-#pragma unroll
-  for (int n = 0; n < 2; ++n)
-    brow[n] = (MODE == kGateUp) ? (n * 128 + wn * 32 + lane % 32)
-                                : (wn * 64 + n * 32 + lane % 32);
-
   struct Frags {
     bf16x8 a[4], b[2];
   };
@@ -180,17 +125,97 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(
     __builtin_amdgcn_sched_barrier(0);
     mfmas(f1);
   };
-
-  const int nk = K / BK;
-  dma(0, 0);
+  dma(0, k0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     // buffer buf^1 was last read before the barrier that ended step kt-1
-    if (kt + 1 < nk) dma(buf ^ 1, (kt + 1) * BK);
+    if (kt + 1 < nk) dma(buf ^ 1, k0 + (kt + 1) * BK);
     compute(buf);
     __syncthreads();  // waits for this wave's loads, then for every wave
   }
+}
+
+// Largest e with tile_off[e] * n_nt <= L (tile_off is non-decreasing).
+__device__ __forceinline__ int find_expert(const int32_t* tile_off, int E, int n_nt, int L) {
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tile_off[mid] * n_nt <= L) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(
+    const uint16_t* __restrict__ a_src,   // gate/up: x [T,H]; down: h [S,I]
+    const uint16_t* __restrict__ w,       // W_gu [E,2I,H] or W_d [E,H,I]
+    uint16_t* __restrict__ out,           // gate/up: h [S,I]; down: y [S,H]
+    const int32_t* __restrict__ slot_token, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off,
+    const int32_t* __restrict__ meta, int E, int H, int I, int n_nt) {
+  __shared__ __attribute__((aligned(16))) TileLds lds;
+
+  // ---- logical tile of this workgroup -------------------------------------
+  const int n_log = meta[kMetaTiles] * n_nt;
+  const int per_xcd = (n_log + kXcds - 1) / kXcds;
+  const int local = blockIdx.x / kXcds;
+  const int L = (blockIdx.x % kXcds) * per_xcd + local;
+  if (local >= per_xcd || L >= n_log) return;
+  const int e = find_expert(tile_off, E, n_nt, L);
+  const int t0 = tile_off[e], nt_e = tile_off[e + 1] - t0;
+  // Within an expert, groups of kGroupM M tiles walk the N tiles together,
+  // so the workgroups resident on one XCD share A and B k-slices in its L2.
+  const int j = L - t0 * n_nt;
+  const int g = j / (kGroupM * n_nt);
+  const int gm = min(kGroupM, nt_e - g * kGroupM);
+  const int jj = j - g * kGroupM * n_nt;
+  const int nt = jj / gm;
+  const int row0 = offsets[e] + (g * kGroupM + jj % gm) * BM;
+  const int row_end = offsets[e] + counts[e];  // first slot past this expert
+  const int K = (MODE == kGateUp) ? H : I;
+
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int wm = wave / 4, wn = wave % 4;
+
+  // 32-bit element offsets from wave-uniform bases (the caller guarantees
+  // S * max(H, I) < 2^31; one expert's weights are far below that).
+  const uint16_t* wbase = (MODE == kGateUp) ? w + static_cast<int64_t>(e) * 2 * I * H
+                                            : w + static_cast<int64_t>(e) * H * I;
+  uint32_t a_off[kLoads], b_off[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int r = dma_row(wave, lane, i);
+    const int c = dma_chunk(r, lane);
+    int slot = row0 + r;
+    if (slot > row_end - 1) slot = row_end - 1;  // padded rows: any valid row
+    if (MODE == kGateUp) {
+      a_off[i] = static_cast<uint32_t>(slot_token[slot]) * H + c * 8;
+      // rows 0..127: gate channels nt*128 + r; rows 128..255: up channels
+      const int wrow = (r < 128) ? (nt * 128 + r) : (I + nt * 128 + (r - 128));
+      b_off[i] = static_cast<uint32_t>(wrow) * H + c * 8;
+    } else {
+      a_off[i] = static_cast<uint32_t>(slot) * I + c * 8;
+      b_off[i] = static_cast<uint32_t>(nt * BN + r) * I + c * 8;
+    }
+  }
+  // A rows of this wave: wm*128 + mi*32 + lane%32.
+  // B rows: gate/up -> gate wn*32 + lane%32 and up 128 + wn*32 + lane%32;
+  //         down    -> wn*64 + ni*32 + lane%32.
+  int arow[4], brow[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) arow[i] = wm * 128 + i * 32 + lane % 32;
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+    brow[n] = (MODE == kGateUp) ? (n * 128 + wn * 32 + lane % 32)
+                                : (wn * 64 + n * 32 + lane % 32);
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) acc[i][n] = f32x16{};
+  tile_mainloop(a_src, a_off, K, wbase, b_off, 0, K / BK, lds, acc, arow, brow);
 
   // ---- epilogue -------------------------------------------------------------
 #pragma unroll
@@ -214,7 +239,69 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(
   }
 }
 
+// Router logits partials: part[z][t][e] = sum over k' in [z c, (z+1) c) of
+// x[t, k' mod H] W3[e, k'] with c = 3H/ks (W3 [E, 3H] holds the three bf16
+// terms of W_r one after another along k').  grid = ceil(T/256) * E/256 * ks.
+__global__ __launch_bounds__(kThreads) void router_gemm_bf16(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w3,
+    float* __restrict__ part, int T, int E, int H, int ks) {
+  __shared__ __attribute__((aligned(16))) TileLds lds;
+  const int n_nt = E / BN;
+  const int per_m = n_nt * ks;
+  const int mt = blockIdx.x / per_m;
+  const int nt = (blockIdx.x % per_m) / ks;
+  const int z = blockIdx.x % ks;
+  const int row0 = mt * BM;
+  const int kc = 3 * H / ks;
+
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int wm = wave / 4, wn = wave % 4;
+  uint32_t a_off[kLoads], b_off[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int r = dma_row(wave, lane, i);
+    const int c = dma_chunk(r, lane);
+    const int t = min(row0 + r, T - 1);  // padded rows: any valid row
+    a_off[i] = static_cast<uint32_t>(t) * H + c * 8;
+    b_off[i] = static_cast<uint32_t>(nt * BN + r) * (3 * H) + c * 8;
+  }
+  int arow[4], brow[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) arow[i] = wm * 128 + i * 32 + lane % 32;
+#pragma unroll
+  for (int n = 0; n < 2; ++n) brow[n] = wn * 64 + n * 32 + lane % 32;
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) acc[i][n] = f32x16{};
+  tile_mainloop(x, a_off, H, w3, b_off, z * kc, kc / BK, lds, acc, arow, brow);
+
+  float* dst = part + static_cast<int64_t>(z) * T * E + nt * BN;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = row0 + wm * 128 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+      if (t >= T) continue;
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+        dst[static_cast<int64_t>(t) * E + wn * 64 + n * 32 + lane % 32] = acc[i][n][r];
+    }
+}
+
 }  // namespace
+
+hipError_t launch_router_gemm(const Plan& p, const void* x, const uint16_t* w3,
+                              float* part, hipStream_t s, Timer* tm) {
+  const int n_nt = p.E / BN;
+  const unsigned grid = static_cast<unsigned>(ceil_div(p.T, BM) * n_nt * p.ks);
+  BEAM_LAUNCH(tm, "router_gemm_bf16", router_gemm_bf16, dim3(grid), dim3(kThreads), 0, s,
+              static_cast<const uint16_t*>(x), w3, part, static_cast<int>(p.T), p.E, p.H,
+              p.ks);
+  return hipGetLastError();
+}
 
 hipError_t launch_grouped_bf16(const Plan& p, const void* x,
                                const void* w_gate_up, const void* w_down,

@@ -22,13 +22,14 @@ struct Plan {
   uint32_t flags;
   int64_t T, S;        // tokens, slots (= T*K)
   int64_t nb;          // permutation blocks
-  int32_t ks;          // router reduction split
+  int32_t ks;          // partial logits the router selection sums
+  bool router_gemm;    // logits by the dense tile GEMM (many tokens)
   bool stream_path;    // weight-streaming experts (few tokens per expert)
   int64_t max_tiles;   // upper bound on grouped-GEMM M tiles
   // byte offsets into the workspace
   size_t off_part, off_idx, off_w, off_hist, off_base, off_rank, off_counts,
       off_offsets, off_slot_token, off_slot_of, off_tile_expert, off_tile_row0,
-      off_meta, off_active, off_tile_off, off_h, off_y, off_xq, off_xs,
+      off_meta, off_active, off_tile_off, off_w3, off_h, off_y, off_xq, off_xs,
       off_hq, off_hs;
   size_t total;
 };
@@ -62,10 +63,15 @@ hipError_t launch_router(const Plan& p, const void* x, const float* w_router,
                          const float* bias, float* logits_out,
                          const float* logits_in, int32_t* idx, float* w,
                          void* ws, hipStream_t s, Timer* tm);
+// experts_grouped.hip: router logits partials by the dense tile GEMM
+hipError_t launch_router_gemm(const Plan& p, const void* x, const uint16_t* w3,
+                              float* part, hipStream_t s, Timer* tm);
 // permute.hip
 hipError_t launch_permute(const Plan& p, const int32_t* idx, int32_t* counts,
                           int32_t* offsets, int32_t* slot_token,
                           int32_t* slot_of, void* ws, hipStream_t s, Timer* tm);
+hipError_t launch_bias_update(const Plan& p, const int32_t* idx, float gamma,
+                              float* bias, hipStream_t s, Timer* tm);
 // experts_grouped.hip (bf16 weights, tiled MFMA grouped GEMM)
 hipError_t launch_grouped_bf16(const Plan& p, const void* x,
                                const void* w_gate_up, const void* w_down,

@@ -14,6 +14,9 @@
 //                 grouped-GEMM M-tile list (with each expert's first tile)
 //                 and the list of active experts.
 //   perm_scatter  slot = offsets[e] + block base + rank.
+//   bias_update   the expert-bias balancing step on the same histogram idea
+//                 ("Reflection AI Introduces Beam ...", load-balancing
+//                 paragraph; DeepSeek-V3's bias-update rule).
 #include "common.h"
 #include "internal.h"
 
@@ -124,7 +127,34 @@ __global__ __launch_bounds__(kPermBlock) void perm_scatter(
   }
 }
 
+// Expert-bias balancing step: one workgroup; integer histogram in LDS, then
+// bias[e] += gamma * sign(T*K - load_e*E) with the sign taken in integers.
+__global__ __launch_bounds__(kMaxE) void bias_update(
+    const int32_t* __restrict__ idx, int64_t TK, int E, float gamma,
+    float* __restrict__ bias) {
+  __shared__ int load[kMaxE];
+  for (int e = threadIdx.x; e < E; e += kMaxE) load[e] = 0;
+  __syncthreads();
+  for (int64_t i = threadIdx.x; i < TK; i += kMaxE) {
+    const uint32_t e = static_cast<uint32_t>(idx[i]);
+    if (e < static_cast<uint32_t>(E)) atomicAdd(&load[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kMaxE) {
+    const int64_t lhs = static_cast<int64_t>(load[e]) * E;
+    const float step = (lhs < TK) ? gamma : ((lhs > TK) ? -gamma : 0.0f);
+    bias[e] = bias[e] + step;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_bias_update(const Plan& p, const int32_t* idx, float gamma,
+                              float* bias, hipStream_t s, Timer* tm) {
+  BEAM_LAUNCH(tm, "bias_update", bias_update, dim3(1), dim3(kMaxE), 0, s, idx,
+              p.S, p.E, gamma, bias);
+  return hipGetLastError();
+}
 
 hipError_t launch_permute(const Plan& p, const int32_t* idx, int32_t* counts,
                           int32_t* offsets, int32_t* slot_token,

@@ -10,8 +10,10 @@
 // group score is the sum of a group's best two biased scores, DeepSeek-V3's
 // rule (arXiv 2412.19437, section 2.1.2), which the pages invoke.
 //
-// Two kernels:
-//   router_logits_*  logits = x W_r^T in fp32.  With bf16 activations the
+// Kernels:
+//   router_logits_*  logits = x W_r^T in fp32 (for many tokens the same
+//                    three-term split feeds the dense tile GEMM of the
+//                    grouped expert path, split over H).  With bf16 activations the
 //                    fp32 router weights are split exactly into three bf16
 //                    terms (hi + mid + lo), so every product is exact and the
 //                    matrix cores accumulate in fp32.  The reduction over H
@@ -89,6 +91,25 @@ __global__ __launch_bounds__(64) void router_logits_mfma(
       out[t * E + e0 + 32 + lane % 32] = acc1[r];
     }
   }
+}
+
+// ---- exact three-term bf16 split of the fp32 router matrix ---------------
+// w3 [E, 3H]: row e = [smallest term | middle term | bf16 rounding of W_r[e]];
+// the three add up to W_r[e] exactly.
+__global__ __launch_bounds__(256) void router_split(const float* __restrict__ wr,
+                                                    uint16_t* __restrict__ w3, int E, int H) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(E) * H) return;
+  const int64_t e = i / H, k = i % H;
+  const float v = wr[i];
+  const bf16 h = static_cast<bf16>(v);
+  const float r1 = v - static_cast<float>(h);
+  const bf16 m = static_cast<bf16>(r1);
+  const float r2 = r1 - static_cast<float>(m);
+  uint16_t* row = w3 + e * 3 * H;
+  row[k] = __builtin_bit_cast(uint16_t, static_cast<bf16>(r2));
+  row[H + k] = __builtin_bit_cast(uint16_t, m);
+  row[2 * H + k] = __builtin_bit_cast(uint16_t, h);
 }
 
 // ---- logits: generic fp32 dot products (fp32 activations, small layers) --
@@ -273,7 +294,14 @@ hipError_t launch_router(const Plan& p, const void* x, const float* w_router,
     ks = p.ks;
     float* buf = ws_at<float>(ws, p.off_part);
     const int kchunk = p.H / ks;
-    if (p.act == BEAM_BF16 && p.E % 64 == 0) {
+    if (p.router_gemm) {
+      uint16_t* w3 = ws_at<uint16_t>(ws, p.off_w3);
+      const int64_t n = static_cast<int64_t>(p.E) * p.H;
+      BEAM_LAUNCH(tm, "router_split", router_split, dim3(static_cast<unsigned>(ceil_div(n, 256))),
+                  dim3(256), 0, s, w_router, w3, p.E, p.H);
+      const hipError_t e = launch_router_gemm(p, x, w3, buf, s, tm);
+      if (e != hipSuccess) return e;
+    } else if (p.act == BEAM_BF16 && p.E % 64 == 0) {
       dim3 grid(static_cast<unsigned>(ceil_div(p.T, 32)), p.E / 64, ks);
       BEAM_LAUNCH(tm, "router_logits_mfma", router_logits_mfma, grid, dim3(64), 0, s,
                          static_cast<const uint16_t*>(x), w_router, buf, p.T,

@@ -160,6 +160,28 @@ int beam_moe_forward(const beam_moe_desc* desc, int64_t T, const void* x,
                      int32_t* topk_idx, float* topk_w, float* logits,
                      void* workspace, size_t ws_bytes, void* stream);
 
+/* Auxiliary-loss-free load balancing step.  The load-balancing paragraph of
+ * "Reflection AI Introduces Beam ..." says Beam builds on DeepSeek-V3's
+ * bias-update balancing with a cosine decay of the update speed; the rule
+ * (arXiv 2412.19437 section 2.1.2) moves each expert's selection bias
+ * towards balance after a batch:
+ *   load_e = #{(t, k) : topk_idx[t, k] == e}
+ *   bias[e] = bias[e] + gamma * sign(T*K/E - load_e)
+ * with the sign decided exactly in integers (load_e*E against T*K; sign 0
+ * leaves the bias unchanged) and one binary32 addition.
+ *   topk_idx  device [T, K] int32 (a routing, e.g. beam_moe_route's);
+ *             entries outside [0, E) are not counted
+ *   bias      device [E] fp32, updated in place
+ * gamma >= 0 and finite (see beam_moe_bias_gamma).  No workspace. */
+int beam_moe_bias_update(const beam_moe_desc* desc, int64_t T,
+                         const int32_t* topk_idx, float gamma, float* bias,
+                         void* stream);
+
+/* Update speed for step t of an n-step cosine schedule from g0 down to g1:
+ * g1 + (g0 - g1) * (1 + cos(pi * t / n)) / 2, evaluated in binary64 and
+ * rounded to binary32; t is clamped to [0, n].  Host only. */
+float beam_moe_bias_gamma(int64_t t, int64_t n, float g0, float g1);
+
 /* ---- measurement support ------------------------------------------------
  * A timer records a HIP event pair around every kernel a timed forward
  * launches, on the stream the kernel runs on, so tools can read per-kernel

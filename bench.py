@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode64")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="override the workload's token count (decode/verify sweep)")
     ap.add_argument("--path", choices=["auto", "stream", "grouped"], default="auto")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -66,6 +68,20 @@ def traffic_for(kernel, workload):
         return None
     h = hashlib.sha256(open(src, "rb").read()).hexdigest()
     return rec["bytes_per_launch"] if h == rec["source_sha256"] else None
+
+
+def read_sclk():
+    """Current shader clock level in MHz from the amdgpu sysfs table, or None."""
+    import glob
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(f):
+                if line.rstrip().endswith("*"):
+                    return int(line.split(":")[1].strip().rstrip("*").strip()
+                               .lower().rstrip("mhz").strip())
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
 
 
 def cpu_baseline(inp, shape, seconds):
@@ -132,7 +148,7 @@ def main():
     w = WORKLOADS[a.workload]
     sh = w.shape
     dev = torch.device("cuda:0")
-    inp = make_inputs(w, device=dev)
+    inp = make_inputs(w, device=dev, tokens=a.tokens)
     T, H, I, E, K = inp.x.shape[0], sh.hidden, sh.intermediate, sh.n_experts, sh.top_k
     S = T * K
     flags = {"auto": 0, "stream": gl.PATH_STREAM, "grouped": gl.PATH_GROUPED}[a.path]
@@ -155,14 +171,16 @@ def main():
         step()
     timer = gl.Timer(capacity=64 * max(a.steps, 1))
     stream = torch.cuda.current_stream()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     torch.cuda.synchronize()
-    t0.record(stream)
-    for _ in range(a.steps):
+    ev[0].record(stream)
+    for i in range(a.steps):
         step(timer)
-    t1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / a.steps
+    ms = ev[0].elapsed_time(ev[-1]) / a.steps
+    step_ms = np.sort([ev[i].elapsed_time(ev[i + 1]) for i in range(a.steps)])
+    sclk = read_sclk()
     per = {}
     for name, kms in timer.records():
         per.setdefault(name, []).append(kms)
@@ -171,21 +189,24 @@ def main():
     dom = max(kern_ms, key=lambda k: kern_ms[k] * launches[k])
     wbytes = 1 if w.weight_dtype == FP8 else (4 if w.weight_dtype == "f32" else 2)
     kb, kf = kernel_bytes_flops(dom, T, S, H, I, E, touched, wbytes)
-    mem_bound = S <= 16 * E
-    if mem_bound or kf is None:
+    peak = FP8_PEAK_TFLOPS if w.weight_dtype == FP8 else (
+        FP32_PEAK_TFLOPS if w.weight_dtype == "f32" else BF16_PEAK_TFLOPS)
+    # the kernel's bound is the larger of its memory time and its compute time
+    mem_bound = kf is None or kb / (HBM_PEAK_GBS * 1e9) >= kf / (peak * 1e12)
+    if mem_bound:
         ach = kb / (kern_ms[dom] * 1e-3) / 1e9 if kb else None
         roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": ach / HBM_PEAK_GBS if ach else None,
                 "traffic": traffic_for(dom, a.workload), "kernel": dom,
                 "kernel_ms": kern_ms[dom], "algorithmic_bytes": kb}
     else:
-        peak = FP8_PEAK_TFLOPS if w.weight_dtype == FP8 else BF16_PEAK_TFLOPS
         ach = kf / (kern_ms[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
                 "frac": ach / peak, "traffic": traffic_for(dom, a.workload),
                 "kernel": dom, "kernel_ms": kern_ms[dom], "algorithmic_flops": kf}
     layer_bytes = touched * 3 * H * I * wbytes + E * H * 4 + 2 * T * H * inp.x.element_size()
     layer_flops = 2.0 * S * 3 * H * I
+    roof_ms = max(layer_bytes / (HBM_PEAK_GBS * 1e9), layer_flops / (peak * 1e12)) * 1e3
     res = {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
@@ -194,6 +215,8 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": ms,
+        "step_ms": {"median": float(np.median(step_ms)), "min": float(step_ms[0]),
+                    "p90": float(step_ms[min(len(step_ms) - 1, int(0.9 * len(step_ms)))])},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -208,9 +231,12 @@ def main():
         "layer": {"hbm_GBps": layer_bytes / (ms * 1e-3) / 1e9,
                   "hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                   "mfma_TFLOPs": layer_flops / (ms * 1e-3) / 1e12,
-                  "mfma_frac": layer_flops / (ms * 1e-3) / 1e12 / (
-                      FP8_PEAK_TFLOPS if w.weight_dtype == FP8 else BF16_PEAK_TFLOPS),
+                  "mfma_frac": layer_flops / (ms * 1e-3) / 1e12 / peak,
+                  "bound": "hbm" if layer_bytes / (HBM_PEAK_GBS * 1e9) >=
+                           layer_flops / (peak * 1e12) else "mfma",
+                  "roofline_ms": roof_ms, "roofline_frac": roof_ms / ms,
                   "algorithmic_bytes": layer_bytes, "expert_flops": layer_flops},
+        "sclk_mhz": sclk,
         "routing": {"touched_experts": touched,
                     "max_over_mean_load": float(counts.max() / counts.mean())},
         "kernels_ms": kern_ms,

@@ -82,7 +82,7 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
   else if (p->flags & BEAM_PATH_GROUPED)
     p->stream_path = false;
   else
-    p->stream_path = p->S <= 16 * static_cast<int64_t>(p->E);
+    p->stream_path = p->S < 4 * static_cast<int64_t>(p->E);
   // streaming kernels exist for bf16 weights only
   if (p->wdt != BEAM_BF16) p->stream_path = false;
   const int64_t S = p->S, E = p->E, H = p->H, I = p->I;

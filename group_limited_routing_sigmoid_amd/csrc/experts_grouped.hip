@@ -67,23 +67,27 @@ __device__ __forceinline__ int dma_chunk(int row, int lane) {
   return (lane % 8) ^ ((row ^ (row >> 3)) & 7);
 }
 
-// acc[i][n] += A[arow_i] . B[brow_n] over columns [k0, k0 + nk*BK) of B;
-// A's column is the same index modulo a_period (a_period >= k0 + nk*BK when
-// A is as wide as B).  a_off / b_off: this lane's element offsets (from
-// a_base / b_base) of its kLoads A and B rows, chunk included.  arow / brow:
-// tile rows whose fragments this lane feeds to the MFMAs.  Ends with a
-// barrier.
+// acc[i][n] += A[arow_i] . B[brow_n] over columns [k0, k0 + nk*BK) of B,
+// for the first NF of the wave's four 32-row A fragments (the others hold
+// only padding rows past the tile's last valid row and are skipped).  A's
+// column is the same index modulo a_period (a_period >= k0 + nk*BK when A is
+// as wide as B).  a_off / b_off: this lane's element offsets (from a_base /
+// b_base) of its kLoads A and B rows, chunk included; a_ok[i]: whether A row
+// i is a valid row (padding rows are not loaded: their LDS rows only feed
+// output rows that are never stored).  arow / brow: tile rows whose
+// fragments this lane feeds to the MFMAs.  Ends with a barrier.
+template <int NF>
 __device__ __forceinline__ void tile_mainloop(
-    const uint16_t* __restrict__ a_base, const uint32_t* a_off, int a_period,
-    const uint16_t* __restrict__ b_base, const uint32_t* b_off, int k0, int nk,
-    TileLds& lds, f32x16 (&acc)[4][2], const int* arow, const int* brow) {
+    const uint16_t* __restrict__ a_base, const uint32_t* a_off, const bool* a_ok,
+    int a_period, const uint16_t* __restrict__ b_base, const uint32_t* b_off, int k0,
+    int nk, TileLds& lds, f32x16 (&acc)[4][2], const int* arow, const int* brow) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   auto dma = [&](int buf, int k) {
     const int ka = k % a_period;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int region = wave + 8 * i;
-      dma16(a_base + (a_off[i] + ka), &lds[buf][region * 1024]);
+      if (a_ok[i]) dma16(a_base + (a_off[i] + ka), &lds[buf][region * 1024]);
       dma16(b_base + (b_off[i] + k), &lds[buf][kTileBytes + region * 1024]);
     }
   };
@@ -93,7 +97,7 @@ __device__ __forceinline__ void tile_mainloop(
   auto load_frags = [&](Frags& f, int buf, int kk) {
     const int c = kk * 2 + lane / 32;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NF; ++i)
       f.a[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&lds[buf][swz(arow[i], c)]));
 #pragma unroll
     for (int n = 0; n < 2; ++n)
@@ -101,7 +105,7 @@ __device__ __forceinline__ void tile_mainloop(
   };
   auto mfmas = [&](const Frags& f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NF; ++i)
 #pragma unroll
       for (int n = 0; n < 2; ++n) acc[i][n] = mfma32x32x16(f.a[i], f.b[n], acc[i][n]);
   };
@@ -131,9 +135,29 @@ __device__ __forceinline__ void tile_mainloop(
     const int buf = kt & 1;
     // buffer buf^1 was last read before the barrier that ended step kt-1
     if (kt + 1 < nk) dma(buf ^ 1, k0 + (kt + 1) * BK);
-    compute(buf);
+    if (NF > 0) compute(buf);
     __syncthreads();  // waits for this wave's loads, then for every wave
   }
+}
+
+// tile_mainloop with the wave's fragment count nf (0..4) made a constant.
+__device__ __forceinline__ void tile_mainloop_rows(
+    int nf, const uint16_t* __restrict__ a_base, const uint32_t* a_off, const bool* a_ok,
+    int a_period, const uint16_t* __restrict__ b_base, const uint32_t* b_off, int k0,
+    int nk, TileLds& lds, f32x16 (&acc)[4][2], const int* arow, const int* brow) {
+  switch (nf) {
+    case 4: tile_mainloop<4>(a_base, a_off, a_ok, a_period, b_base, b_off, k0, nk, lds, acc, arow, brow); break;
+    case 3: tile_mainloop<3>(a_base, a_off, a_ok, a_period, b_base, b_off, k0, nk, lds, acc, arow, brow); break;
+    case 2: tile_mainloop<2>(a_base, a_off, a_ok, a_period, b_base, b_off, k0, nk, lds, acc, arow, brow); break;
+    case 1: tile_mainloop<1>(a_base, a_off, a_ok, a_period, b_base, b_off, k0, nk, lds, acc, arow, brow); break;
+    default: tile_mainloop<0>(a_base, a_off, a_ok, a_period, b_base, b_off, k0, nk, lds, acc, arow, brow); break;
+  }
+}
+
+// Number of the wave's 32-row A fragments (rows wm*128 + 32 i ...) that hold
+// at least one of the tile's m_valid rows.
+__device__ __forceinline__ int wave_frags(int m_valid, int wm) {
+  return min(4, max(0, (m_valid - wm * 128 + 31) / 32));
 }
 
 // Largest e with tile_off[e] * n_nt <= L (tile_off is non-decreasing).
@@ -182,11 +206,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(
   // S * max(H, I) < 2^31; one expert's weights are far below that).
   const uint16_t* wbase = (MODE == kGateUp) ? w + static_cast<int64_t>(e) * 2 * I * H
                                             : w + static_cast<int64_t>(e) * H * I;
+  const int m_valid = min(BM, row_end - row0);
   uint32_t a_off[kLoads], b_off[kLoads];
+  bool a_ok[kLoads];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     const int r = dma_row(wave, lane, i);
     const int c = dma_chunk(r, lane);
+    a_ok[i] = r < m_valid;
     int slot = row0 + r;
     if (slot > row_end - 1) slot = row_end - 1;  // padded rows: any valid row
     if (MODE == kGateUp) {
@@ -215,7 +242,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int n = 0; n < 2; ++n) acc[i][n] = f32x16{};
-  tile_mainloop(a_src, a_off, K, wbase, b_off, 0, K / BK, lds, acc, arow, brow);
+  tile_mainloop_rows(wave_frags(m_valid, wm), a_src, a_off, a_ok, K, wbase, b_off, 0,
+                     K / BK, lds, acc, arow, brow);
 
   // ---- epilogue -------------------------------------------------------------
 #pragma unroll
@@ -256,11 +284,14 @@ __global__ __launch_bounds__(kThreads) void router_gemm_bf16(
 
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int wm = wave / 4, wn = wave % 4;
+  const int m_valid = min(BM, T - row0);
   uint32_t a_off[kLoads], b_off[kLoads];
+  bool a_ok[kLoads];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     const int r = dma_row(wave, lane, i);
     const int c = dma_chunk(r, lane);
+    a_ok[i] = r < m_valid;
     const int t = min(row0 + r, T - 1);  // padded rows: any valid row
     a_off[i] = static_cast<uint32_t>(t) * H + c * 8;
     b_off[i] = static_cast<uint32_t>(nt * BN + r) * (3 * H) + c * 8;
@@ -276,7 +307,8 @@ __global__ __launch_bounds__(kThreads) void router_gemm_bf16(
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int n = 0; n < 2; ++n) acc[i][n] = f32x16{};
-  tile_mainloop(x, a_off, H, w3, b_off, z * kc, kc / BK, lds, acc, arow, brow);
+  tile_mainloop_rows(wave_frags(m_valid, wm), x, a_off, a_ok, H, w3, b_off, z * kc,
+                     kc / BK, lds, acc, arow, brow);
 
   float* dst = part + static_cast<int64_t>(z) * T * E + nt * BN;
 #pragma unroll

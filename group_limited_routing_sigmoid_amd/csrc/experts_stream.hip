@@ -1,17 +1,17 @@
 // Expert MLPs for decode-sized batches: each touched expert sees only a few
 // tokens, so the work is bound by reading its weights once from HBM.  The
 // weights are the 16-row A side of 16x16x32 bf16 MFMA and up to 16 tokens
-// are the B side.  Gate/up: one wave streams 32 rows over the whole hidden
-// dimension.  Down (rows half as long): the reduction over the intermediate
-// dimension is split over the 4 waves of a workgroup and summed in LDS in a
-// fixed order.  Experts with more than 16 tokens are handled in chunks of 16.
+// are the B side.  Gate/up: one wave streams 32 rows (16 gate, 16 up) over
+// the whole hidden dimension; down: one wave streams 16 rows of W_d over the
+// whole intermediate dimension.  No cross-wave reduction.  Experts with more
+// than 16 tokens are handled in chunks of 16.
 //
 // Same SwiGLU expert as the grouped path ("Hugging Face releases Beam ..."
 // MoE paragraph): h = silu(x W_g^T) * (x W_u^T) for gate/up, y = h W_d^T for
 // down.  h is kept in bf16 (the down product's input); y in fp32.
 //
 // Work items: (active expert j, 16-channel block) for gate/up and (active
-// expert j, 32-row block of W_d) for down.  The grid covers every expert
+// expert j, 16-row block of W_d) for down.  The grid covers every expert
 // that could be active; items past the device-side count exit at once, so
 // the host never waits for the routing result.
 #include "common.h"
@@ -22,7 +22,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kUnroll = 8;   // k-steps of 32 in flight per wave
 
 // One wave per (active expert j, 16-channel block): it streams the 16 gate
 // and 16 up rows over the whole hidden dimension with two independent
@@ -83,92 +82,57 @@ __global__ __launch_bounds__(kThreads) void stream_gate_up(
   }
 }
 
-// Down: a work item is (active expert j, 16*kDnTiles rows of W_d); its
-// reduction over I is split over kDnSplit waves and summed in LDS in a fixed
-// order.  A workgroup of 4 waves holds 4 / kDnSplit items.
-#ifndef BEAM_DN_TILES
-#define BEAM_DN_TILES 2
-#endif
-#ifndef BEAM_DN_SPLIT
-#define BEAM_DN_SPLIT 4
-#endif
+// Down: one wave per (active expert j, 16-row block of W_d), streaming the
+// 16 rows over the whole intermediate dimension with two accumulator chains
+// (even and odd k-steps) added once at the end.
+// grid ceil(max_active * H/16 / 4), block 256 (4 work items per workgroup)
 #ifndef BEAM_DN_UNROLL
-#define BEAM_DN_UNROLL 8
+#define BEAM_DN_UNROLL 20
 #endif
-constexpr int kDnTiles = BEAM_DN_TILES;
-constexpr int kDnSplit = BEAM_DN_SPLIT;
-constexpr int kDnUnroll = BEAM_DN_UNROLL;
-constexpr int kDnRows = 16 * kDnTiles;
-constexpr int kDnItems = kWaves / kDnSplit;
+constexpr int kDnUnroll = BEAM_DN_UNROLL;  // k-steps of 32 in flight per wave
 
 __global__ __launch_bounds__(kThreads) void stream_down(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ w_d,
     float* __restrict__ y, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
     const int32_t* __restrict__ meta, int H, int I) {
-  __shared__ f32x4 red[kWaves][kDnTiles][kWave];
-  const int n_ob = H / kDnRows;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int item = blockIdx.x * kDnItems + wave / kDnSplit;
-  const int part = wave % kDnSplit;
+  const int n_ob = H / 16;
+  const int item = blockIdx.x * kWaves + threadIdx.x / kWave;
   const int j = item / n_ob;
   const int ob = item % n_ob;
-  // every wave of the workgroup reaches the barriers below, valid or not
-  const bool valid = j < meta[kMetaActive];
-  const int e = valid ? active[j] : 0;
-  const int off = valid ? offsets[e] : 0, cnt = valid ? counts[e] : 0;
-  const int kw = I / kDnSplit;
-  const int kofs = part * kw + 8 * (lane / 16);
-  const uint16_t* w0 = w_d + (static_cast<int64_t>(e) * H + ob * kDnRows + lane % 16) * I + kofs;
+  if (j >= meta[kMetaActive]) return;
+  const int e = active[j];
+  const int off = offsets[e], cnt = counts[e];
+  const int lane = threadIdx.x % kWave;
+  const int kofs = 8 * (lane / 16);
+  const uint16_t* w0 = w_d + (static_cast<int64_t>(e) * H + ob * 16 + lane % 16) * I + kofs;
 
-  // all items of a workgroup loop the same number of 16-token chunks
-  __shared__ int chunk_cnt[kDnItems];
-  if (lane == 0 && part == 0) chunk_cnt[wave / kDnSplit] = cnt;
-  __syncthreads();
-  int loops = 0;
-#pragma unroll
-  for (int o = 0; o < kDnItems; ++o) loops = max(loops, chunk_cnt[o]);
-
-  for (int c0 = 0; c0 < loops; c0 += 16) {
-    const int ntok = max(0, min(16, cnt - c0));
+  for (int c0 = 0; c0 < cnt; c0 += 16) {
+    const int ntok = min(16, cnt - c0);
     const bool has_tok = (lane % 16) < ntok;
     const uint16_t* hr = h + static_cast<int64_t>(off + c0 + (has_tok ? lane % 16 : 0)) * I + kofs;
-    f32x4 a[kDnTiles];
+    f32x4 a0 = {}, a1 = {};
+    for (int k = 0; k < I; k += 32 * kDnUnroll) {
+      u32x4 wv[kDnUnroll], hb[kDnUnroll];
 #pragma unroll
-    for (int t = 0; t < kDnTiles; ++t) a[t] = f32x4{};
-    if (ntok > 0) {
-      for (int k = 0; k < kw; k += 32 * kDnUnroll) {
-        u32x4 wv[kDnTiles][kDnUnroll], hb[kDnUnroll];
+      for (int u = 0; u < kDnUnroll; ++u) {
+        const bool in = k + 32 * u < I;
+        wv[u] = in ? ld16(w0 + k + 32 * u) : u32x4{0, 0, 0, 0};
+        hb[u] = (in && has_tok) ? ld16(hr + k + 32 * u) : u32x4{0, 0, 0, 0};
+      }
 #pragma unroll
-        for (int u = 0; u < kDnUnroll; ++u) {
-          const bool in = k + 32 * u < kw;
-#pragma unroll
-          for (int t = 0; t < kDnTiles; ++t)
-            wv[t][u] = in ? ld16(w0 + static_cast<int64_t>(16 * t) * I + k + 32 * u) : u32x4{0, 0, 0, 0};
-          hb[u] = (in && has_tok) ? ld16(hr + k + 32 * u) : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int u = 0; u < kDnUnroll; ++u)
-#pragma unroll
-          for (int t = 0; t < kDnTiles; ++t)
-            a[t] = mfma16x16x32(as_bf16x8(wv[t][u]), as_bf16x8(hb[u]), a[t]);
+      for (int u = 0; u < kDnUnroll; ++u) {
+        if (u % 2 == 0) a0 = mfma16x16x32(as_bf16x8(wv[u]), as_bf16x8(hb[u]), a0);
+        else            a1 = mfma16x16x32(as_bf16x8(wv[u]), as_bf16x8(hb[u]), a1);
       }
     }
+    const f32x4 r = a0 + a1;
+    if (has_tok) {
+      // element q: row ob*16 + 4*(lane/16) + q of W_d, token lane%16
+      float* yr = y + static_cast<int64_t>(off + c0 + lane % 16) * H + ob * 16 + 4 * (lane / 16);
 #pragma unroll
-    for (int t = 0; t < kDnTiles; ++t) red[wave][t][lane] = a[t];
-    __syncthreads();
-    if (part == 0 && has_tok) {
-      float* yr = y + static_cast<int64_t>(off + c0 + lane % 16) * H + ob * kDnRows + 4 * (lane / 16);
-#pragma unroll
-      for (int t = 0; t < kDnTiles; ++t) {
-        f32x4 r = red[wave][t][lane];
-#pragma unroll
-        for (int w = 1; w < kDnSplit; ++w) r += red[wave + w][t][lane];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) yr[16 * t + q] = r[q];
-      }
+      for (int q = 0; q < 4; ++q) yr[q] = r[q];
     }
-    __syncthreads();
   }
 }
 
@@ -191,7 +155,7 @@ hipError_t launch_stream_bf16(const Plan& p, const void* x,
                      static_cast<const uint16_t*>(w_gate_up), h, slot_token,
                      counts, offsets, active, meta, p.H, p.I);
   BEAM_LAUNCH(tm, "stream_down_bf16", stream_down,
-              dim3(static_cast<unsigned>(ceil_div(max_active * (p.H / kDnRows), kDnItems))),
+              dim3(static_cast<unsigned>(ceil_div(max_active * (p.H / 16), kWaves))),
                      dim3(kThreads), 0, s, h, static_cast<const uint16_t*>(w_down),
                      y, counts, offsets, active, meta, p.H, p.I);
   return hipGetLastError();

@@ -18,12 +18,7 @@
 // bank-conflict free; operand fragments are double buffered in registers.
 // 8 waves (2 per SIMD) each compute 128x64 with 32x32x16 bf16 MFMA.
 //
-// XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, each with
-// its own L2.  Workgroup b takes logical tile (b % 8) * ceil(n/8) + b / 8, so
-// every XCD walks a contiguous stretch of the logical order: expert, then
-// groups of 4 M tiles, then N tile, then M tile inside the group.  The ~32
-// workgroups an XCD runs at once then cover about 4 M tiles x 8 N tiles of
-// one expert and share both operands' current k-slices in its L2.
+// Tile layout, DMA pattern and the XCD-aware tile order: grouped_tile.h.
 //
 // Router logits for many tokens use the same tile loop as a dense product:
 // the fp32 router matrix is split exactly into three bf16 matrices, laid side
@@ -31,41 +26,15 @@
 // (its column index wraps modulo H), so every product is exact and the sums
 // are fp32.  The reduction is split into ks slices; the router's selection
 // kernel adds the ks partial logits in a fixed order.
-#include "common.h"
-#include "internal.h"
+#include "grouped_tile.h"
 
 namespace beam {
 namespace {
 
-constexpr int BM = kGemmBM;  // 256 rows
-constexpr int BN = 256;
-constexpr int BK = 64;
-constexpr int kThreads = 512;
-constexpr int kRowBytes = BK * 2;           // 128 bytes per tile row in LDS
-constexpr int kTileBytes = BM * kRowBytes;  // 32 KiB per operand tile
-constexpr int kXcds = 8;
-constexpr int kGroupM = 4;                  // M tiles per rasterisation group
-constexpr int kLoads = (BM * BK * 2) / (16 * kThreads);  // DMA regions per wave per operand
+using namespace tile;
+constexpr int BK = 64;  // bf16 values per tile row per k-step
 
 enum Mode { kGateUp = 0, kDown = 1 };
-
-typedef unsigned char TileLds[2][2 * kTileBytes];
-
-__device__ __forceinline__ int swz(int row, int chunk) {
-  // the 8 chunks of any 8 consecutive rows land on distinct bank groups,
-  // and so do the even (and the odd) rows of any 16 consecutive rows
-  return row * kRowBytes + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
-}
-
-// Tile row and logical 16-byte chunk that lane `lane` of wave `wave` loads in
-// DMA region i: one region = 1 KiB = 8 tile rows, lane l writing physical
-// chunk l % 8 of row l / 8; wave w fills regions w + 8i.
-__device__ __forceinline__ int dma_row(int wave, int lane, int i) {
-  return 8 * (wave + 8 * i) + lane / 8;
-}
-__device__ __forceinline__ int dma_chunk(int row, int lane) {
-  return (lane % 8) ^ ((row ^ (row >> 3)) & 7);
-}
 
 // acc[i][n] += A[arow_i] . B[brow_n] over columns [k0, k0 + nk*BK) of B,
 // for the first NF of the wave's four 32-row A fragments (the others hold
@@ -154,22 +123,6 @@ __device__ __forceinline__ void tile_mainloop_rows(
   }
 }
 
-// Number of the wave's 32-row A fragments (rows wm*128 + 32 i ...) that hold
-// at least one of the tile's m_valid rows.
-__device__ __forceinline__ int wave_frags(int m_valid, int wm) {
-  return min(4, max(0, (m_valid - wm * 128 + 31) / 32));
-}
-
-// Largest e with tile_off[e] * n_nt <= L (tile_off is non-decreasing).
-__device__ __forceinline__ int find_expert(const int32_t* tile_off, int E, int n_nt, int L) {
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tile_off[mid] * n_nt <= L) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(
     const uint16_t* __restrict__ a_src,   // gate/up: x [T,H]; down: h [S,I]
@@ -180,23 +133,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(
     const int32_t* __restrict__ meta, int E, int H, int I, int n_nt) {
   __shared__ __attribute__((aligned(16))) TileLds lds;
 
-  // ---- logical tile of this workgroup -------------------------------------
-  const int n_log = meta[kMetaTiles] * n_nt;
-  const int per_xcd = (n_log + kXcds - 1) / kXcds;
-  const int local = blockIdx.x / kXcds;
-  const int L = (blockIdx.x % kXcds) * per_xcd + local;
-  if (local >= per_xcd || L >= n_log) return;
-  const int e = find_expert(tile_off, E, n_nt, L);
-  const int t0 = tile_off[e], nt_e = tile_off[e + 1] - t0;
-  // Within an expert, groups of kGroupM M tiles walk the N tiles together,
-  // so the workgroups resident on one XCD share A and B k-slices in its L2.
-  const int j = L - t0 * n_nt;
-  const int g = j / (kGroupM * n_nt);
-  const int gm = min(kGroupM, nt_e - g * kGroupM);
-  const int jj = j - g * kGroupM * n_nt;
-  const int nt = jj / gm;
-  const int row0 = offsets[e] + (g * kGroupM + jj % gm) * BM;
-  const int row_end = offsets[e] + counts[e];  // first slot past this expert
+  Coords tc;
+  if (!tile_coords(counts, offsets, tile_off, meta, E, n_nt, tc)) return;
+  const int e = tc.e, nt = tc.nt, row0 = tc.row0, row_end = tc.row_end;
   const int K = (MODE == kGateUp) ? H : I;
 
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
@@ -223,7 +162,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(
       b_off[i] = static_cast<uint32_t>(wrow) * H + c * 8;
     } else {
       a_off[i] = static_cast<uint32_t>(slot) * I + c * 8;
-      b_off[i] = static_cast<uint32_t>(nt * BN + r) * I + c * 8;
+      // the last N tile may run past H (H is a multiple of 128 only)
+      b_off[i] = static_cast<uint32_t>(min(nt * BN + r, H - 1)) * I + c * 8;
     }
   }
   // A rows of this wave: wm*128 + mi*32 + lane%32.
@@ -260,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
           const int col = nt * BN + wn * 64 + n * 32 + lane % 32;
-          out[static_cast<int64_t>(row) * H + col] = f32_to_bf16_bits(acc[i][n][r]);
+          if (col < H) out[static_cast<int64_t>(row) * H + col] = f32_to_bf16_bits(acc[i][n][r]);
         }
       }
     }
@@ -346,17 +286,12 @@ hipError_t launch_grouped_bf16(const Plan& p, const void* x,
   uint16_t* h = ws_at<uint16_t>(ws, p.off_h);
   uint16_t* y = ws_at<uint16_t>(ws, p.off_y);
   const int nt_gu = p.I / 128;
-  const int nt_dn = p.H / BN;
-  // grid: an upper bound on the logical tiles, rounded to whole XCD rounds
-  auto grid_for = [&](int n_nt) {
-    const int64_t per = ceil_div(p.max_tiles * n_nt, kXcds);
-    return dim3(static_cast<unsigned>(per * kXcds));
-  };
-  BEAM_LAUNCH(tm, "grouped_gate_up_bf16", grouped_gemm_bf16<kGateUp>, grid_for(nt_gu),
+  const int nt_dn = static_cast<int>(ceil_div(p.H, BN));
+  BEAM_LAUNCH(tm, "grouped_gate_up_bf16", grouped_gemm_bf16<kGateUp>, grid_for(p, nt_gu),
               dim3(kThreads), 0, s, static_cast<const uint16_t*>(x),
               static_cast<const uint16_t*>(w_gate_up), h, slot_token, counts,
               offsets, toff, meta, p.E, p.H, p.I, nt_gu);
-  BEAM_LAUNCH(tm, "grouped_down_bf16", grouped_gemm_bf16<kDown>, grid_for(nt_dn),
+  BEAM_LAUNCH(tm, "grouped_down_bf16", grouped_gemm_bf16<kDown>, grid_for(p, nt_dn),
               dim3(kThreads), 0, s, h, static_cast<const uint16_t*>(w_down), y,
               slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_dn);
   return hipGetLastError();

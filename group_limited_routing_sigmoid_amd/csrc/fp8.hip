@@ -4,8 +4,7 @@
 // library reads it as e4m3fn weights with one fp32 scale per 128x128 block,
 // activations quantised per token per 128 channels with scale = amax/448,
 // and fp32 accumulation with the scales applied per 128-deep slice.
-#include "common.h"
-#include "internal.h"
+#include "grouped_tile.h"
 
 namespace beam {
 namespace {
@@ -82,44 +81,153 @@ bool fp8_experts_built() { return true; }
 
 namespace {
 
-constexpr int BM = kGemmBM;  // 256 slots
-constexpr int BN = 128;
-constexpr int BK = 128;      // one scale block per k step
-constexpr int kThreads = 512;
-constexpr int kRowBytes = BK;                // 128 e4m3 codes per tile row
-constexpr int kATile = BM * kRowBytes;       // 32 KiB
-constexpr int kBTile = BN * kRowBytes;       // 16 KiB
-constexpr int kXcds = 8;
-constexpr int kALoads = kATile / (16 * kThreads);  // 4
-constexpr int kBLoads = kBTile / (16 * kThreads);  // 2
+using namespace tile;
 
 enum Mode { kGateUp = 0, kDown = 1 };
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-  // the 8 chunks of any 8 consecutive rows land on distinct bank groups,
-  // and so do the even (and the odd) rows of any 16 consecutive rows
-  return row * kRowBytes + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
-}
-
-__device__ __forceinline__ int find_expert(const int32_t* tile_off, int E, int n_nt, int L) {
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tile_off[mid] * n_nt <= L) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 // D = A(32x64) * B(64x32) + C on e4m3 codes (format 0, unit E8M0 scales).
+// Lane l supplies row (l % 32) of A and column (l % 32) of B, codes
+// 32*(l/32) .. +32 of the 64-deep slice; C as for the bf16 32x32 MFMA.
 __device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// Grouped e4m3 GEMM with per-128 block scales: for every 128-deep slice kb,
-// P = sum_k qa*qw on the matrix cores (exact products, fp32 sums), then
-// acc += P * (s_a[row, kb] * s_w[nblock, kb]) in fp32.  Same work list, XCD
-// order and SwiGLU epilogue as the bf16 grouped GEMM; 256x128 tiles (a
-// gate/up tile = 64 gate + 64 up rows), 8 waves of 64x64, LDS double buffer.
+// LDS addresses of the lane's MFMA fragments.  A fragment row is
+// base + 32 f (f = fragment index), and with the tile swizzle the physical
+// chunk of logical chunk c = 4 hlf + 2 (lane/32) + j of that row is
+// ((2 (lane/32) + j) ^ key) ^ 4 ((hlf + f) & 1), key = (l ^ (l >> 3)) & 7 for
+// l = lane % 32 (base is a multiple of 64).  So every fragment address is a
+// per-lane row offset, one of four per-lane chunk offsets and a constant.
+struct FragAddr {
+  uint32_t a_row, b_row;  // byte offsets of the lane's A row (f = 0) and B row (n = 0)
+  uint32_t p[2][2];       // p[j][flip]: chunk byte offset
+  uint32_t r_row;         // byte offset of the lane's first ratio (per-row factor)
+};
+
+__device__ __forceinline__ FragAddr frag_addr(int wm, int wn, int lane) {
+  FragAddr fa;
+  const int l = lane % 32;
+  const int key = (l ^ (l >> 3)) & 7;
+  fa.a_row = static_cast<uint32_t>(wm * 128 + l) * kRowBytes;
+  fa.b_row = static_cast<uint32_t>(wn * 64 + l) * kRowBytes;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+      fa.p[j][f] = static_cast<uint32_t>((((2 * (lane / 32) + j) ^ key) ^ (4 * f)) << 4);
+  fa.r_row = static_cast<uint32_t>(wm * 128 + 4 * (lane / 32)) * 4;
+  return fa;
+}
+
+// The lane's 32 codes of 64-deep half hlf of fragment f (32 rows apart).
+__device__ __forceinline__ i32x8 frag8(const unsigned char* t, uint32_t row, const FragAddr& fa,
+                                       int f, int hlf) {
+  const int flip = (hlf + f) & 1;
+  const unsigned char* r = t + row + f * 32 * kRowBytes;
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(r + fa.p[0][flip]);
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(r + fa.p[1][flip]);
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+// acc[i][n] *= v[row of element] for the 16 rows fragment i holds in this
+// lane (v: the 256 per-row factors of the wave's weight block, in LDS).
+__device__ __forceinline__ void scale_rows(f32x16 (&acc)[4][2], int i, const float* v,
+                                           const FragAddr& fa) {
+  const unsigned char* base = reinterpret_cast<const unsigned char*>(v) + fa.r_row;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(base + (i * 32 + 8 * q) * 4);
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][n][4 * q + j] *= t[j];
+  }
+}
+
+// One 128-deep stage for the wave's first NF fragments: rescale the
+// accumulators to this stage's scale and add the stage's exact products, one
+// 64-deep half at a time (B fragments of the half held, A fragments read one
+// ahead).  Fragment i is rescaled just before its first product of the
+// stage, so the multiplies overlap the matrix-core work of fragment i-1.
+template <int NF>
+__device__ __forceinline__ void fp8_stage(const unsigned char* at, const unsigned char* bt,
+                                          const float* ratio, f32x16 (&acc)[4][2],
+                                          const FragAddr& fa) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const i32x8 b0 = frag8(bt, fa.b_row, fa, 0, h);
+    const i32x8 b1 = frag8(bt, fa.b_row, fa, 1, h);
+    i32x8 a = frag8(at, fa.a_row, fa, 0, h);
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      i32x8 an = a;
+      if (i + 1 < NF) an = frag8(at, fa.a_row, fa, i + 1, h);
+      if (h == 0) scale_rows(acc, i, ratio, fa);
+      acc[i][0] = mfma_fp8_32x32x64(a, b0, acc[i][0]);
+      acc[i][1] = mfma_fp8_32x32x64(a, b1, acc[i][1]);
+      a = an;
+    }
+  }
+}
+
+// Main loop over the K/128 stages.  Block scales: the exact product of a
+// 128-deep stage kb is P_kb (unit scales); the result is sum_kb s_kb * P_kb
+// with s_kb = s_a[row, kb] * s_w[block, kb].  The accumulator is kept in units
+// of the current stage's s: before adding P_kb it is multiplied by
+// s_{kb-1} / s_kb, and the epilogue multiplies by the last s.  Thread
+// (blk, srow) = (tid / 256, tid % 256) computes the factor of tile row srow
+// for weight block blk one stage ahead into rsc.  Returns that thread's last s.
+template <int NF>
+__device__ __forceinline__ float fp8_mainloop(
+    const uint8_t* __restrict__ a_src, const uint32_t* a_off, const bool* a_ok,
+    const uint8_t* __restrict__ wb, const uint32_t* b_off, const float* sa_src,
+    const float* sw_src, int nkb, TileLds& lds, float (&rsc)[2][2][BM], int blk, int srow,
+    f32x16 (&acc)[4][2], const FragAddr& fa, int wn) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  auto dma = [&](int buf, int kb) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int region = wave + 8 * i;
+      if (a_ok[i]) dma16(a_src + (a_off[i] + kb * 128), &lds[buf][region * 1024]);
+      dma16(wb + (b_off[i] + kb * 128), &lds[buf][kTileBytes + region * 1024]);
+    }
+  };
+  dma(0, 0);
+  float s_prev = sa_src[0] * sw_src[0];
+  // factors of stage 1, loaded a stage ahead of their use
+  float sa_n = sa_src[min(1, nkb - 1)], sw_n = sw_src[min(1, nkb - 1)];
+  rsc[0][blk][srow] = 1.0f;
+  __syncthreads();
+  for (int kt = 0; kt < nkb; ++kt) {
+    const int buf = kt & 1;
+    // buffer buf^1 and rsc[buf^1] were last read before the barrier that
+    // ended step kt-1
+    if (kt + 1 < nkb) dma(buf ^ 1, kt + 1);
+    // scale factors of stage kt+2 (consumed after the next barrier)
+    const int k2 = min(kt + 2, nkb - 1);
+    const float sa2 = sa_src[k2], sw2 = sw_src[k2];
+    // no branch from here to the barrier, so the compiler keeps the
+    // stage's reads next to the products that use them
+    if (NF > 0)
+      fp8_stage<NF>(&lds[buf][0], &lds[buf][kTileBytes], &rsc[buf][wn / 2][0], acc, fa);
+    // factor of stage kt+1 (after the last stage it lands in an unused buffer)
+    const float s = sa_n * sw_n;
+    rsc[buf ^ 1][blk][srow] = s_prev / s;
+    s_prev = (kt + 1 < nkb) ? s : s_prev;
+    sa_n = sa2;
+    sw_n = sw2;
+    __syncthreads();  // waits for this wave's loads, then for every wave
+  }
+  return s_prev;
+}
+
+// Grouped e4m3 GEMM with per-128 block scales.  Same work list, tile
+// layout, DMA pattern and XCD order as the bf16 grouped GEMM: 256x256 tiles,
+// 128 codes deep per stage, 8 waves of 128x64.  Each wave's 64 columns lie in
+// one 128-row block of weight scales: waves 0-1 hold gate channels and 2-3
+// the matching up channels of a gate/up tile (128 channels), whose up values
+// reach the gate waves through LDS for silu(g)*u.
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
     const uint8_t* __restrict__ a_src,   // gate/up: xq [T,H]; down: hq [S,I]
@@ -130,172 +238,121 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
     const int32_t* __restrict__ slot_token, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off,
     const int32_t* __restrict__ meta, int E, int H, int I, int n_nt) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2][kATile + kBTile];
-  __shared__ __attribute__((aligned(16))) float sa[2][BM];
+  __shared__ __attribute__((aligned(16))) TileLds lds;
+  __shared__ __attribute__((aligned(16))) float rsc[2][2][BM];
 
-  const int n_log = meta[kMetaTiles] * n_nt;
-  const int per_xcd = (n_log + kXcds - 1) / kXcds;
-  const int local = blockIdx.x / kXcds;
-  const int L = (blockIdx.x % kXcds) * per_xcd + local;
-  if (local >= per_xcd || L >= n_log) return;
-  const int e = find_expert(tile_off, E, n_nt, L);
-  const int t0 = tile_off[e], nt_e = tile_off[e + 1] - t0;
-  const int j = L - t0 * n_nt;
-  const int nt = j / nt_e;
-  const int row0 = offsets[e] + (j % nt_e) * BM;
-  const int row_end = offsets[e] + counts[e];
+  Coords tc;
+  if (!tile_coords(counts, offsets, tile_off, meta, E, n_nt, tc)) return;
+  const int e = tc.e, nt = tc.nt, row0 = tc.row0, row_end = tc.row_end;
   const int K = (MODE == kGateUp) ? H : I;
   const int nkb = K / 128;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int wm = wave / 4, wn = wave % 4;
+  const int m_valid = min(BM, row_end - row0);
 
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave, wave = tid / kWave;
-  const int wm = wave / 2, wn = wave % 2;
+  const uint8_t* wb = w + static_cast<int64_t>(e) * ((MODE == kGateUp) ? 2 * I : H) * K;
+  uint32_t a_off[kLoads], b_off[kLoads];
+  bool a_ok[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int r = dma_row(wave, lane, i);
+    const int c = dma_chunk(r, lane);
+    a_ok[i] = r < m_valid;
+    const int slot = min(row0 + r, row_end - 1);  // padded rows: any valid row
+    a_off[i] = ((MODE == kGateUp) ? static_cast<uint32_t>(slot_token[slot]) * H
+                                  : static_cast<uint32_t>(slot) * I) + c * 16;
+    // gate/up: rows 0..127 gate channels nt*128 + r, rows 128..255 the up
+    // channels; down: weight row nt*256 + r (the last tile may pass H)
+    const int wrow = (MODE == kGateUp) ? ((r < 128) ? nt * 128 + r : I + nt * 128 + (r - 128))
+                                       : min(nt * BN + r, H - 1);
+    b_off[i] = static_cast<uint32_t>(wrow) * K + c * 16;
+  }
+  // scale thread: tile row srow, weight block blk of the tile
+  const int blk = tid / BM, srow = tid % BM;
+  const int sslot = min(row0 + srow, row_end - 1);
+  const float* sa_src = a_scale + static_cast<int64_t>(
+      (MODE == kGateUp) ? slot_token[sslot] : sslot) * nkb;
+  const int nrb = (MODE == kGateUp) ? 2 * I / 128 : H / 128;
+  const int wblock = (MODE == kGateUp) ? (blk == 0 ? nt : I / 128 + nt)
+                                       : min(2 * nt + blk, nrb - 1);
+  const float* sw_src = w_scale + (static_cast<int64_t>(e) * nrb + wblock) * nkb;
 
-  const int chunk = tid % 8;
-  const uint8_t* wbase = (MODE == kGateUp) ? w + static_cast<int64_t>(e) * 2 * I * H
-                                           : w + static_cast<int64_t>(e) * H * I;
-  uint32_t a_off[kALoads], b_off[kBLoads];
-  int la_off[kALoads], lb_off[kBLoads];
-#pragma unroll
-  for (int i = 0; i < kALoads; ++i) {
-    const int r = tid / 8 + (kThreads / 8) * i;
-    int slot = row0 + r;
-    if (slot > row_end - 1) slot = row_end - 1;
-    a_off[i] = (MODE == kGateUp) ? static_cast<uint32_t>(slot_token[slot]) * H + chunk * 16
-                                 : static_cast<uint32_t>(slot) * I + chunk * 16;
-    la_off[i] = swz(r, chunk);
-  }
-#pragma unroll
-  for (int i = 0; i < kBLoads; ++i) {
-    const int r = tid / 8 + (kThreads / 8) * i;
-    if (MODE == kGateUp) {
-      // rows 0..63: gate channels nt*64 + r; rows 64..127: up channels
-      const int wrow = (r < 64) ? (nt * 64 + r) : (I + nt * 64 + (r - 64));
-      b_off[i] = static_cast<uint32_t>(wrow) * H + chunk * 16;
-    } else {
-      b_off[i] = static_cast<uint32_t>(nt * BN + r) * I + chunk * 16;
-    }
-    lb_off[i] = kATile + swz(r, chunk);
-  }
-  // row scale source for threads 0..255 (one A row each)
-  uint32_t sa_off = 0;
-  if (tid < BM) {
-    int slot = row0 + tid;
-    if (slot > row_end - 1) slot = row_end - 1;
-    sa_off = (MODE == kGateUp) ? static_cast<uint32_t>(slot_token[slot]) * nkb
-                               : static_cast<uint32_t>(slot) * nkb;
-  }
-  // weight-scale rows of this wave's two 32-column blocks
-  const float* sw0;
-  const float* sw1;
-  if (MODE == kGateUp) {
-    const int cb = (nt * 64) / 128;  // 128-channel block of this tile's channels
-    sw0 = w_scale + (static_cast<int64_t>(e) * (2 * I / 128) + cb) * nkb;
-    sw1 = w_scale + (static_cast<int64_t>(e) * (2 * I / 128) + I / 128 + cb) * nkb;
-  } else {
-    sw0 = w_scale + (static_cast<int64_t>(e) * (H / 128) + nt) * nkb;
-    sw1 = sw0;
-  }
+  // A rows of this wave: wm*128 + 32 i + lane%32; B rows: wn*64 + 32 n + lane%32
+  const FragAddr fa = frag_addr(wm, wn, lane);
 
-  u32x4 ra[kALoads], rb[kBLoads];
-  float rs = 0.0f;
-  auto gload = [&](int kb) {
+  f32x16 acc[4][2];
 #pragma unroll
-    for (int i = 0; i < kALoads; ++i) ra[i] = ld16(a_src + (a_off[i] + kb * 128));
-#pragma unroll
-    for (int i = 0; i < kBLoads; ++i) rb[i] = ld16(wbase + (b_off[i] + kb * 128));
-    if (tid < BM) rs = a_scale[sa_off + kb];
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kALoads; ++i) *reinterpret_cast<u32x4*>(&lds[buf][la_off[i]]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < kBLoads; ++i) *reinterpret_cast<u32x4*>(&lds[buf][lb_off[i]]) = rb[i];
-    if (tid < BM) sa[buf][tid] = rs;
-  };
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int n = 0; n < 2; ++n) acc[i][n] = f32x16{};
 
-  // A rows of this wave: wm*64 + i*32 + lane%32.  B rows: gate/up -> gate
-  // wn*32 + lane%32, up 64 + wn*32 + lane%32; down -> wn*64 + n*32 + lane%32.
-  int arow[2], brow[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) arow[i] = wm * 64 + i * 32 + lane % 32;
-#pragma unroll
-  for (int n = 0; n < 2; ++n)
-    brow[n] = (MODE == kGateUp) ? (n * 64 + wn * 32 + lane % 32)
-                                : (wn * 64 + n * 32 + lane % 32);
+  const int nf = wave_frags(m_valid, wm);
+  float s_last;
+#define BEAM_FP8_LOOP(NF)                                                                   \
+  s_last = fp8_mainloop<NF>(a_src, a_off, a_ok, wb, b_off, sa_src, sw_src, nkb, lds, rsc, \
+                            blk, srow, acc, fa, wn)
+  switch (nf) {
+    case 4: BEAM_FP8_LOOP(4); break;
+    case 3: BEAM_FP8_LOOP(3); break;
+    case 2: BEAM_FP8_LOOP(2); break;
+    case 1: BEAM_FP8_LOOP(1); break;
+    default: BEAM_FP8_LOOP(0); break;
+  }
+#undef BEAM_FP8_LOOP
 
-  // lane's 32 codes of a 64-deep half: chunks hlf*4 + 2*(lane/32) and +1
-  auto frag = [&](int buf, int base, int row, int hlf) {
-    const int c = hlf * 4 + 2 * (lane / 32);
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(&lds[buf][base + swz(row, c)]);
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(&lds[buf][base + swz(row, c + 1)]);
-    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-  };
+  // ---- epilogue: last stage's scale, then store ---------------------------
+  rsc[0][blk][srow] = s_last;  // rsc is no longer read by the main loop
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i < nf) scale_rows(acc, i, &rsc[0][wn / 2][0], fa);
 
-  auto compute = [&](int buf, int kb) {
-    const float w0 = sw0[kb], w1 = sw1[kb];
-    i32x8 a[2][2], b[2][2];
+  if (MODE == kGateUp) {
+    // up values, fp32, [256 rows][128 channels] over the two tile buffers
+    float* ex = reinterpret_cast<float*>(&lds[0][0]);
+    if (wn >= 2) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      a[i][0] = frag(buf, 0, arow[i], 0);
-      a[i][1] = frag(buf, 0, arow[i], 1);
-      b[i][0] = frag(buf, kATile, brow[i], 0);
-      b[i][1] = frag(buf, kATile, brow[i], 1);
-    }
+      for (int i = 0; i < 4; ++i) {
+        if (i >= nf) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+        for (int r = 0; r < 16; ++r) {
+          const int rl = wm * 128 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        f32x16 p = {};
-        p = mfma_fp8_32x32x64(a[i][0], b[n][0], p);
-        p = mfma_fp8_32x32x64(a[i][1], b[n][1], p);
-        const float wsc = n == 0 ? w0 : w1;
-        // element r of p is row wm*64 + i*32 + 8*(r/4) + 4*(lane/32) + r%4
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(
-              &sa[buf][wm * 64 + i * 32 + 8 * q + 4 * (lane / 32)]);
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            acc[i][n][4 * q + t] = __builtin_fmaf(p[4 * q + t], v[t] * wsc, acc[i][n][4 * q + t]);
+          for (int n = 0; n < 2; ++n)
+            ex[rl * 128 + (wn - 2) * 64 + n * 32 + lane % 32] = acc[i][n][r];
         }
       }
     }
-  };
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nkb) gload(kb + 1);
-    compute(buf, kb);
-    if (kb + 1 < nkb) sstore(buf ^ 1);
     __syncthreads();
-  }
-
+    if (wn < 2) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < 4; ++i) {
+        if (i >= nf) continue;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = row0 + wm * 64 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
-      if (row >= row_end) continue;
-      if (MODE == kGateUp) {
-        const int ch = nt * 64 + wn * 32 + lane % 32;
-        const float h = silu(acc[i][0][r]) * acc[i][1][r];
-        out[static_cast<int64_t>(row) * I + ch] = f32_to_bf16_bits(h);
-      } else {
+        for (int r = 0; r < 16; ++r) {
+          const int rl = wm * 128 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+          if (row0 + rl >= row_end) continue;
+#pragma unroll
+          for (int n = 0; n < 2; ++n) {
+            const int ch = wn * 64 + n * 32 + lane % 32;
+            const float h = silu(acc[i][n][r]) * ex[rl * 128 + ch];
+            out[static_cast<int64_t>(row0 + rl) * I + nt * 128 + ch] = f32_to_bf16_bits(h);
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i >= nf) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + wm * 128 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+        if (row >= row_end) continue;
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
           const int col = nt * BN + wn * 64 + n * 32 + lane % 32;
-          out[static_cast<int64_t>(row) * H + col] = f32_to_bf16_bits(acc[i][n][r]);
+          if (col < H) out[static_cast<int64_t>(row) * H + col] = f32_to_bf16_bits(acc[i][n][r]);
         }
       }
     }
@@ -323,17 +380,14 @@ hipError_t launch_experts_fp8(const Plan& p, const void* x,
   const int32_t* meta = ws_at<int32_t>(ws, p.off_meta);
   hipError_t e = launch_quant_e4m3(p.T, p.H, BEAM_BF16, x, xq, xs, s, tm);
   if (e != hipSuccess) return e;
-  const int nt_gu = p.I / 64, nt_dn = p.H / BN;
-  auto grid_for = [&](int n_nt) {
-    const int64_t per = ceil_div(p.max_tiles * n_nt, kXcds);
-    return dim3(static_cast<unsigned>(per * kXcds));
-  };
-  BEAM_LAUNCH(tm, "gate_up_fp8", grouped_gemm_fp8<kGateUp>, grid_for(nt_gu),
+  const int nt_gu = p.I / 128;
+  const int nt_dn = static_cast<int>(ceil_div(p.H, BN));
+  BEAM_LAUNCH(tm, "gate_up_fp8", grouped_gemm_fp8<kGateUp>, grid_for(p, nt_gu),
               dim3(kThreads), 0, s, xq, xs, w_gate_up, s_gate_up, h, slot_token,
               counts, offsets, toff, meta, p.E, p.H, p.I, nt_gu);
   e = launch_quant_e4m3(p.S, p.I, BEAM_BF16, h, hq, hs, s, tm);
   if (e != hipSuccess) return e;
-  BEAM_LAUNCH(tm, "down_fp8", grouped_gemm_fp8<kDown>, grid_for(nt_dn),
+  BEAM_LAUNCH(tm, "down_fp8", grouped_gemm_fp8<kDown>, grid_for(p, nt_dn),
               dim3(kThreads), 0, s, hq, hs, w_down, s_down, y, slot_token,
               counts, offsets, toff, meta, p.E, p.H, p.I, nt_dn);
   return hipGetLastError();

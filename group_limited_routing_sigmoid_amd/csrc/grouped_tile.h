@@ -1,0 +1,102 @@
+// Tile machinery shared by the grouped expert GEMMs (bf16 and e4m3): the
+// LDS tile layout, its global -> LDS copy pattern and the XCD-aware mapping
+// of workgroups to (expert, M tile, N tile).
+//
+// A tile is 256 rows of 128 bytes (64 bf16 or 128 e4m3 values along k), so
+// both GEMMs stage the same bytes per k-step and share every address below.
+#pragma once
+
+#include "common.h"
+#include "internal.h"
+
+namespace beam {
+namespace tile {
+
+constexpr int BM = kGemmBM;                 // 256 rows (slots) per M tile
+constexpr int BN = 256;                     // weight rows per N tile
+constexpr int kThreads = 512;               // 8 waves
+constexpr int kRowBytes = 128;              // bytes per tile row per k-step
+constexpr int kTileBytes = BM * kRowBytes;  // 32 KiB per operand tile
+constexpr int kXcds = 8;
+constexpr int kGroupM = 4;                  // M tiles per rasterisation group
+constexpr int kLoads = kTileBytes / (16 * kThreads);  // DMA regions per wave per operand
+
+// Two stages of (A tile, B tile).
+typedef unsigned char TileLds[2][2 * kTileBytes];
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+  // the 8 chunks of any 8 consecutive rows land on distinct bank groups,
+  // and so do the even (and the odd) rows of any 16 consecutive rows
+  return row * kRowBytes + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+}
+
+// Tile row and logical 16-byte chunk that lane `lane` of wave `wave` loads in
+// DMA region i: one region = 1 KiB = 8 tile rows, lane l writing physical
+// chunk l % 8 of row l / 8; wave w fills regions w + 8i.
+__device__ __forceinline__ int dma_row(int wave, int lane, int i) {
+  return 8 * (wave + 8 * i) + lane / 8;
+}
+__device__ __forceinline__ int dma_chunk(int row, int lane) {
+  return (lane % 8) ^ ((row ^ (row >> 3)) & 7);
+}
+
+// Largest e with tile_off[e] * n_nt <= L (tile_off is non-decreasing).
+__device__ __forceinline__ int find_expert(const int32_t* tile_off, int E, int n_nt, int L) {
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tile_off[mid] * n_nt <= L) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+struct Coords {
+  int e;        // expert
+  int nt;       // N tile
+  int row0;     // first slot of the M tile
+  int row_end;  // first slot past the expert's slots
+};
+
+// Workgroups are dealt round-robin to the 8 XCDs, each with its own L2.
+// Workgroup b takes logical tile (b % 8) * ceil(n/8) + b / 8, so every XCD
+// walks a contiguous stretch of the logical order: expert, then groups of
+// kGroupM M tiles, then N tile, then M tile inside the group.  The ~32
+// workgroups an XCD runs at once then cover about 4 M tiles x 8 N tiles of
+// one expert and share both operands' current k-slices in its L2.
+// Returns false for workgroups past the last logical tile.
+__device__ __forceinline__ bool tile_coords(const int32_t* counts, const int32_t* offsets,
+                                            const int32_t* tile_off, const int32_t* meta,
+                                            int E, int n_nt, Coords& c) {
+  const int n_log = meta[kMetaTiles] * n_nt;
+  const int per_xcd = (n_log + kXcds - 1) / kXcds;
+  const int local = blockIdx.x / kXcds;
+  const int L = (blockIdx.x % kXcds) * per_xcd + local;
+  if (local >= per_xcd || L >= n_log) return false;
+  const int e = find_expert(tile_off, E, n_nt, L);
+  const int t0 = tile_off[e], nt_e = tile_off[e + 1] - t0;
+  const int j = L - t0 * n_nt;
+  const int g = j / (kGroupM * n_nt);
+  const int gm = min(kGroupM, nt_e - g * kGroupM);
+  const int jj = j - g * kGroupM * n_nt;
+  c.e = e;
+  c.nt = jj / gm;
+  c.row0 = offsets[e] + (g * kGroupM + jj % gm) * BM;
+  c.row_end = offsets[e] + counts[e];
+  return true;
+}
+
+// Number of a wave's 32-row A fragments (rows wm*128 + 32 i ...) that hold
+// at least one of the tile's m_valid rows.
+__device__ __forceinline__ int wave_frags(int m_valid, int wm) {
+  return min(4, max(0, (m_valid - wm * 128 + 31) / 32));
+}
+
+// Grid of a grouped launch: an upper bound on the logical tiles, rounded to
+// whole XCD rounds.
+inline dim3 grid_for(const Plan& p, int n_nt) {
+  const int64_t per = ceil_div(p.max_tiles * n_nt, kXcds);
+  return dim3(static_cast<unsigned>(per * kXcds));
+}
+
+}  // namespace tile
+}  // namespace beam

@@ -69,6 +69,17 @@ def test_small_bf16_skewed_long_chunks():
                f"small skew path={path}")
 
 
+@pytest.mark.parametrize("path", [gl.PATH_STREAM, gl.PATH_GROUPED])
+def test_odd_widths_skewed(path):
+    # hidden and intermediate multiples of 128 but not of 256: the last
+    # 256-wide down tile of the grouped path is half outside H
+    sh = small_shape(hidden=384, intermediate=384)
+    w = WORKLOADS["prefill16k_skew"]
+    inp = make_inputs(w, device=device(), tokens=600, shape=sh, seed=91)
+    _check(inp, sh, desc_for(w, sh, path), np.arange(0, 600, 2), BF16_TOL,
+           f"H=I=384 skew path={path}")
+
+
 @pytest.mark.parametrize("path", [0, gl.PATH_GROUPED])
 def test_beam_decode64(path):
     w = WORKLOADS["decode64"]

@@ -68,3 +68,14 @@ def test_fp8_beam_sampled():
     rows = np.sort(np.random.default_rng(2).choice(T, 16, replace=False))
     rows[-1] = T - 1
     _check(inp, BEAM, rows, "fp8_8k sampled")
+
+
+@pytest.mark.parametrize("T", [300, 700])
+def test_fp8_odd_widths_skewed(T):
+    # hidden and intermediate multiples of 128 but not of 256 (the last
+    # 256-wide down tile is half outside H); hot experts with several
+    # 256-slot M tiles and a ragged last tile
+    sh = small_shape(hidden=384, intermediate=384)
+    inp = make_inputs(WORKLOADS["fp8_8k"], device=device(), tokens=T, shape=sh,
+                      seed=40 + T, bias="skew:0.5:0,1,2,3,32,33,34,35")
+    _check(inp, sh, np.arange(0, T, 2), f"fp8 H=I=384 skew T={T}")

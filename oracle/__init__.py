@@ -31,6 +31,15 @@ What each oracle function follows, and what pins it (tests/test_oracle_*.py):
                       DeepSeek-V3).  Pinned by a closed form on crafted loads
                       and by repeated route/update rounds driving the expert
                       load towards balance (a flipped sign diverges).
+  * residual_epilogue -- post-block RMSNorm (SandwichNorm's post-norm) and
+                      the depth-scaled FP32 residual stream ("Reflection Beam",
+                      section "Hybrid Attention and Unusual Residuals").
+                      Pinned by the telescoped stream (after steps 1..K every
+                      addend carries weight 1/sqrt(K)), the unit-scale
+                      property (the two weights' squares sum to one), the
+                      constant-row closed form of the norm and its scale
+                      invariance.  The norm's eps and weights are not on the
+                      pages: caller inputs.
   * e4m3 codec     -- pinned against torch.float8_e4m3fn on all 256 codes and
                       on random values.  The FP8 activation recipe (per-128
                       amax/448 scales) is a reading the pages do not fix:
@@ -92,6 +101,8 @@ def lib():
         L.bo_forward_tokens.restype = i32
         L.bo_bias_update.argtypes = [i32, i64, i32, vp, ctypes.c_float, vp]
         L.bo_bias_update.restype = None
+        L.bo_residual_epilogue.argtypes = [i64, i32, vp, vp, ctypes.c_double, i32, vp]
+        L.bo_residual_epilogue.restype = None
         L.bo_bias_gamma.argtypes = [i64, i64, ctypes.c_float, ctypes.c_float]
         L.bo_bias_gamma.restype = ctypes.c_float
         L.bo_max_threads.argtypes = []
@@ -241,3 +252,15 @@ def bias_update(n_experts, idx, gamma, bias):
 def bias_gamma(t, n, g0, g1):
     """Cosine-decayed update speed for step t of n."""
     return lib().bo_bias_gamma(t, n, g0, g1)
+
+
+def residual_epilogue(out, gamma, eps, k, residual):
+    """Post-block RMSNorm and depth-scaled residual update (binary64):
+    returns sqrt((k-1)/k) * residual + RMSNorm(out) * gamma / sqrt(k)."""
+    o = np.ascontiguousarray(_np(out), np.float64)
+    r = np.array(_np(residual), dtype=np.float64, copy=True)
+    g = np.ascontiguousarray(_np(gamma), np.float32)
+    T, H = o.shape
+    assert r.shape == (T, H) and g.shape == (H,) and k >= 1
+    lib().bo_residual_epilogue(T, H, _ptr(o), _ptr(g), float(eps), int(k), _ptr(r))
+    return r

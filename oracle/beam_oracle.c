@@ -400,6 +400,27 @@ float bo_bias_gamma(int64_t t, int64_t n, float g0, float g1) {
   return (float)((double)g1 + ((double)g0 - (double)g1) * c);
 }
 
+/* Post-block epilogue of the depth-scaled residual stream ("Reflection Beam",
+ * section "Hybrid Attention and Unusual Residuals"; SandwichNorm and FP32
+ * residual accumulation from the pretraining paragraph of "Reflection AI
+ * Introduces Beam ..."), in binary64 for each of the T rows:
+ *   n = o / sqrt(mean(o^2) + eps) * gamma      (post-sublayer RMSNorm)
+ *   r = sqrt((k - 1) / k) * r + n / sqrt(k)    (step k >= 1 of the stream)
+ * o [T, H] and r [T, H] binary64, gamma [H] binary32; r is updated in place. */
+void bo_residual_epilogue(int64_t T, int H, const double* o, const float* gamma,
+                          double eps, int k, double* r) {
+  const double a = sqrt((double)(k - 1) / (double)k);
+  const double b = 1.0 / sqrt((double)k);
+  for (int64_t t = 0; t < T; ++t) {
+    const double* ot = o + t * (int64_t)H;
+    double* rt = r + t * (int64_t)H;
+    double ss = 0.0;
+    for (int j = 0; j < H; ++j) ss += ot[j] * ot[j];
+    const double inv = 1.0 / sqrt(ss / (double)H + eps);
+    for (int j = 0; j < H; ++j) rt[j] = a * rt[j] + b * (ot[j] * inv * (double)gamma[j]);
+  }
+}
+
 int bo_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

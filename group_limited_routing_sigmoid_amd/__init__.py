@@ -26,7 +26,8 @@ SYMBOLS = ("beam_status_string", "beam_moe_validate", "beam_moe_workspace_bytes"
            "beam_moe_route", "beam_moe_permute", "beam_moe_quant_e4m3",
            "beam_moe_forward", "beam_moe_timer_create", "beam_moe_timer_destroy",
            "beam_moe_timer_reset", "beam_moe_timer_count", "beam_moe_timer_read",
-           "beam_moe_forward_timed", "beam_moe_bias_update", "beam_moe_bias_gamma")
+           "beam_moe_forward_timed", "beam_moe_bias_update", "beam_moe_bias_gamma",
+           "beam_moe_forward_residual")
 
 
 class Desc(ctypes.Structure):
@@ -68,6 +69,8 @@ def lib():
         L.beam_moe_forward.argtypes = [D, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                        vp, vp, vp, vp, sz, vp]
         L.beam_moe_forward_timed.argtypes = L.beam_moe_forward.argtypes + [vp]
+        L.beam_moe_forward_residual.argtypes = [D, i64, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                ctypes.c_float, i32, vp, vp, vp, sz, vp]
         L.beam_moe_timer_create.argtypes = [i32, ctypes.POINTER(vp)]
         L.beam_moe_timer_destroy.argtypes = [vp]
         L.beam_moe_timer_destroy.restype = None
@@ -205,6 +208,27 @@ def permute(desc: Desc, topk_idx: torch.Tensor,
     out["slot_token"] = out["slot_token"][:S]
     out["slot_of"] = out["slot_of"][:S].view(T, desc.top_k)
     return out
+
+
+def forward_residual(desc: Desc, x: torch.Tensor, w_router: Optional[torch.Tensor],
+                     bias: Optional[torch.Tensor], w_gate_up: torch.Tensor,
+                     w_down: torch.Tensor, norm_weight: torch.Tensor, eps: float,
+                     step: int, residual: torch.Tensor,
+                     s_gate_up: Optional[torch.Tensor] = None,
+                     s_down: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None,
+                     workspace: Optional[Workspace] = None, stream=None):
+    """beam_moe_forward_residual: the block, then residual (fp32 [T,H], in
+    place) = sqrt((k-1)/k) residual + RMSNorm(block output) * norm_weight /
+    sqrt(k).  Returns residual (and writes out when given)."""
+    T, dev = x.shape[0], x.device
+    buf, n = _ws(desc, T, workspace, dev)
+    _check(lib().beam_moe_forward_residual(
+        ctypes.byref(desc), T, _p(x), _p(w_router), _p(bias), _p(w_gate_up),
+        _p(s_gate_up), _p(w_down), _p(s_down), _p(norm_weight), float(eps),
+        int(step), _p(residual), _p(out), _p(buf), n, _stream(stream)),
+        "beam_moe_forward_residual")
+    return residual
 
 
 def bias_update(desc: Desc, topk_idx: torch.Tensor, gamma: float,

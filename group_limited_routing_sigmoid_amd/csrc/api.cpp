@@ -263,14 +263,14 @@ static int forward_impl(const beam_moe_desc* d, int64_t T, const void* x,
                         const void* w_down, const float* s_down, void* out,
                         int32_t* topk_idx, float* topk_w, float* logits,
                         void* workspace, size_t ws_bytes, void* stream,
-                        Timer* tm) {
+                        Timer* tm, const Epilogue* ep = nullptr) {
   Plan p;
   int st = make_plan(d, T, &p);
   if (st != BEAM_OK) return st;
   if (T == 0) return BEAM_OK;
   const bool lin = d->flags & BEAM_ROUTE_LOGITS_IN;
   const bool fp8 = d->weight_dtype == BEAM_FP8_E4M3;
-  if (!x || !w_gate_up || !w_down || !out) return BEAM_ERR_INVALID_ARG;
+  if (!x || !w_gate_up || !w_down || (!out && !ep)) return BEAM_ERR_INVALID_ARG;
   if (lin ? !logits : !w_router) return BEAM_ERR_INVALID_ARG;
   if (fp8 && (!s_gate_up || !s_down)) return BEAM_ERR_INVALID_ARG;
   if (fp8 && !fp8_experts_built()) return BEAM_ERR_UNSUPPORTED;
@@ -304,7 +304,7 @@ static int forward_impl(const beam_moe_desc* d, int64_t T, const void* x,
   else
     e = launch_grouped_bf16(p, x, w_gate_up, w_down, workspace, s, tm);
   if (e != hipSuccess) return BEAM_ERR_HIP;
-  return hip_status(launch_combine(p, slot_of, w, out, workspace, s, tm));
+  return hip_status(launch_combine(p, slot_of, w, out, workspace, s, tm, ep));
 }
 
 int beam_moe_forward(const beam_moe_desc* d, int64_t T, const void* x,
@@ -316,6 +316,32 @@ int beam_moe_forward(const beam_moe_desc* d, int64_t T, const void* x,
   return forward_impl(d, T, x, w_router, bias, w_gate_up, s_gate_up, w_down,
                       s_down, out, topk_idx, topk_w, logits, workspace,
                       ws_bytes, stream, nullptr);
+}
+
+int beam_moe_forward_residual(const beam_moe_desc* d, int64_t T, const void* x,
+                              const float* w_router, const float* bias,
+                              const void* w_gate_up, const float* s_gate_up,
+                              const void* w_down, const float* s_down,
+                              const float* norm_weight, float eps, int32_t step,
+                              float* residual, void* out, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(d, T, &p);
+  if (st != BEAM_OK) return st;
+  if (step < 1 || !(eps >= 0.0f) || !isfinite(eps)) return BEAM_ERR_INVALID_ARG;
+  // the token's fp32 row is held in LDS between the norm's two passes
+  if (static_cast<int64_t>(d->hidden) * 4 > 160 * 1024) return BEAM_ERR_UNSUPPORTED;
+  if (T == 0) return BEAM_OK;
+  if (!norm_weight || !residual || !aligned16(norm_weight) || !aligned16(residual))
+    return BEAM_ERR_INVALID_ARG;
+  Epilogue ep;
+  ep.gamma = norm_weight;
+  ep.eps = eps;
+  ep.a = static_cast<float>(sqrt(static_cast<double>(step - 1) / static_cast<double>(step)));
+  ep.b = static_cast<float>(1.0 / sqrt(static_cast<double>(step)));
+  ep.residual = residual;
+  return forward_impl(d, T, x, w_router, bias, w_gate_up, s_gate_up, w_down, s_down, out,
+                      nullptr, nullptr, nullptr, workspace, ws_bytes, stream, nullptr, &ep);
 }
 
 int beam_moe_forward_timed(const beam_moe_desc* d, int64_t T, const void* x,

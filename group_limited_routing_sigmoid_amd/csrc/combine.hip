@@ -3,6 +3,14 @@
 // once to the output dtype.  There is no shared expert to add ("Reflection
 // Releases Beam ...", section "Where Beam Saves and Where the Memory Bill
 // Comes In").  One workgroup per token, 8 consecutive columns per thread.
+//
+// combine_residual also applies the step after the block: the post-sublayer
+// RMSNorm of SandwichNorm and the depth-scaled FP32 residual stream
+// ("Reflection Beam", section "Hybrid Attention and Unusual Residuals";
+// pretraining paragraph of "Reflection AI Introduces Beam ..."):
+//   r = sqrt((k-1)/k) r + (1/sqrt(k)) o / sqrt(mean(o^2) + eps) * gamma
+// on the fp32 block output o before any rounding, held in LDS between the
+// two passes; the sum of squares is reduced in a fixed order.
 #include "common.h"
 #include "internal.h"
 
@@ -68,14 +76,108 @@ __global__ __launch_bounds__(128) void combine(
   }
 }
 
+template <typename YT>
+__device__ __forceinline__ void store_out(void* out, int64_t at, const float* acc, bool bf16) {
+  if (bf16) {
+    u32x4 q;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      q[i] = static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * i + 1])) << 16);
+    st16(static_cast<uint16_t*>(out) + at, q);
+  } else {
+    float* o = static_cast<float*>(out) + at;
+    st16(o, u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]),
+                  __float_as_uint(acc[2]), __float_as_uint(acc[3])});
+    st16(o + 4, u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]),
+                      __float_as_uint(acc[6]), __float_as_uint(acc[7])});
+  }
+}
+
+constexpr int kCombineThreads = 128;
+
+template <typename YT, bool OUT_BF16>
+__global__ __launch_bounds__(kCombineThreads) void combine_residual(
+    const YT* __restrict__ y, const int32_t* __restrict__ slot_of,
+    const float* __restrict__ w, void* __restrict__ out, int K, int H,
+    const float* __restrict__ gamma, float eps, float a, float b,
+    float* __restrict__ residual) {
+  extern __shared__ float row[];  // the token's fp32 block output, H values
+  __shared__ float part[kCombineThreads / kWave];
+  const int64_t t = blockIdx.x;
+  int slot[16];
+  float wk[16];
+  for (int k = 0; k < K; ++k) {
+    slot[k] = slot_of[t * K + k];
+    wk[k] = w[t * K + k];
+  }
+  float ss = 0.0f;
+  for (int c = threadIdx.x * 8; c < H; c += kCombineThreads * 8) {
+    float acc[8] = {};
+    for (int k = 0; k < K; ++k) {
+      float v[8];
+      load8<YT>(y + static_cast<int64_t>(slot[k]) * H + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wk[k], v[i], acc[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      row[c + i] = acc[i];
+      ss = __builtin_fmaf(acc[i], acc[i], ss);
+    }
+    if (out) store_out<YT>(out, t * H + c, acc, OUT_BF16);
+  }
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  if (threadIdx.x % kWave == 0) part[threadIdx.x / kWave] = ss;
+  __syncthreads();
+  float total = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kCombineThreads / kWave; ++i) total += part[i];
+  const float inv = 1.0f / sqrtf(total / static_cast<float>(H) + eps);
+  for (int c = threadIdx.x * 8; c < H; c += kCombineThreads * 8) {
+    float* r = residual + t * H + c;
+    const u32x4 r0 = ld16(r), r1 = ld16(r + 4);
+    const u32x4 g0 = ld16(gamma + c), g1 = ld16(gamma + c + 4);
+    float nr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float rv = __uint_as_float(i < 4 ? r0[i] : r1[i - 4]);
+      const float gv = __uint_as_float(i < 4 ? g0[i] : g1[i - 4]);
+      const float n = row[c + i] * inv * gv;
+      nr[i] = __builtin_fmaf(a, rv, b * n);
+    }
+    st16(r, u32x4{__float_as_uint(nr[0]), __float_as_uint(nr[1]), __float_as_uint(nr[2]),
+                  __float_as_uint(nr[3])});
+    st16(r + 4, u32x4{__float_as_uint(nr[4]), __float_as_uint(nr[5]), __float_as_uint(nr[6]),
+                      __float_as_uint(nr[7])});
+  }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const Plan& p, const int32_t* slot_of,
                           const float* w, void* out, void* ws, hipStream_t s,
-                          Timer* tm) {
+                          Timer* tm, const Epilogue* ep) {
   const dim3 grid(static_cast<unsigned>(p.T)), block(128);
   const bool y_f32 = p.wdt == BEAM_F32 || p.stream_path;
   const bool out_bf16 = p.act == BEAM_BF16;
+  if (ep) {
+    const size_t lds = static_cast<size_t>(p.H) * sizeof(float);
+#define BEAM_COMBINE_RES(YT, OB, YP)                                                        \
+  BEAM_LAUNCH(tm, "combine_residual", (combine_residual<YT, OB>), grid, dim3(kCombineThreads), \
+              lds, s, YP, slot_of, w, out, p.K, p.H, ep->gamma, ep->eps, ep->a, ep->b,       \
+              ep->residual)
+    if (y_f32) {
+      const float* y = ws_at<float>(ws, p.off_y);
+      if (out_bf16) BEAM_COMBINE_RES(float, true, y); else BEAM_COMBINE_RES(float, false, y);
+    } else {
+      const uint16_t* y = ws_at<uint16_t>(ws, p.off_y);
+      if (out_bf16) BEAM_COMBINE_RES(uint16_t, true, y); else BEAM_COMBINE_RES(uint16_t, false, y);
+    }
+#undef BEAM_COMBINE_RES
+    return hipGetLastError();
+  }
   if (y_f32) {
     const float* y = ws_at<float>(ws, p.off_y);
     if (out_bf16)

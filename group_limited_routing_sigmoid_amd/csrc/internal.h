@@ -85,8 +85,18 @@ hipError_t launch_experts_f32(const Plan& p, const float* x,
                               const float* w_gate_up, const float* w_down,
                               void* ws, hipStream_t s, Timer* tm);
 // combine.hip
+// Post-block epilogue fused into the combine: residual = a * residual +
+// b * RMSNorm(block output) * gamma per token (a = sqrt((k-1)/k), b = 1/sqrt(k)).
+struct Epilogue {
+  const float* gamma;  // [H]
+  float eps, a, b;
+  float* residual;     // [T, H] fp32, in place
+};
+
+// out may be null when ep is given (the block output is then not stored).
 hipError_t launch_combine(const Plan& p, const int32_t* slot_of,
-                          const float* w, void* out, void* ws, hipStream_t s, Timer* tm);
+                          const float* w, void* out, void* ws, hipStream_t s,
+                          Timer* tm, const Epilogue* ep = nullptr);
 // fp8.hip
 hipError_t launch_quant_e4m3(int64_t rows, int64_t cols, int32_t dtype,
                              const void* v, uint8_t* q, float* scales,

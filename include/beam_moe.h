@@ -160,6 +160,31 @@ int beam_moe_forward(const beam_moe_desc* desc, int64_t T, const void* x,
                      int32_t* topk_idx, float* topk_w, float* logits,
                      void* workspace, size_t ws_bytes, void* stream);
 
+/* beam_moe_forward followed, in the same combine kernel, by the step after
+ * the block in a Beam layer stack: the post-sublayer RMSNorm of SandwichNorm
+ * and the depth-scaled FP32 residual stream ("Reflection Beam", section
+ * "Hybrid Attention and Unusual Residuals": at step k the stream is scaled
+ * by sqrt((k-1)/k) and the sublayer output added with weight 1/sqrt(k);
+ * SandwichNorm and FP32 residual accumulation from the pretraining paragraph
+ * of "Reflection AI Introduces Beam ...").  Per token t, with o the fp32
+ * block output before any rounding:
+ *   residual[t] = sqrt((k-1)/k) * residual[t]
+ *               + (1/sqrt(k)) * o / sqrt(mean(o^2) + eps) * norm_weight
+ *   norm_weight  device [H] fp32 (the norm's weights; the pages give none)
+ *   eps          >= 0 and finite (not on the pages; 1e-6 is usual)
+ *   step         k >= 1 (k = 1 discards the incoming residual)
+ *   residual     device [T, H] fp32, read and written in place
+ *   out          device [T, H] act_dtype block output, or NULL to skip it
+ * Other arguments as beam_moe_forward (routing outputs are not returned).
+ * Requires H * 4 <= 160 KiB (BEAM_ERR_UNSUPPORTED otherwise). */
+int beam_moe_forward_residual(const beam_moe_desc* desc, int64_t T, const void* x,
+                              const float* w_router, const float* bias,
+                              const void* w_gate_up, const float* s_gate_up,
+                              const void* w_down, const float* s_down,
+                              const float* norm_weight, float eps, int32_t step,
+                              float* residual, void* out, void* workspace,
+                              size_t ws_bytes, void* stream);
+
 /* Auxiliary-loss-free load balancing step.  The load-balancing paragraph of
  * "Reflection AI Introduces Beam ..." says Beam builds on DeepSeek-V3's
  * bias-update balancing with a cosine decay of the update speed; the rule

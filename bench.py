@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="time a plain 4 GiB device copy instead (the known-size "
+                         "kernel that scales HBM byte counters)")
     return ap.parse_args()
 
 
@@ -56,18 +59,48 @@ def kernel_bytes_flops(name, T, S, H, I, E, touched, wbytes):
     return None, None
 
 
+def sources_sha256(paths):
+    """SHA-256 over the listed source files (repository-relative), in order."""
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def traffic_for(kernel, workload):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
+    were taken on the current kernel sources; else None."""
     p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
-    src = os.path.join(ROOT, rec["source"])
-    if not os.path.exists(src):
+    try:
+        h = sources_sha256(rec["sources"])
+    except (OSError, KeyError):
         return None
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    return rec["bytes_per_launch"] if h == rec["source_sha256"] else None
+    return rec["bytes_per_launch"] if h == rec["sources_sha256"] else None
+
+
+def calibrate_copy(steps):
+    """A plain device copy of 4 GiB (torch's copy kernel): reads and writes
+    known byte counts, so HBM counters of other kernels can be scaled."""
+    import torch
+    n = 4 * 2**30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n,
+                      "ms": ms, "GBps_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}),
+          flush=True)
 
 
 def read_sclk():
@@ -139,6 +172,9 @@ def main():
               "this build has no multi-GPU path (the block runs whole on one "
               "MI355X).", file=sys.stderr)
         sys.exit(2)
+    if a.calibrate_copy:
+        calibrate_copy(max(a.steps, 1))
+        return
     import numpy as np
     import torch
 

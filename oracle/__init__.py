@@ -40,6 +40,15 @@ What each oracle function follows, and what pins it (tests/test_oracle_*.py):
                       constant-row closed form of the norm and its scale
                       invariance.  The norm's eps and weights are not on the
                       pages: caller inputs.
+  * MX codecs      -- OCP Microscaling v1.0: E2M1 elements pinned against
+                      the specification's value table (tests/golden) and a
+                      brute-force nearest-even encoder; E8M0 scales against
+                      torch.float8_e8m0fnu; the shared-exponent rule by the
+                      block maximum landing in the element format's top
+                      binade; MXFP8 elements against torch e4m3fn of the
+                      exactly scaled values.  MXFP4 weights with MXFP8
+                      activations stand in for the pages' 4-bit (NVFP4)
+                      checkpoint: parity with NVFP4 itself is not claimed.
   * e4m3 codec     -- pinned against torch.float8_e4m3fn on all 256 codes and
                       on random values.  The FP8 activation recipe (per-128
                       amax/448 scales) is a reading the pages do not fix:
@@ -54,7 +63,7 @@ import numpy as np
 
 from . import build as _build
 
-F32, BF16, E4M3 = 0, 1, 2
+F32, BF16, E4M3, MXFP4 = 0, 1, 2, 3
 
 _lib = None
 
@@ -94,6 +103,14 @@ def lib():
         L.bo_route.restype = i32
         L.bo_logits.argtypes = [ctypes.POINTER(Shape), i64, vp, i32, vp, vp, i32]
         L.bo_logits.restype = None
+        L.bo_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.bo_e2m1_decode.restype = ctypes.c_double
+        L.bo_e2m1_encode.argtypes = [ctypes.c_double]
+        L.bo_e2m1_encode.restype = ctypes.c_uint8
+        L.bo_mx_scale.argtypes = [ctypes.c_double, i32]
+        L.bo_mx_scale.restype = ctypes.c_uint8
+        L.bo_quant_mx.argtypes = [vp, i64, i32, vp, vp]
+        L.bo_quant_mx.restype = None
         L.bo_quant_e4m3.argtypes = [vp, i64, i32, vp, vp]
         L.bo_quant_e4m3.restype = None
         L.bo_forward_tokens.argtypes = [ctypes.POINTER(Shape), i64, vp, vp, i32,
@@ -170,6 +187,35 @@ def e4m3_encode(v) -> np.ndarray:
                     dtype=np.uint8)
 
 
+def e2m1_decode(codes) -> np.ndarray:
+    """OCP MX FP4 (E2M1) values of 4-bit codes."""
+    f = lib().bo_e2m1_decode
+    return np.array([f(int(c)) for c in np.asarray(codes).ravel()])
+
+
+def e2m1_encode(v) -> np.ndarray:
+    f = lib().bo_e2m1_encode
+    return np.array([f(float(a)) for a in np.asarray(v, np.float64).ravel()], dtype=np.uint8)
+
+
+def mx_scale(amax, emax_elem) -> int:
+    """E8M0 code of an MX block's shared scale."""
+    return int(lib().bo_mx_scale(float(amax), int(emax_elem)))
+
+
+def quant_mx(v, fmt: int):
+    """MX quantisation of each row of v [rows, n] (n a multiple of 32):
+    fmt 4 -> (E2M1 codes packed [rows, n/2] uint8, E8M0 scales [rows, n/32]);
+    fmt 8 -> (E4M3 codes [rows, n] uint8, E8M0 scales)."""
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float32))
+    rows, n = v.reshape(-1, v.shape[-1]).shape
+    q = np.zeros((rows, n // 2 if fmt == 4 else n), np.uint8)
+    sc = np.empty((rows, n // 32), np.uint8)
+    lib().bo_quant_mx(_ptr(v), rows * n, int(fmt), _ptr(q), _ptr(sc))
+    return (q.reshape(v.shape[:-1] + (q.shape[-1],)),
+            sc.reshape(v.shape[:-1] + (n // 32,)))
+
+
 def quant_e4m3(v, block: int = 128):
     """Per-block dynamic e4m3 quantisation of each row of v [rows, n]."""
     v = np.ascontiguousarray(np.asarray(v, dtype=np.float32))
@@ -214,8 +260,9 @@ def forward_tokens(shape, tokens, x, idx, w, w_gate_up, w_down,
                    s_gate_up=None, s_down=None, act_quant: bool = False,
                    nthreads: int = 0) -> np.ndarray:
     """binary64 block output for the listed tokens given their routing.
-    Weights may be f32, bf16 (uint16 bits) or e4m3 codes (uint8) with their
-    per-128x128 scales."""
+    Weights may be f32, bf16 (uint16 bits), e4m3 codes (uint8) with fp32
+    per-128x128 scales, or MXFP4 (E2M1 codes packed two per byte, uint8)
+    with E8M0 scales (uint8) per 32 values of a row."""
     sh = shape_of(shape)
     tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
     xa = _np(x)
@@ -225,10 +272,15 @@ def forward_tokens(shape, tokens, x, idx, w, w_gate_up, w_down,
     wd = _np(w_down)
     dt = _dtype_code(wgu)
     assert _dtype_code(wd) == dt
-    sgu = None if s_gate_up is None else np.ascontiguousarray(_np(s_gate_up), np.float32)
-    sdn = None if s_down is None else np.ascontiguousarray(_np(s_down), np.float32)
+    sgu = None if s_gate_up is None else np.ascontiguousarray(_np(s_gate_up))
+    sdn = None if s_down is None else np.ascontiguousarray(_np(s_down))
     if dt == E4M3:
         assert sgu is not None and sdn is not None
+        if sgu.dtype == np.uint8:        # E8M0 scales: packed MXFP4 weights
+            assert sdn.dtype == np.uint8
+            dt = MXFP4
+        else:
+            sgu, sdn = sgu.astype(np.float32), sdn.astype(np.float32)
     out = np.empty((tok.size, sh.hidden), np.float64)
     rc = lib().bo_forward_tokens(
         ctypes.byref(sh), tok.size, _ptr(tok), _ptr(xa), _dtype_code(xa),

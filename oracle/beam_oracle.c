@@ -45,6 +45,7 @@
 #define BO_F32 0
 #define BO_BF16 1
 #define BO_E4M3 2
+#define BO_MXFP4 3
 
 typedef struct {
   int32_t hidden;           /* H */
@@ -105,6 +106,69 @@ uint8_t bo_e4m3_encode(float f) {
   int code = ((e + 7) << 3) | man;
   if (code > 0x7E) code = 0x7E;
   return sign | (uint8_t)code;
+}
+
+/* OCP Microscaling (MX) formats, specification v1.0: FP4 E2M1 elements (1
+ * sign, 2 exponent bits with bias 1, 1 mantissa bit, no inf/NaN, largest 6)
+ * and E8M0 shared scales (2^(s - 127)); a block is 32 consecutive values. */
+double bo_e2m1_decode(uint8_t nib) {
+  int sign = (nib >> 3) & 1, ex = (nib >> 1) & 3, man = nib & 1;
+  double v = (ex == 0) ? 0.5 * man : ldexp(1.0 + 0.5 * man, ex - 1);
+  return sign ? -v : v;
+}
+
+/* Nearest E2M1 value, ties to the even code, magnitudes above 6 saturate. */
+uint8_t bo_e2m1_encode(double v) {
+  uint8_t sign = signbit(v) ? 8 : 0;
+  double a = fabs(v);
+  if (isnan(v)) return sign | 7;
+  uint8_t best = 0;
+  for (uint8_t c = 1; c < 8; ++c) {
+    double d = fabs(bo_e2m1_decode(c) - a), db = fabs(bo_e2m1_decode(best) - a);
+    if (d < db || (d == db && (c & 1) == 0)) best = c;
+  }
+  return sign | best;
+}
+
+/* Shared exponent of an MX block: floor(log2(amax)) - emax_elem (2 for
+ * E2M1, 8 for E4M3), clamped to the E8M0 range [-127, 127]; -127 for an
+ * all-zero block.  Returns the E8M0 code (exponent + 127). */
+uint8_t bo_mx_scale(double amax, int emax_elem) {
+  int x = -127;
+  if (amax > 0.0) {
+    int e;
+    frexp(amax, &e);            /* amax = m 2^e, m in [0.5, 1): floor(log2) = e - 1 */
+    x = e - 1 - emax_elem;
+    if (x < -127) x = -127;
+    if (x > 127) x = 127;
+  }
+  return (uint8_t)(x + 127);
+}
+
+/* MX quantisation of n values (n a multiple of 32): fmt 4 -> E2M1 codes
+ * packed two per byte (even index in the low nibble), fmt 8 -> E4M3 codes;
+ * one E8M0 scale per block; elements = encode(v / 2^x) (exact scaling). */
+void bo_quant_mx(const float* v, int64_t n, int fmt, uint8_t* q, uint8_t* scales) {
+  const int emax = (fmt == 4) ? 2 : 8;
+  for (int64_t b0 = 0; b0 < n; b0 += 32) {
+    double amax = 0.0;
+    for (int j = 0; j < 32; ++j) {
+      double a = fabs((double)v[b0 + j]);
+      if (a > amax) amax = a;
+    }
+    const uint8_t s = bo_mx_scale(amax, emax);
+    scales[b0 / 32] = s;
+    for (int j = 0; j < 32; ++j) {
+      const double u = ldexp((double)v[b0 + j], 127 - (int)s);
+      if (fmt == 4) {
+        const uint8_t c = bo_e2m1_encode(u);
+        const int64_t i = b0 + j;
+        if (i % 2 == 0) q[i / 2] = c; else q[i / 2] |= (uint8_t)(c << 4);
+      } else {
+        q[b0 + j] = bo_e4m3_encode((float)u);
+      }
+    }
+  }
 }
 
 /* ------------------------------------------------------------------------ */
@@ -269,6 +333,15 @@ void bo_quant_e4m3(const float* v, int64_t n, int block, uint8_t* q,
   }
 }
 
+/* Round-trip a row through MXFP8 (E4M3 elements, E8M0 per 32 values). */
+static void fake_quant_row_mx(const double* in, int64_t n, double* out, float* tmpf,
+                              uint8_t* tmpq, uint8_t* tmps) {
+  for (int64_t i = 0; i < n; ++i) tmpf[i] = (float)in[i];
+  bo_quant_mx(tmpf, n, 8, tmpq, tmps);
+  for (int64_t i = 0; i < n; ++i)
+    out[i] = ldexp(bo_e4m3_decode(tmpq[i]), (int)tmps[i / 32] - 127);
+}
+
 /* Round-trip a row through bo_quant_e4m3 and return the dequantised values. */
 static void fake_quant_row(const double* in, int64_t n, int block, double* out,
                            float* tmpf, uint8_t* tmpq, float* tmps) {
@@ -296,14 +369,21 @@ void bo_logits(const bo_shape* sh, int64_t T, const void* x, int x_dtype,
   }
 }
 
-/* Weight element with its FP8 block scale applied (scale arrays are
- * [rows/128, cols/128] per expert; unused for f32/bf16). */
-static double weight(const void* w, int dtype, const float* sc, int64_t e,
+/* Weight element with its block scale applied.  FP8: fp32 scale arrays
+ * [rows/128, cols/128] per expert.  MXFP4: codes [rows, cols/2] (even column
+ * in the low nibble) and E8M0 scales [rows, cols/32] per expert. */
+static double weight(const void* w, int dtype, const void* sc, int64_t e,
                      int64_t rows, int64_t cols, int64_t r, int64_t c) {
+  if (dtype == BO_MXFP4) {
+    const int64_t row = e * rows + r;
+    const uint8_t b = ((const uint8_t*)w)[row * (cols / 2) + c / 2];
+    const uint8_t s = ((const uint8_t*)sc)[row * (cols / 32) + c / 32];
+    return ldexp(bo_e2m1_decode((c % 2) ? (b >> 4) : (b & 15)), (int)s - 127);
+  }
   double v = load_val(w, dtype, (e * rows + r) * cols + c);
   if (dtype == BO_E4M3) {
     int64_t nb_c = cols / 128;
-    v *= (double)sc[(e * (rows / 128) + r / 128) * nb_c + c / 128];
+    v *= (double)((const float*)sc)[(e * (rows / 128) + r / 128) * nb_c + c / 128];
   }
   return v;
 }
@@ -314,19 +394,21 @@ static double weight(const void* w, int dtype, const float* sc, int64_t e,
  *     h = silu(g) * v, silu(g) = g / (1 + e^-g)      (SwiGLU MLP)
  *     y_e = h W_d[e]^T
  *   out[t] = sum_k w_k y_{e_k}, in rank order; no shared expert ([P2]).
- * Everything in binary64.  act_quant = 1 first round-trips x (per token, per
- * 128 channels) and h (per assignment, per 128 channels) through
- * bo_quant_e4m3, which is the FP8 variant's activation recipe.
+ * Everything in binary64.  act_quant = 1 first round-trips x (per token) and
+ * h (per assignment) through the variant's activation recipe: bo_quant_e4m3
+ * per 128 channels for FP8 weights, MXFP8 (bo_quant_mx, 32 channels) for
+ * MXFP4 weights.
  * tokens[n] lists which rows of x to evaluate; out is [n, H]. */
 int bo_forward_tokens(const bo_shape* sh, int64_t n, const int64_t* tokens,
                       const void* x, int x_dtype, const int32_t* idx,
                       const float* w, const void* w_gate_up,
-                      const float* s_gate_up, const void* w_down,
-                      const float* s_down, int w_dtype, int act_quant,
+                      const void* s_gate_up, const void* w_down,
+                      const void* s_down, int w_dtype, int act_quant,
                       double* out, int nthreads) {
   const int64_t H = sh->hidden, I = sh->intermediate;
   const int K = sh->top_k;
-  if (act_quant && (H % 128 || I % 128)) return -1;
+  const int64_t qb = (w_dtype == BO_MXFP4) ? 32 : 128;  /* activation block */
+  if (act_quant && (H % qb || I % qb)) return -1;
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
 #pragma omp parallel for schedule(dynamic, 1)
@@ -340,8 +422,11 @@ int bo_forward_tokens(const bo_shape* sh, int64_t n, const int64_t* tokens,
     float* tf = (float*)malloc(sizeof(float) * m);
     uint8_t* tq = (uint8_t*)malloc(m);
     float* ts = (float*)malloc(sizeof(float) * (m / 128 + 1));
+    uint8_t* tm = (uint8_t*)malloc(m / 32 + 1);
+    const int mx = w_dtype == BO_MXFP4;
     for (int64_t h = 0; h < H; ++h) xr[h] = load_val(x, x_dtype, t * H + h);
-    if (act_quant) fake_quant_row(xr, H, 128, xr, tf, tq, ts);
+    if (act_quant && mx) fake_quant_row_mx(xr, H, xr, tf, tq, tm);
+    else if (act_quant) fake_quant_row(xr, H, 128, xr, tf, tq, ts);
     for (int k = 0; k < K; ++k) {
       const int64_t e = idx[t * K + k];
       for (int64_t j = 0; j < I; ++j) {
@@ -352,7 +437,8 @@ int bo_forward_tokens(const bo_shape* sh, int64_t n, const int64_t* tokens,
         }
         hv[j] = g / (1.0 + exp(-g)) * v;
       }
-      if (act_quant) fake_quant_row(hv, I, 128, hv, tf, tq, ts);
+      if (act_quant && mx) fake_quant_row_mx(hv, I, hv, tf, tq, tm);
+      else if (act_quant) fake_quant_row(hv, I, 128, hv, tf, tq, ts);
       const double wk = (double)w[t * K + k];
       for (int64_t o = 0; o < H; ++o) {
         double y = 0.0;
@@ -362,6 +448,7 @@ int bo_forward_tokens(const bo_shape* sh, int64_t n, const int64_t* tokens,
       }
     }
     memcpy(out + i * H, acc, sizeof(double) * H);
+    free(tm);
     free(ts);
     free(tq);
     free(tf);

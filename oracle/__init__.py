@@ -43,10 +43,13 @@ What each oracle function follows, and what pins it (tests/test_oracle_*.py):
   * MX codecs      -- OCP Microscaling v1.0: E2M1 elements pinned against
                       the specification's value table (tests/golden) and a
                       brute-force nearest-even encoder; E8M0 scales against
-                      torch.float8_e8m0fnu; the shared-exponent rule by the
-                      block maximum landing in the element format's top
-                      binade; MXFP8 elements against torch e4m3fn of the
-                      exactly scaled values.  MXFP4 weights with MXFP8
+                      torch.float8_e8m0fnu; the OCP shared-exponent rule by
+                      the block maximum landing in the element format's top
+                      binade; the activation blocks' exponent (a reading:
+                      the smallest power of two keeping the maximum within
+                      448, no saturation) by its range (224, 448]; MXFP8
+                      elements against torch e4m3fn of the exactly scaled
+                      values.  MXFP4 weights with MXFP8
                       activations stand in for the pages' 4-bit (NVFP4)
                       checkpoint: parity with NVFP4 itself is not claimed.
   * e4m3 codec     -- pinned against torch.float8_e4m3fn on all 256 codes and
@@ -110,6 +113,8 @@ def lib():
         L.bo_mx_scale.argtypes = [ctypes.c_double, i32]
         L.bo_mx_scale.restype = ctypes.c_uint8
         L.bo_quant_mx.argtypes = [vp, i64, i32, vp, vp]
+        L.bo_mx8_act_scale.argtypes = [ctypes.c_double]
+        L.bo_mx8_act_scale.restype = ctypes.c_uint8
         L.bo_quant_mx.restype = None
         L.bo_quant_e4m3.argtypes = [vp, i64, i32, vp, vp]
         L.bo_quant_e4m3.restype = None
@@ -203,10 +208,16 @@ def mx_scale(amax, emax_elem) -> int:
     return int(lib().bo_mx_scale(float(amax), int(emax_elem)))
 
 
+def mx8_act_scale(amax) -> int:
+    """E8M0 code of the 4-bit variant's activation blocks (no saturation)."""
+    return int(lib().bo_mx8_act_scale(float(amax)))
+
+
 def quant_mx(v, fmt: int):
     """MX quantisation of each row of v [rows, n] (n a multiple of 32):
-    fmt 4 -> (E2M1 codes packed [rows, n/2] uint8, E8M0 scales [rows, n/32]);
-    fmt 8 -> (E4M3 codes [rows, n] uint8, E8M0 scales)."""
+    fmt 4 -> (E2M1 codes packed [rows, n/2] uint8, E8M0 scales [rows, n/32]),
+    OCP shared exponent; fmt 8 -> (E4M3 codes [rows, n] uint8, E8M0 scales),
+    the activation recipe's exponent (block maximum within 448)."""
     v = np.ascontiguousarray(np.asarray(v, dtype=np.float32))
     rows, n = v.reshape(-1, v.shape[-1]).shape
     q = np.zeros((rows, n // 2 if fmt == 4 else n), np.uint8)

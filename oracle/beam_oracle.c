@@ -145,18 +145,28 @@ uint8_t bo_mx_scale(double amax, int emax_elem) {
   return (uint8_t)(x + 127);
 }
 
+/* Shared exponent of the activation recipe of the 4-bit variant (a reading:
+ * the pages give no recipe for it): the smallest power of two 2^x with
+ * amax / 2^x <= 448, so the block maximum never saturates, clamped to the
+ * E8M0 range; -127 for an all-zero block.  Returns the E8M0 code. */
+uint8_t bo_mx8_act_scale(double amax) {
+  int s = bo_mx_scale(amax, 8);                   /* floor rule: amax/2^x < 512 */
+  if (amax > 0.0 && s < 254 && ldexp(amax, 127 - s) > 448.0) s += 1;
+  return (uint8_t)s;
+}
+
 /* MX quantisation of n values (n a multiple of 32): fmt 4 -> E2M1 codes
- * packed two per byte (even index in the low nibble), fmt 8 -> E4M3 codes;
- * one E8M0 scale per block; elements = encode(v / 2^x) (exact scaling). */
+ * packed two per byte (even index in the low nibble) with the OCP shared
+ * exponent; fmt 8 -> E4M3 codes with the activation exponent above; one E8M0
+ * scale per block; elements = encode(v / 2^x) (exact scaling). */
 void bo_quant_mx(const float* v, int64_t n, int fmt, uint8_t* q, uint8_t* scales) {
-  const int emax = (fmt == 4) ? 2 : 8;
   for (int64_t b0 = 0; b0 < n; b0 += 32) {
     double amax = 0.0;
     for (int j = 0; j < 32; ++j) {
       double a = fabs((double)v[b0 + j]);
       if (a > amax) amax = a;
     }
-    const uint8_t s = bo_mx_scale(amax, emax);
+    const uint8_t s = (fmt == 4) ? bo_mx_scale(amax, 2) : bo_mx8_act_scale(amax);
     scales[b0 / 32] = s;
     for (int j = 0; j < 32; ++j) {
       const double u = ldexp((double)v[b0 + j], 127 - (int)s);

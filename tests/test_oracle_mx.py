@@ -56,6 +56,28 @@ def test_scale_rule_top_binade(emax):
     np.testing.assert_array_equal(ref, 2.0 ** (codes.numpy().astype(np.float64) - 127))
 
 
+def test_activation_scale_rule_no_saturation():
+    # the 4-bit variant's activation exponent: smallest power of two with
+    # amax / 2^x <= 448, i.e. the block maximum lands in (224, 448]
+    rng = np.random.default_rng(9)
+    amax = np.concatenate([np.exp(rng.uniform(np.log(1e-30), np.log(1e30), 3000)),
+                           [448.0, 449.0, 224.0, 224.5, 1.0, 2.0 ** -120]])
+    for a in amax:
+        s = oracle.mx8_act_scale(a)
+        ratio = a / 2.0 ** (s - G["e8m0_bias"])
+        # (at the bottom of the E8M0 range the block maximum may sit lower)
+        assert (224.0 < ratio or s == 0) and ratio <= 448.0, (a, s)
+    assert oracle.mx8_act_scale(0.0) == 0
+    v = (rng.standard_normal((50, 64)) * 3.0).astype(np.float32)
+    q, sc = oracle.quant_mx(v, 8)
+    vals = torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.all(np.abs(vals) <= 448.0)
+    for r in range(50):
+        for b in range(2):
+            blk = np.abs(v[r, 32 * b:32 * b + 32]).max()
+            assert sc[r, b] == oracle.mx8_act_scale(blk)
+
+
 def test_mxfp8_elements_match_torch():
     rng = np.random.default_rng(3)
     v = (rng.standard_normal((9, 256)) * np.logspace(-3, 3, 9)[:, None]).astype(np.float32)

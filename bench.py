@@ -56,6 +56,13 @@ def kernel_bytes_flops(name, T, S, H, I, E, touched, wbytes):
         ybytes = 4 if name.startswith("stream") else 2
         return (touched * H * I * wbytes + S * I * 2 + S * H * ybytes,
                 2.0 * S * H * I)
+    # MXFP4 weights (wbytes includes the E8M0 bytes), MXFP8 activations
+    if name == "stream_gate_up_mx":
+        return (touched * 2 * I * H * wbytes + T * H * (1 + 1 / 32) + S * I * 2,
+                2.0 * S * 2 * I * H)
+    if name == "stream_down_mx":
+        return (touched * H * I * wbytes + S * I * (1 + 1 / 32) + S * H * 4,
+                2.0 * S * H * I)
     return None, None
 
 
@@ -203,7 +210,7 @@ def main():
     import torch
 
     import group_limited_routing_sigmoid_amd as gl
-    from synth import WORKLOADS, make_inputs, FP8
+    from synth import WORKLOADS, make_inputs, FP8, MXFP4
 
     w = WORKLOADS[a.workload]
     sh = w.shape
@@ -212,8 +219,7 @@ def main():
     T, H, I, E, K = inp.x.shape[0], sh.hidden, sh.intermediate, sh.n_experts, sh.top_k
     S = T * K
     flags = {"auto": 0, "stream": gl.PATH_STREAM, "grouped": gl.PATH_GROUPED}[a.path]
-    wdt = gl.FP8_E4M3 if w.weight_dtype == FP8 else (
-        gl.F32 if w.weight_dtype == "f32" else gl.BF16)
+    wdt = {FP8: gl.FP8_E4M3, MXFP4: gl.MXFP4, "f32": gl.F32}.get(w.weight_dtype, gl.BF16)
     act = gl.F32 if w.act_dtype == "f32" else gl.BF16
     d = gl.make_desc(sh, act, wdt, flags)
     ws = gl.Workspace(dev)
@@ -247,9 +253,10 @@ def main():
     kern_ms = {k: sum(v) / len(v) for k, v in per.items()}
     launches = {k: len(v) / a.steps for k, v in per.items()}
     dom = max(kern_ms, key=lambda k: kern_ms[k] * launches[k])
-    wbytes = 1 if w.weight_dtype == FP8 else (4 if w.weight_dtype == "f32" else 2)
+    wbytes = {FP8: 1, MXFP4: 0.5 + 1 / 32, "f32": 4}.get(w.weight_dtype, 2)
     kb, kf = kernel_bytes_flops(dom, T, S, H, I, E, touched, wbytes)
-    peak = FP8_PEAK_TFLOPS if w.weight_dtype == FP8 else (
+    # the e4m3 x E2M1 products of the MXFP4 path are priced at the fp8 rate
+    peak = FP8_PEAK_TFLOPS if w.weight_dtype in (FP8, MXFP4) else (
         FP32_PEAK_TFLOPS if w.weight_dtype == "f32" else BF16_PEAK_TFLOPS)
     # the kernel's bound is the larger of its memory time and its compute time
     mem_bound = kf is None or kb / (HBM_PEAK_GBS * 1e9) >= kf / (peak * 1e12)
@@ -280,7 +287,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp8": "fp8", "f32": "f32"}.get(w.weight_dtype, "bf16"),
+        "dtype": {"fp8": "fp8", "f32": "f32", "mxfp4": "mxfp4"}.get(w.weight_dtype, "bf16"),
         "data": "synthetic",
         "config": {"workload": a.workload, "tokens": T, "hidden": H,
                    "intermediate": I, "experts": E, "groups": sh.n_groups,

@@ -18,7 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbeam_moe.so")
 
-F32, BF16, FP8_E4M3 = 0, 1, 2
+F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
 ROUTE_LOGITS_IN, PATH_STREAM, PATH_GROUPED = 1 << 0, 1 << 1, 1 << 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
@@ -27,7 +27,7 @@ SYMBOLS = ("beam_status_string", "beam_moe_validate", "beam_moe_workspace_bytes"
            "beam_moe_forward", "beam_moe_timer_create", "beam_moe_timer_destroy",
            "beam_moe_timer_reset", "beam_moe_timer_count", "beam_moe_timer_read",
            "beam_moe_forward_timed", "beam_moe_bias_update", "beam_moe_bias_gamma",
-           "beam_moe_forward_residual")
+           "beam_moe_forward_residual", "beam_moe_quant_mxfp8")
 
 
 class Desc(ctypes.Structure):
@@ -66,6 +66,7 @@ def lib():
         L.beam_moe_route.argtypes = [D, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.beam_moe_permute.argtypes = [D, i64, vp, vp, vp, vp, vp, vp, sz, vp]
         L.beam_moe_quant_e4m3.argtypes = [i64, i64, i32, vp, vp, vp, vp]
+        L.beam_moe_quant_mxfp8.argtypes = [i64, i64, i32, vp, vp, vp, vp]
         L.beam_moe_forward.argtypes = [D, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                        vp, vp, vp, vp, sz, vp]
         L.beam_moe_forward_timed.argtypes = L.beam_moe_forward.argtypes + [vp]
@@ -256,6 +257,20 @@ def quant_e4m3(v: torch.Tensor, stream=None):
     _check(lib().beam_moe_quant_e4m3(rows, cols, dt, _p(v), _p(q), _p(s),
                                      _stream(stream)), "beam_moe_quant_e4m3")
     return q, s[:, :cols // 128]
+
+
+def quant_mxfp8(v: torch.Tensor, stream=None):
+    """beam_moe_quant_mxfp8 of a 2-D fp32/bf16 tensor: (codes uint8, E8M0
+    scales uint8 [rows, cols/32])."""
+    rows, cols = v.shape
+    if v.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(v.dtype)
+    dt = BF16 if v.dtype == torch.bfloat16 else F32
+    q = torch.empty(rows, cols, dtype=torch.uint8, device=v.device)
+    s = torch.empty(rows, max(cols // 32, 16), dtype=torch.uint8, device=v.device)
+    _check(lib().beam_moe_quant_mxfp8(rows, cols, dt, _p(v), _p(q), _p(s),
+                                      _stream(stream)), "beam_moe_quant_mxfp8")
+    return q, s[:, :cols // 32]
 
 
 class Timer:

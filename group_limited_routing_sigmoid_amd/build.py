@@ -4,7 +4,7 @@ hipcc, then one shared library.
 Flags:
   -Xclang -target-feature -Xclang -packed-fp32-ops
       no packed fp32 instructions anywhere;
-  -ffp-contract=off for router.hip and fp8.hip
+  -ffp-contract=off for router.hip, fp8.hip and mxfp4.hip
       the routing specification and the activation quantiser round every
       binary32 operation separately.
 """
@@ -22,8 +22,9 @@ BUILD = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "router.hip", "permute.hip", "experts_grouped.hip",
-           "experts_stream.hip", "experts_f32.hip", "combine.hip", "fp8.hip"]
-NO_CONTRACT = {"router.hip", "fp8.hip"}
+           "experts_stream.hip", "experts_f32.hip", "combine.hip", "fp8.hip",
+           "mxfp4.hip"]
+NO_CONTRACT = {"router.hip", "fp8.hip", "mxfp4.hip"}
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -85,6 +85,8 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
     p->stream_path = p->S < 4 * static_cast<int64_t>(p->E);
   // streaming kernels exist for bf16 weights only
   if (p->wdt != BEAM_BF16) p->stream_path = false;
+  // 4-bit MX weights run on the streaming kernels at every T
+  if (p->wdt == BEAM_MXFP4) p->stream_path = true;
   const int64_t S = p->S, E = p->E, H = p->H, I = p->I;
   p->max_tiles = S / kGemmBM + (S < E ? S : E) + 1;
   const bool f32 = p->wdt == BEAM_F32;
@@ -110,8 +112,16 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
   p->off_meta = take(kMetaWords * 4);
   p->off_active = take(E * 4);
   p->off_tile_off = take((E + 1) * 4);
-  p->off_h = take(S * I * (f32 ? 4 : 2));
+  // h is fp32 on the fp32 path and before the MXFP8 quantisation of the
+  // 4-bit path, bf16 otherwise
+  p->off_h = take(S * I * ((f32 || p->wdt == BEAM_MXFP4) ? 4 : 2));
   p->off_y = take(S * H * ((f32 || p->stream_path) ? 4 : 2));
+  if (p->wdt == BEAM_MXFP4) {
+    p->off_xq = take(T * H);
+    p->off_xs = take(T * (H / 32));
+    p->off_hq = take(S * I);
+    p->off_hs = take(S * (I / 32));
+  }
   if (p->wdt == BEAM_FP8_E4M3) {
     p->off_xq = take(T * H);
     p->off_xs = take(T * (H / 128) * 4);
@@ -147,7 +157,7 @@ int beam_moe_validate(const beam_moe_desc* d, int64_t T) {
     return BEAM_ERR_INVALID_ARG;
   if (d->act_dtype != BEAM_F32 && d->act_dtype != BEAM_BF16) return BEAM_ERR_INVALID_ARG;
   if (d->weight_dtype != BEAM_F32 && d->weight_dtype != BEAM_BF16 &&
-      d->weight_dtype != BEAM_FP8_E4M3)
+      d->weight_dtype != BEAM_FP8_E4M3 && d->weight_dtype != BEAM_MXFP4)
     return BEAM_ERR_INVALID_ARG;
   if (!(d->routed_scale > 0.0f) || !isfinite(d->routed_scale)) return BEAM_ERR_INVALID_ARG;
   const int E = d->n_experts, G = d->n_groups;
@@ -257,10 +267,22 @@ int beam_moe_quant_e4m3(int64_t rows, int64_t cols, int32_t dtype,
                                       static_cast<hipStream_t>(stream), nullptr));
 }
 
+int beam_moe_quant_mxfp8(int64_t rows, int64_t cols, int32_t dtype,
+                         const void* v, uint8_t* q, uint8_t* scales, void* stream) {
+  if (rows < 0 || cols < 0 || (dtype != BEAM_F32 && dtype != BEAM_BF16))
+    return BEAM_ERR_INVALID_ARG;
+  if (cols % 128) return BEAM_ERR_UNSUPPORTED;
+  if (rows == 0 || cols == 0) return BEAM_OK;
+  if (!v || !q || !scales || !aligned16(v) || !aligned16(q) || !aligned16(scales))
+    return BEAM_ERR_INVALID_ARG;
+  return hip_status(launch_quant_mxfp8(rows, cols, dtype, v, q, scales,
+                                       static_cast<hipStream_t>(stream), nullptr));
+}
+
 static int forward_impl(const beam_moe_desc* d, int64_t T, const void* x,
                         const float* w_router, const float* bias,
-                        const void* w_gate_up, const float* s_gate_up,
-                        const void* w_down, const float* s_down, void* out,
+                        const void* w_gate_up, const void* s_gate_up,
+                        const void* w_down, const void* s_down, void* out,
                         int32_t* topk_idx, float* topk_w, float* logits,
                         void* workspace, size_t ws_bytes, void* stream,
                         Timer* tm, const Epilogue* ep = nullptr) {
@@ -270,9 +292,10 @@ static int forward_impl(const beam_moe_desc* d, int64_t T, const void* x,
   if (T == 0) return BEAM_OK;
   const bool lin = d->flags & BEAM_ROUTE_LOGITS_IN;
   const bool fp8 = d->weight_dtype == BEAM_FP8_E4M3;
+  const bool mx4 = d->weight_dtype == BEAM_MXFP4;
   if (!x || !w_gate_up || !w_down || (!out && !ep)) return BEAM_ERR_INVALID_ARG;
   if (lin ? !logits : !w_router) return BEAM_ERR_INVALID_ARG;
-  if (fp8 && (!s_gate_up || !s_down)) return BEAM_ERR_INVALID_ARG;
+  if ((fp8 || mx4) && (!s_gate_up || !s_down)) return BEAM_ERR_INVALID_ARG;
   if (fp8 && !fp8_experts_built()) return BEAM_ERR_UNSUPPORTED;
   const void* ptrs[] = {x, w_router, bias, w_gate_up, s_gate_up, w_down,
                         s_down, out, topk_idx, topk_w, logits};
@@ -297,8 +320,15 @@ static int forward_impl(const beam_moe_desc* d, int64_t T, const void* x,
                            static_cast<const float*>(w_gate_up),
                            static_cast<const float*>(w_down), workspace, s, tm);
   else if (fp8)
-    e = launch_experts_fp8(p, x, static_cast<const uint8_t*>(w_gate_up), s_gate_up,
-                           static_cast<const uint8_t*>(w_down), s_down, workspace, s, tm);
+    e = launch_experts_fp8(p, x, static_cast<const uint8_t*>(w_gate_up),
+                           static_cast<const float*>(s_gate_up),
+                           static_cast<const uint8_t*>(w_down),
+                           static_cast<const float*>(s_down), workspace, s, tm);
+  else if (mx4)
+    e = launch_experts_mxfp4(p, x, static_cast<const uint8_t*>(w_gate_up),
+                             static_cast<const uint8_t*>(s_gate_up),
+                             static_cast<const uint8_t*>(w_down),
+                             static_cast<const uint8_t*>(s_down), workspace, s, tm);
   else if (p.stream_path)
     e = launch_stream_bf16(p, x, w_gate_up, w_down, workspace, s, tm);
   else
@@ -309,8 +339,8 @@ static int forward_impl(const beam_moe_desc* d, int64_t T, const void* x,
 
 int beam_moe_forward(const beam_moe_desc* d, int64_t T, const void* x,
                      const float* w_router, const float* bias,
-                     const void* w_gate_up, const float* s_gate_up,
-                     const void* w_down, const float* s_down, void* out,
+                     const void* w_gate_up, const void* s_gate_up,
+                     const void* w_down, const void* s_down, void* out,
                      int32_t* topk_idx, float* topk_w, float* logits,
                      void* workspace, size_t ws_bytes, void* stream) {
   return forward_impl(d, T, x, w_router, bias, w_gate_up, s_gate_up, w_down,
@@ -320,8 +350,8 @@ int beam_moe_forward(const beam_moe_desc* d, int64_t T, const void* x,
 
 int beam_moe_forward_residual(const beam_moe_desc* d, int64_t T, const void* x,
                               const float* w_router, const float* bias,
-                              const void* w_gate_up, const float* s_gate_up,
-                              const void* w_down, const float* s_down,
+                              const void* w_gate_up, const void* s_gate_up,
+                              const void* w_down, const void* s_down,
                               const float* norm_weight, float eps, int32_t step,
                               float* residual, void* out, void* workspace,
                               size_t ws_bytes, void* stream) {
@@ -346,8 +376,8 @@ int beam_moe_forward_residual(const beam_moe_desc* d, int64_t T, const void* x,
 
 int beam_moe_forward_timed(const beam_moe_desc* d, int64_t T, const void* x,
                            const float* w_router, const float* bias,
-                           const void* w_gate_up, const float* s_gate_up,
-                           const void* w_down, const float* s_down, void* out,
+                           const void* w_gate_up, const void* s_gate_up,
+                           const void* w_down, const void* s_down, void* out,
                            int32_t* topk_idx, float* topk_w, float* logits,
                            void* workspace, size_t ws_bytes, void* stream,
                            beam_moe_timer* timer) {

@@ -9,30 +9,6 @@
 namespace beam {
 namespace {
 
-// binary32 -> e4m3fn, round to nearest even, magnitudes >= 448 saturate.
-__device__ __forceinline__ uint32_t e4m3_rne(float f) {
-  const uint32_t bits = __float_as_uint(f);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const uint32_t mag = bits & 0x7FFFFFFFu;
-  if (mag > 0x7F800000u) return sign | 0x7Fu;            // NaN
-  const float a = __uint_as_float(mag);
-  if (a >= 448.0f) return sign | 0x7Eu;
-  if (a < 0.015625f) {                                   // below 2^-6: step 2^-9
-    return sign | static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
-  }
-  int ex = static_cast<int>(mag >> 23) - 127;            // -6 .. 8
-  uint32_t keep = (mag >> 20) & 7u;
-  const uint32_t rest = mag & 0xFFFFFu;
-  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ++keep;
-  if (keep == 8u) {
-    keep = 0;
-    ++ex;
-  }
-  uint32_t code = (static_cast<uint32_t>(ex + 7) << 3) | keep;
-  if (code > 0x7Eu) code = 0x7Eu;
-  return sign | code;
-}
-
 // One wave per (row, 128-column block); lane i handles columns 2i, 2i+1.
 template <bool BF16>
 __global__ __launch_bounds__(256) void quant_e4m3_rows(

@@ -70,6 +70,12 @@ hipError_t launch_router_gemm(const Plan& p, const void* x, const uint16_t* w3,
 hipError_t launch_permute(const Plan& p, const int32_t* idx, int32_t* counts,
                           int32_t* offsets, int32_t* slot_token,
                           int32_t* slot_of, void* ws, hipStream_t s, Timer* tm);
+// mxfp4.hip (4-bit MX weights, MXFP8 activations)
+hipError_t launch_quant_mxfp8(int64_t rows, int64_t cols, int32_t dtype, const void* v,
+                              uint8_t* q, uint8_t* scales, hipStream_t s, Timer* tm);
+hipError_t launch_experts_mxfp4(const Plan& p, const void* x, const uint8_t* w_gate_up,
+                                const uint8_t* s_gate_up, const uint8_t* w_down,
+                                const uint8_t* s_down, void* ws, hipStream_t s, Timer* tm);
 hipError_t launch_bias_update(const Plan& p, const int32_t* idx, float gamma,
                               float* bias, hipStream_t s, Timer* tm);
 // experts_grouped.hip (bf16 weights, tiled MFMA grouped GEMM)

@@ -1,0 +1,256 @@
+// 4-bit expert weights: OCP MX FP4 (E2M1 codes, two per byte, the even k in
+// the low nibble) with one E8M0 scale per 32 consecutive k of a weight row,
+// and activations quantised on the fly to MXFP8 (E4M3 codes, one E8M0 scale
+// per 32 channels, the scale the smallest power of two that keeps the
+// block's largest value within 448).  The pages ship a 4-bit checkpoint for other hardware
+// ("Hugging Face releases Beam ..." checkpoint paragraph; "Reflection Beam",
+// section "Where to run it"); MX is the 4-bit format the gfx950 matrix cores
+// scale in hardware: v_mfma_scale_f32_32x32x64_f8f6f4 multiplies each lane's
+// 32 k-values by 2^(scale - 127) for both operands, so the block scales are
+// exact and no vector work rescales the sums.
+//
+// The streaming kernels serve decode-sized batches: weights are the 32-row A
+// side (fp4), up to 32 tokens the B side (fp8).  Gate/up: a wave owns 16 gate
+// and the 16 matching up rows, whose products land in the same lane (rows r
+// and r + 16 are accumulator elements q and q + 8).  Down: a wave owns 32
+// rows of W_d.  Experts with more than 32 tokens are handled in chunks.
+#include "common.h"
+#include "internal.h"
+
+namespace beam {
+namespace {
+
+// Exponent of an activation block: the smallest power of two 2^x with
+// amax / 2^x <= 448 (the largest E4M3 value), so the block maximum never
+// saturates; clamped to the E8M0 range [-127, 127], -127 for a zero block.
+// floor(log2(amax)) - 8 puts amax / 2^x in [256, 512); one more when above 448.
+__device__ __forceinline__ int mx8_exponent(float amax) {
+  const int eb = (__float_as_uint(amax) >> 23) & 0xFF;  // amax >= 0
+  const int fl = (eb == 0) ? -127 : eb - 127;            // floor(log2), subnormals clamp
+  int x = max(-127, min(127, fl - 8));
+  if (amax > 0.0f && x < 127 && ldexpf(amax, -x) > 448.0f) ++x;
+  return x;
+}
+
+// One thread per 32-value block of a row: E4M3 codes of v * 2^-x (exact
+// scaling, round to nearest even, saturating) and the E8M0 code x + 127.
+template <bool BF16>
+__global__ __launch_bounds__(256) void quant_mxfp8_rows(
+    const void* __restrict__ v, int64_t rows, int64_t cols, uint8_t* __restrict__ q,
+    uint8_t* __restrict__ scales) {
+  const int64_t blk = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t nbc = cols / 32;
+  if (blk >= rows * nbc) return;
+  const int64_t at = (blk / nbc) * cols + (blk % nbc) * 32;
+  float a[32];
+  if (BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 w = ld16(static_cast<const uint16_t*>(v) + at + 8 * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+        a[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4 w = ld16(static_cast<const float*>(v) + at + 4 * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[4 * i + j] = __uint_as_float(w[j]);
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(a[i]));
+  const int x = mx8_exponent(amax);
+  u32x4 out[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) word |= e4m3_rne(ldexpf(a[4 * i + j], -x)) << (8 * j);
+    out[i / 4][i % 4] = word;
+  }
+  st16(q + at, out[0]);
+  st16(q + at + 16, out[1]);
+  scales[blk] = static_cast<uint8_t>(x + 127);
+}
+
+// D = A(32x64, E2M1) * B(64x32, E4M3) + C with per-lane E8M0 scales.  Lane
+// l = 32 h + r supplies row r of A and column r of B.  With E2M1 A (4
+// registers) the matrix cores read the lane's 32 nibbles as k = 16 h + j
+// (j < 16) and 32 + 16 h + (j - 16), and apply the lane's A scale to exactly
+// those; the B scale of lane l covers the same k positions of column r.  So
+// a lane hands over one contiguous 32-value weight block (bytes 16 h .. of
+// the 32-byte step) with its scale, and its B side is activation values
+// 16 h .. 16 h + 15 and 32 + 16 h .. 32 + 16 h + 15 of the 64-value step
+// (the same k positions) with the scale of activation block h; every
+// product then carries its own two block scales.
+__device__ __forceinline__ f32x16 mfma_mx(u32x4 a, u32x4 b0, u32x4 b1, f32x16 c, uint32_t sa,
+                                          uint32_t sb) {
+  const i32x8 av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  const i32x8 bv = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                    (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 0, 0, (int)sa, 0, (int)sb);
+}
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+#ifndef BEAM_MX_UNROLL
+#define BEAM_MX_UNROLL 8
+#endif
+constexpr int kMxUnroll = BEAM_MX_UNROLL;  // 64-deep k-steps in flight per wave
+static_assert(kMxUnroll % 2 == 0, "scale words cover two k-steps");
+
+// byte b of a little-endian array of words
+__device__ __forceinline__ uint32_t byte_of(const uint32_t* w, int b) {
+  return (w[b / 4] >> (8 * (b % 4))) & 0xFFu;
+}
+
+// Streams `rows32` (32 weight rows of n_k 64-deep steps, at w_row / s_row for
+// this lane's row) against the chunk's tokens: returns the 32x32 sums.
+// Lane l: weight row l % 32, token column l % 32 (valid if has_tok).
+__device__ __forceinline__ f32x16 mx_rows(const uint8_t* __restrict__ w_row,
+                                          const uint8_t* __restrict__ s_row,
+                                          const uint8_t* __restrict__ a_row,
+                                          const uint8_t* __restrict__ as_row, bool has_tok,
+                                          int n_k, int half) {
+  f32x16 acc0 = {}, acc1 = {};
+  for (int s0 = 0; s0 < n_k; s0 += kMxUnroll) {
+    u32x4 wv[kMxUnroll], xv[kMxUnroll][2];
+    uint32_t ws[kMxUnroll / 2], xs[kMxUnroll / 2];
+#pragma unroll
+    for (int u = 0; u < kMxUnroll; ++u) {
+      const bool in = s0 + u < n_k;
+      wv[u] = in ? ld16(w_row + (s0 + u) * 32 + half * 16) : u32x4{0, 0, 0, 0};
+      xv[u][0] = (in && has_tok) ? ld16(a_row + (s0 + u) * 64 + half * 16) : u32x4{0, 0, 0, 0};
+      xv[u][1] = (in && has_tok) ? ld16(a_row + (s0 + u) * 64 + 32 + half * 16) : u32x4{0, 0, 0, 0};
+    }
+    // scale bytes of steps s0 .. s0+U-1: 2 per step (the two 32-value halves)
+#pragma unroll
+    for (int i = 0; i < kMxUnroll / 2; ++i) {
+      const bool in = s0 + 2 * i < n_k;
+      ws[i] = in ? *reinterpret_cast<const uint32_t*>(s_row + 2 * s0 + 4 * i) : 127u;
+      xs[i] = (in && has_tok) ? *reinterpret_cast<const uint32_t*>(as_row + 2 * s0 + 4 * i)
+                              : 0x7F7F7F7Fu;
+    }
+#pragma unroll
+    for (int u = 0; u < kMxUnroll; ++u) {
+      const uint32_t sa = byte_of(ws, 2 * u + half), sb = byte_of(xs, 2 * u + half);
+      if (u % 2 == 0) acc0 = mfma_mx(wv[u], xv[u][0], xv[u][1], acc0, sa, sb);
+      else            acc1 = mfma_mx(wv[u], xv[u][0], xv[u][1], acc1, sa, sb);
+    }
+  }
+  return acc0 + acc1;
+}
+
+// Gate/up: one wave per (active expert j, 16-channel block); rows 0..15 of
+// its A side are gate channels cb*16 + r, rows 16..31 the up channels.
+// grid ceil(max_active * I/16 / 4), block 256.
+__global__ __launch_bounds__(kThreads) void stream_gate_up_mx(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+    const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws, float* __restrict__ h,
+    const int32_t* __restrict__ slot_token, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
+    const int32_t* __restrict__ meta, int H, int I) {
+  const int n_cb = I / 16;
+  const int item = blockIdx.x * kWaves + threadIdx.x / kWave;
+  const int j = item / n_cb, cb = item % n_cb;
+  if (j >= meta[kMetaActive]) return;
+  const int e = active[j];
+  const int off = offsets[e], cnt = counts[e];
+  const int lane = threadIdx.x % kWave, r = lane % 32, half = lane / 32;
+  const int wrow = (r < 16) ? (cb * 16 + r) : (I + cb * 16 + (r - 16));
+  const int64_t grow = static_cast<int64_t>(e) * 2 * I + wrow;
+  const uint8_t* w_row = w + grow * (H / 2);
+  const uint8_t* s_row = ws + grow * (H / 32);
+  for (int c0 = 0; c0 < cnt; c0 += 32) {
+    const bool has_tok = r < cnt - c0;
+    const int64_t tok = has_tok ? slot_token[off + c0 + r] : 0;
+    const f32x16 acc = mx_rows(w_row, s_row, xq + tok * H, xs + tok * (H / 32), has_tok, H / 64,
+                               half);
+    if (has_tok) {
+      // element q: row 8*(q/4) + 4*half + q%4 (q < 8: gate), up row + 16 in q + 8
+      float* hr = h + static_cast<int64_t>(off + c0 + r) * I + cb * 16;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) hr[8 * (q / 4) + 4 * half + q % 4] = silu(acc[q]) * acc[q + 8];
+    }
+  }
+}
+
+// Down: one wave per (active expert j, 32 rows of W_d); the tokens' h in
+// MXFP8.  grid ceil(max_active * H/32 / 4), block 256.
+__global__ __launch_bounds__(kThreads) void stream_down_mx(
+    const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs,
+    const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws, float* __restrict__ y,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ active, const int32_t* __restrict__ meta, int H, int I) {
+  const int n_ob = H / 32;
+  const int item = blockIdx.x * kWaves + threadIdx.x / kWave;
+  const int j = item / n_ob, ob = item % n_ob;
+  if (j >= meta[kMetaActive]) return;
+  const int e = active[j];
+  const int off = offsets[e], cnt = counts[e];
+  const int lane = threadIdx.x % kWave, r = lane % 32, half = lane / 32;
+  const int64_t grow = static_cast<int64_t>(e) * H + ob * 32 + r;
+  const uint8_t* w_row = w + grow * (I / 2);
+  const uint8_t* s_row = ws + grow * (I / 32);
+  for (int c0 = 0; c0 < cnt; c0 += 32) {
+    const bool has_tok = r < cnt - c0;
+    const int64_t slot = off + c0 + (has_tok ? r : 0);
+    const f32x16 acc = mx_rows(w_row, s_row, hq + slot * I, hs + slot * (I / 32), has_tok,
+                               I / 64, half);
+    if (has_tok) {
+      float* yr = y + static_cast<int64_t>(off + c0 + r) * H + ob * 32;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) yr[8 * (q / 4) + 4 * half + q % 4] = acc[q];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_mxfp8(int64_t rows, int64_t cols, int32_t dtype, const void* v,
+                              uint8_t* q, uint8_t* scales, hipStream_t s, Timer* tm) {
+  const dim3 grid(static_cast<unsigned>(ceil_div(rows * (cols / 32), 256)));
+  if (dtype == BEAM_BF16)
+    BEAM_LAUNCH(tm, "quant_mxfp8", quant_mxfp8_rows<true>, grid, dim3(256), 0, s, v, rows, cols, q, scales);
+  else
+    BEAM_LAUNCH(tm, "quant_mxfp8", quant_mxfp8_rows<false>, grid, dim3(256), 0, s, v, rows, cols, q, scales);
+  return hipGetLastError();
+}
+
+// x -> MXFP8; gate/up with SwiGLU -> h (fp32); h -> MXFP8; down -> y (fp32).
+hipError_t launch_experts_mxfp4(const Plan& p, const void* x, const uint8_t* w_gate_up,
+                                const uint8_t* s_gate_up, const uint8_t* w_down,
+                                const uint8_t* s_down, void* ws, hipStream_t s, Timer* tm) {
+  uint8_t* xq = ws_at<uint8_t>(ws, p.off_xq);
+  uint8_t* xs = ws_at<uint8_t>(ws, p.off_xs);
+  uint8_t* hq = ws_at<uint8_t>(ws, p.off_hq);
+  uint8_t* hs = ws_at<uint8_t>(ws, p.off_hs);
+  float* h = ws_at<float>(ws, p.off_h);
+  float* y = ws_at<float>(ws, p.off_y);
+  const int32_t* slot_token = ws_at<int32_t>(ws, p.off_slot_token);
+  const int32_t* counts = ws_at<int32_t>(ws, p.off_counts);
+  const int32_t* offsets = ws_at<int32_t>(ws, p.off_offsets);
+  const int32_t* active = ws_at<int32_t>(ws, p.off_active);
+  const int32_t* meta = ws_at<int32_t>(ws, p.off_meta);
+  const int64_t max_active = p.S < p.E ? p.S : p.E;
+  hipError_t e = launch_quant_mxfp8(p.T, p.H, BEAM_BF16, x, xq, xs, s, tm);
+  if (e != hipSuccess) return e;
+  BEAM_LAUNCH(tm, "stream_gate_up_mx", stream_gate_up_mx,
+              dim3(static_cast<unsigned>(ceil_div(max_active * (p.I / 16), kWaves))),
+              dim3(kThreads), 0, s, xq, xs, w_gate_up, s_gate_up, h, slot_token, counts,
+              offsets, active, meta, p.H, p.I);
+  e = launch_quant_mxfp8(p.S, p.I, BEAM_F32, h, hq, hs, s, tm);
+  if (e != hipSuccess) return e;
+  BEAM_LAUNCH(tm, "stream_down_mx", stream_down_mx,
+              dim3(static_cast<unsigned>(ceil_div(max_active * (p.H / 32), kWaves))),
+              dim3(kThreads), 0, s, hq, hs, w_down, s_down, y, counts, offsets, active, meta,
+              p.H, p.I);
+  return hipGetLastError();
+}
+
+}  // namespace beam

@@ -60,7 +60,9 @@ typedef enum {
 typedef enum {
   BEAM_F32 = 0,      /* IEEE binary32 */
   BEAM_BF16 = 1,     /* bfloat16 */
-  BEAM_FP8_E4M3 = 2  /* OCP e4m3fn codes with per-128x128-block fp32 scales */
+  BEAM_FP8_E4M3 = 2, /* OCP e4m3fn codes with per-128x128-block fp32 scales */
+  BEAM_MXFP4 = 3     /* OCP MX FP4: E2M1 codes two per byte (even k in the low
+                        nibble), one E8M0 scale byte per 32 k of a row */
 } beam_dtype;
 
 /* flags */
@@ -78,7 +80,7 @@ typedef struct {
   int32_t group_score_topn; /* 1 or 2 best biased scores summed per group: 2 */
   float routed_scale;       /* 2.5 */
   int32_t act_dtype;        /* dtype of x and out: BEAM_F32 or BEAM_BF16 */
-  int32_t weight_dtype;     /* BEAM_F32 (needs act F32), BEAM_BF16, BEAM_FP8_E4M3 */
+  int32_t weight_dtype;     /* BEAM_F32 (needs act F32), BEAM_BF16, BEAM_FP8_E4M3, BEAM_MXFP4 */
   uint32_t flags;           /* BEAM_* flags above */
 } beam_moe_desc;
 
@@ -138,25 +140,43 @@ int beam_moe_permute(const beam_moe_desc* desc, int64_t T,
 int beam_moe_quant_e4m3(int64_t rows, int64_t cols, int32_t dtype,
                         const void* v, uint8_t* q, float* scales, void* stream);
 
+/* Per-row MXFP8 quantisation (the MXFP4 variant's activation recipe, OCP
+ * Microscaling layout): for each block of 32 columns, x = the smallest
+ * integer with amax / 2^x <= 448, clamped to [-127, 127] (-127 for an
+ * all-zero block), code = e4m3(v * 2^-x) (exact scaling, round to nearest
+ * even), scale byte x + 127.  (OCP's own rule, floor(log2(amax)) - 8, can
+ * saturate the block maximum; this one never does.)
+ *   v       device [rows, cols] in `dtype` (BEAM_F32 or BEAM_BF16)
+ *   q       device [rows, cols] uint8 codes
+ *   scales  device [rows, cols/32] uint8 E8M0
+ * cols % 128 == 0.  No workspace. */
+int beam_moe_quant_mxfp8(int64_t rows, int64_t cols, int32_t dtype,
+                         const void* v, uint8_t* q, uint8_t* scales, void* stream);
+
 /* The whole block.
  *   x          device [T, H] act_dtype
  *   w_router   device [E, H] fp32 (unused with BEAM_ROUTE_LOGITS_IN)
  *   bias       device [E] fp32 or NULL
  *   w_gate_up  device [E, 2I, H] weight_dtype: rows 0..I-1 gate, I..2I-1 up
- *   s_gate_up  device [E, 2I/128, H/128] fp32 block scales (FP8 only, else NULL)
- *   w_down     device [E, H, I] weight_dtype
- *   s_down     device [E, H/128, I/128] fp32 block scales (FP8 only, else NULL)
+ *              (MXFP4: [E, 2I, H/2] bytes)
+ *   s_gate_up  device block scales, NULL for f32/bf16 weights: FP8 fp32
+ *              [E, 2I/128, H/128], positive; MXFP4 E8M0 bytes [E, 2I, H/32]
+ *   w_down     device [E, H, I] weight_dtype (MXFP4: [E, H, I/2] bytes)
+ *   s_down     as s_gate_up: FP8 fp32 [E, H/128, I/128]; MXFP4 bytes [E, H, I/32]
  *   out        device [T, H] act_dtype
  *   topk_idx, topk_w  device [T, K] outputs of the router, or NULL
  *   logits     device [T, E] fp32: output, or input with BEAM_ROUTE_LOGITS_IN;
  *              may be NULL without that flag
  * FP8 weights also quantise x and h per token per 128 channels
  * (beam_moe_quant_e4m3's recipe) and run e4m3 matrix products with binary32
- * accumulation and block scales applied per 128-deep slice. */
+ * accumulation and block scales applied per 128-deep slice.  MXFP4 weights
+ * quantise x and h to MXFP8 (beam_moe_quant_mxfp8's recipe) and run E2M1 x
+ * E4M3 matrix products whose E8M0 block scales the matrix cores apply, with
+ * binary32 accumulation. */
 int beam_moe_forward(const beam_moe_desc* desc, int64_t T, const void* x,
                      const float* w_router, const float* bias,
-                     const void* w_gate_up, const float* s_gate_up,
-                     const void* w_down, const float* s_down, void* out,
+                     const void* w_gate_up, const void* s_gate_up,
+                     const void* w_down, const void* s_down, void* out,
                      int32_t* topk_idx, float* topk_w, float* logits,
                      void* workspace, size_t ws_bytes, void* stream);
 
@@ -179,8 +199,8 @@ int beam_moe_forward(const beam_moe_desc* desc, int64_t T, const void* x,
  * Requires H * 4 <= 160 KiB (BEAM_ERR_UNSUPPORTED otherwise). */
 int beam_moe_forward_residual(const beam_moe_desc* desc, int64_t T, const void* x,
                               const float* w_router, const float* bias,
-                              const void* w_gate_up, const float* s_gate_up,
-                              const void* w_down, const float* s_down,
+                              const void* w_gate_up, const void* s_gate_up,
+                              const void* w_down, const void* s_down,
                               const float* norm_weight, float eps, int32_t step,
                               float* residual, void* out, void* workspace,
                               size_t ws_bytes, void* stream);
@@ -230,8 +250,8 @@ int beam_moe_timer_read(beam_moe_timer* timer, int32_t i, const char** name,
  * the timer's capacity are dropped).  timer may be NULL. */
 int beam_moe_forward_timed(const beam_moe_desc* desc, int64_t T, const void* x,
                            const float* w_router, const float* bias,
-                           const void* w_gate_up, const float* s_gate_up,
-                           const void* w_down, const float* s_down, void* out,
+                           const void* w_gate_up, const void* s_gate_up,
+                           const void* w_down, const void* s_down, void* out,
                            int32_t* topk_idx, float* topk_w, float* logits,
                            void* workspace, size_t ws_bytes, void* stream,
                            beam_moe_timer* timer);

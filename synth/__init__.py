@@ -26,7 +26,7 @@ from typing import Optional
 
 import torch
 
-F32, BF16, FP8 = "f32", "bf16", "fp8"
+F32, BF16, FP8, MXFP4 = "f32", "bf16", "fp8", "mxfp4"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -57,7 +57,8 @@ class Workload:
     tokens: int
     shape: Shape
     act_dtype: str          # dtype of x and out: f32 or bf16
-    weight_dtype: str       # f32, bf16 or fp8 (e4m3 + 128x128 fp32 scales)
+    weight_dtype: str       # f32, bf16, fp8 (e4m3 + 128x128 fp32 scales) or
+                            # mxfp4 (E2M1 pairs + one E8M0 byte per 32 of a row)
     bias: str               # "zero", "uniform:<a>", "skew:<v>:<e0,e1,...>"
     seed: int
     expert_std: float = 0.02
@@ -71,6 +72,9 @@ WORKLOADS = {
     "prefill16k_skew": Workload("prefill16k_skew", 16384, BEAM, BF16, BF16,
                                 "skew:0.5:0,1,2,3,32,33,34,35", 3),
     "fp8_8k": Workload("fp8_8k", 8192, BEAM, BF16, FP8, "zero", 4),
+    # the 4-bit checkpoint form (MXFP4 stands in for the pages' NVFP4)
+    "mxfp4_decode64": Workload("mxfp4_decode64", 64, BEAM, BF16, MXFP4, "zero", 5),
+    "mxfp4_8k": Workload("mxfp4_8k", 8192, BEAM, BF16, MXFP4, "zero", 6),
 }
 
 
@@ -110,16 +114,46 @@ def _fp8_blocks(w: torch.Tensor, block: int = 128):
     return q.view(torch.uint8).contiguous(), scale.to(torch.float32).contiguous()
 
 
+_E2M1_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def _mxfp4_rows(w: torch.Tensor):
+    """Offline weight preparation for the 4-bit checkpoint form, OCP MX FP4:
+    per 32 consecutive values of a row the shared exponent is floor(log2 of
+    the block's largest magnitude) - 2 (E8M0 byte, exponent + 127, -127 for a
+    zero block); each value scaled by 2^-exponent goes to the nearest E2M1
+    value (ties to the even code, saturating at 6).  Codes are packed two per
+    byte, the even column in the low nibble."""
+    R, C = w.shape
+    wb = w.reshape(R, C // 32, 32)
+    amax = wb.abs().amax(dim=-1)
+    _, e = torch.frexp(amax)
+    x = torch.where(amax > 0, e - 3, torch.full_like(e, -127)).clamp(-127, 127)
+    u = torch.ldexp(wb, (-x)[..., None].to(wb.dtype))
+    a = u.abs().contiguous()
+    grid = torch.tensor(_E2M1_MAGNITUDES, dtype=a.dtype, device=a.device)
+    lo = (torch.searchsorted(grid, a, right=True) - 1).clamp(0, 7)
+    hi = (lo + 1).clamp(max=7)
+    dlo, dhi = a - grid[lo], grid[hi] - a
+    code = torch.where((dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0)), hi, lo)
+    code = (code + 8 * torch.signbit(u).to(code.dtype)).reshape(R, C).to(torch.uint8)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).contiguous()
+    return packed, (x + 127).to(torch.uint8).contiguous()
+
+
 @dataclasses.dataclass
 class Inputs:
     workload: Workload
     x: torch.Tensor            # [T, H] f32 or bf16
     w_router: torch.Tensor     # [E, H] f32
     bias: torch.Tensor         # [E] f32
-    w_gate_up: torch.Tensor    # [E, 2I, H] f32/bf16, or uint8 e4m3 codes
-    w_down: torch.Tensor       # [E, H, I]  f32/bf16, or uint8 e4m3 codes
-    s_gate_up: Optional[torch.Tensor] = None   # [E, 2I/128, H/128] f32 (fp8)
-    s_down: Optional[torch.Tensor] = None      # [E, H/128, I/128]  f32 (fp8)
+    w_gate_up: torch.Tensor    # [E, 2I, H] f32/bf16, uint8 e4m3 codes, or
+                               # [E, 2I, H/2] uint8 E2M1 pairs (mxfp4)
+    w_down: torch.Tensor       # [E, H, I] likewise ([E, H, I/2] for mxfp4)
+    s_gate_up: Optional[torch.Tensor] = None   # [E, 2I/128, H/128] f32 (fp8);
+                                               # [E, 2I, H/32] uint8 E8M0 (mxfp4)
+    s_down: Optional[torch.Tensor] = None      # [E, H/128, I/128] f32 (fp8);
+                                               # [E, H, I/32] uint8 E8M0 (mxfp4)
 
 
 def make_inputs(w: Workload, device="cpu", tokens: Optional[int] = None,
@@ -144,18 +178,28 @@ def make_inputs(w: Workload, device="cpu", tokens: Optional[int] = None,
     b = _bias(bspec, E, g, dev)
 
     fp8 = w.weight_dtype == FP8
-    st = torch.uint8 if fp8 else (torch.float32 if w.weight_dtype == F32
-                                  else torch.bfloat16)
-    wgu = torch.empty(E, 2 * I, H, dtype=st, device=dev)
-    wd = torch.empty(E, H, I, dtype=st, device=dev)
-    sgu = torch.empty(E, 2 * I // 128, H // 128, device=dev) if fp8 else None
-    sdn = torch.empty(E, H // 128, I // 128, device=dev) if fp8 else None
+    mx4 = w.weight_dtype == MXFP4
+    st = torch.uint8 if (fp8 or mx4) else (torch.float32 if w.weight_dtype == F32
+                                           else torch.bfloat16)
+    div = 2 if mx4 else 1
+    wgu = torch.empty(E, 2 * I, H // div, dtype=st, device=dev)
+    wd = torch.empty(E, H, I // div, dtype=st, device=dev)
+    sgu = sdn = None
+    if fp8:
+        sgu = torch.empty(E, 2 * I // 128, H // 128, device=dev)
+        sdn = torch.empty(E, H // 128, I // 128, device=dev)
+    if mx4:
+        sgu = torch.empty(E, 2 * I, H // 32, dtype=torch.uint8, device=dev)
+        sdn = torch.empty(E, H, I // 32, dtype=torch.uint8, device=dev)
     for e in range(E):
         a = torch.randn(2 * I, H, generator=g, device=dev) * w.expert_std
         c = torch.randn(H, I, generator=g, device=dev) * w.expert_std
         if fp8:
             wgu[e], sgu[e] = _fp8_blocks(a)
             wd[e], sdn[e] = _fp8_blocks(c)
+        elif mx4:
+            wgu[e], sgu[e] = _mxfp4_rows(a)
+            wd[e], sdn[e] = _mxfp4_rows(c)
         else:
             wgu[e] = a.to(st)
             wd[e] = c.to(st)

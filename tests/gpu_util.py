@@ -12,7 +12,7 @@ import torch
 
 import group_limited_routing_sigmoid_amd as gl
 import oracle
-from synth import WORKLOADS, Shape, make_inputs, small_shape, F32, BF16, FP8
+from synth import WORKLOADS, Shape, make_inputs, small_shape, F32, BF16, FP8, MXFP4
 
 
 def device():
@@ -31,7 +31,7 @@ def inputs(name: str, tokens=None, shape=None, bias=None, seed=None):
 
 def desc_for(w, shape, flags=0):
     act = gl.F32 if w.act_dtype == F32 else gl.BF16
-    wd = {F32: gl.F32, BF16: gl.BF16, FP8: gl.FP8_E4M3}[w.weight_dtype]
+    wd = {F32: gl.F32, BF16: gl.BF16, FP8: gl.FP8_E4M3, MXFP4: gl.MXFP4}[w.weight_dtype]
     return gl.make_desc(shape, act, wd, flags)
 
 

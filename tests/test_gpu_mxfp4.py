@@ -1,0 +1,82 @@
+"""4-bit expert weights (OCP MXFP4) with MXFP8 activations on the GPU.
+
+The activation quantiser is bit-exact against the oracle's MX codec.  Layer
+outputs: against the binary64 oracle on the same (exactly dequantised) MXFP4
+weights with unquantised activations, max rel err <= 6e-2 (the 8-bit
+activations set the error, as on the FP8 path); against the oracle that also
+round-trips x and h through MXFP8 (what the kernels compute, h quantised
+from fp32) the remaining difference is h evaluated in fp32 rather than
+binary64: an h value within ~1e-6 of an e4m3 rounding midpoint may land on
+the other side, moving that element by one e4m3 step (<= 2^-3 of it), about
+2^-3 / sqrt(I/2) of the output per flip (0.8% at I = 256, 0.25% at I =
+2560).  The bar for this comparison is 1e-2: a few flips pass, while a wrong
+operand layout or block scale gives errors of order one."""
+import numpy as np
+import pytest
+import torch
+
+import group_limited_routing_sigmoid_amd as gl
+import oracle
+from synth import BEAM, WORKLOADS, make_inputs, small_shape
+from gpu_util import desc_for, device, inputs, max_rel_err, oracle_forward
+
+pytestmark = pytest.mark.gpu
+
+MX_TOL = 6e-2
+EMU_TOL = 1e-2
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_quant_mxfp8_bit_exact(dtype):
+    dev = device()
+    g = torch.Generator().manual_seed(0)
+    v = torch.randn(37, 640, generator=g) * torch.logspace(-3, 3, 37)[:, None]
+    v[3, :32] = 0.0                                   # all-zero block
+    v[5, 130] = 1e-30                                 # tiny block maximum
+    v[7, 256:288] = torch.linspace(-500.0, 500.0, 32)  # saturation
+    v[9, 320:352] = 2.0 ** torch.arange(-16, 16).float()
+    v = v.to(dtype)
+    q, s = gl.quant_mxfp8(v.to(dev))
+    oq, os_ = oracle.quant_mx(v.float().numpy(), 8)
+    np.testing.assert_array_equal(q.cpu().numpy(), oq)
+    np.testing.assert_array_equal(s.cpu().numpy(), os_)
+
+
+def _check(inp, shape, tokens, label):
+    d = desc_for(WORKLOADS["mxfp4_8k"], shape)
+    out, idx, w, lg = gl.forward(d, inp.x, inp.w_router, inp.bias, inp.w_gate_up,
+                                 inp.w_down, inp.s_gate_up, inp.s_down,
+                                 return_routing=True)
+    torch.cuda.synchronize()
+    oi, ow, _ = oracle.route(shape, lg.cpu().numpy(), inp.bias.cpu().numpy())
+    np.testing.assert_array_equal(idx.cpu().numpy(), oi)
+    np.testing.assert_array_equal(w.cpu().numpy().view(np.uint32), ow.view(np.uint32))
+    got = out.float().cpu().numpy()[np.asarray(tokens)]
+    ref = oracle_forward(inp, shape, tokens, oi, ow, act_quant=False)
+    emu = oracle_forward(inp, shape, tokens, oi, ow, act_quant=True)
+    e_ref, e_emu = max_rel_err(got, ref), max_rel_err(got, emu)
+    print(f"{label}: max rel err {e_ref:.3e} vs MXFP4-weight oracle, "
+          f"{e_emu:.3e} vs MXFP8-activation emulation")
+    assert e_ref <= MX_TOL, e_ref
+    assert e_emu <= EMU_TOL, e_emu
+
+
+@pytest.mark.parametrize("T", [1, 5, 40, 300])
+def test_mxfp4_small(T):
+    sh = small_shape()
+    inp = make_inputs(WORKLOADS["mxfp4_8k"], device=device(), tokens=T, shape=sh,
+                      seed=70 + T)
+    _check(inp, sh, np.arange(T), f"mxfp4 small T={T}")
+
+
+def test_mxfp4_odd_widths_skewed():
+    # several 32-token chunks per hot expert; widths multiples of 128 only
+    sh = small_shape(hidden=384, intermediate=384)
+    inp = make_inputs(WORKLOADS["mxfp4_8k"], device=device(), tokens=500, shape=sh,
+                      seed=79, bias="skew:0.5:0,1,2,3,32,33,34,35")
+    _check(inp, sh, np.arange(0, 500, 3), "mxfp4 H=I=384 skew")
+
+
+def test_mxfp4_beam_decode64():
+    inp = inputs("mxfp4_decode64")
+    _check(inp, BEAM, np.arange(64), "mxfp4_decode64")

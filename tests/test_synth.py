@@ -40,3 +40,20 @@ def test_fp8_weights():
     # each 128x128 block reaches the largest code magnitude
     blk = a.w_gate_up.view(torch.float8_e4m3fn).float().abs().reshape(8, 2, 128, 2, 128)
     assert bool((blk.amax(dim=(2, 4)) == 448.0).all())
+
+
+def test_mxfp4_checkpoint_preparation_matches_oracle_codec():
+    # the synthetic 4-bit checkpoint follows the OCP MX FP4 rule the oracle
+    # implements (independently: torch ops here, C there)
+    import numpy as np
+    import oracle
+    from synth import _mxfp4_rows
+    g = torch.Generator().manual_seed(0)
+    w = torch.randn(64, 256, generator=g) * 0.02
+    w[3, :32] = 0.0
+    w[5, 40] = -0.0
+    w[7, 64:96] = torch.linspace(-7.0, 7.0, 32)
+    q, s = _mxfp4_rows(w)
+    oq, os_ = oracle.quant_mx(w.numpy(), 4)
+    np.testing.assert_array_equal(q.numpy(), oq)
+    np.testing.assert_array_equal(s.numpy(), os_)

@@ -63,6 +63,12 @@ def kernel_bytes_flops(name, T, S, H, I, E, touched, wbytes):
     if name == "stream_down_mx":
         return (touched * H * I * wbytes + S * I * (1 + 1 / 32) + S * H * 4,
                 2.0 * S * H * I)
+    if name == "grouped_gate_up_mx":
+        return (touched * 2 * I * H * wbytes + T * H * (1 + 1 / 32) + S * I * 4,
+                2.0 * S * 2 * I * H)
+    if name == "grouped_down_mx":
+        return (touched * H * I * wbytes + S * I * (1 + 1 / 32) + S * H * 4,
+                2.0 * S * H * I)
     return None, None
 
 

@@ -85,8 +85,13 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
     p->stream_path = p->S < 4 * static_cast<int64_t>(p->E);
   // streaming kernels exist for bf16 weights only
   if (p->wdt != BEAM_BF16) p->stream_path = false;
-  // 4-bit MX weights run on the streaming kernels at every T
-  if (p->wdt == BEAM_MXFP4) p->stream_path = true;
+  // 4-bit MX weights: streaming kernels for few tokens per expert, grouped
+  // tiles otherwise (same switch as bf16)
+  if (p->wdt == BEAM_MXFP4) {
+    if (p->flags & BEAM_PATH_STREAM) p->stream_path = true;
+    else if (p->flags & BEAM_PATH_GROUPED) p->stream_path = false;
+    else p->stream_path = p->S < 4 * static_cast<int64_t>(p->E);
+  }
   const int64_t S = p->S, E = p->E, H = p->H, I = p->I;
   p->max_tiles = S / kGemmBM + (S < E ? S : E) + 1;
   const bool f32 = p->wdt == BEAM_F32;
@@ -115,7 +120,7 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
   // h is fp32 on the fp32 path and before the MXFP8 quantisation of the
   // 4-bit path, bf16 otherwise
   p->off_h = take(S * I * ((f32 || p->wdt == BEAM_MXFP4) ? 4 : 2));
-  p->off_y = take(S * H * ((f32 || p->stream_path) ? 4 : 2));
+  p->off_y = take(S * H * ((f32 || p->stream_path || p->wdt == BEAM_MXFP4) ? 4 : 2));
   if (p->wdt == BEAM_MXFP4) {
     p->off_xq = take(T * H);
     p->off_xs = take(T * (H / 32));

@@ -160,7 +160,7 @@ hipError_t launch_combine(const Plan& p, const int32_t* slot_of,
                           const float* w, void* out, void* ws, hipStream_t s,
                           Timer* tm, const Epilogue* ep) {
   const dim3 grid(static_cast<unsigned>(p.T)), block(128);
-  const bool y_f32 = p.wdt == BEAM_F32 || p.stream_path;
+  const bool y_f32 = p.wdt == BEAM_F32 || p.wdt == BEAM_MXFP4 || p.stream_path;
   const bool out_bf16 = p.act == BEAM_BF16;
   if (ep) {
     const size_t lds = static_cast<size_t>(p.H) * sizeof(float);

@@ -14,8 +14,7 @@
 // and the 16 matching up rows, whose products land in the same lane (rows r
 // and r + 16 are accumulator elements q and q + 8).  Down: a wave owns 32
 // rows of W_d.  Experts with more than 32 tokens are handled in chunks.
-#include "common.h"
-#include "internal.h"
+#include "grouped_tile.h"
 
 namespace beam {
 namespace {
@@ -210,6 +209,176 @@ __global__ __launch_bounds__(kThreads) void stream_down_mx(
   }
 }
 
+// ---- grouped E2M1 x E4M3 GEMM for prefill-sized batches -------------------
+// Same work list and XCD order as the bf16 grouped GEMM (256-slot M tiles x
+// 256-row N tiles), 128 k per stage, two stages copied straight into LDS:
+// activation tile (E4M3, 256 slots x 128 bytes, the bf16 tiles' layout and
+// swizzle), weight tile (E2M1, 256 rows x 64 bytes), and both tiles' E8M0
+// bytes (4 per row per stage).  The weights are the MFMA A side, the slots
+// the B side, so a wave's accumulators are channels x slots; a wave owns 32
+// channels x 128 slots twice (gate and the matching up channels for gate/up,
+// 64 consecutive output columns for down).
+namespace mxg {
+
+using namespace tile;
+
+constexpr int kXBytes = BM * 128;            // activation tile per stage
+constexpr int kWBytes = BN * 64;             // weight tile per stage
+constexpr int kStage = kXBytes + kWBytes + 2 * BM * 4;
+typedef unsigned char Lds[2][kStage];
+
+__device__ __forceinline__ int wswz(int row, int chunk) {  // 64-byte weight rows
+  return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+enum Mode { kGateUp = 0, kDown = 1 };
+
+template <int NJ, int MODE>
+__device__ __forceinline__ void stage_products(const unsigned char* st, f32x16 (&acc)[2][4],
+                                               const int* wrow, const int* srow, int half) {
+  const unsigned char* X = st;
+  const unsigned char* W = st + kXBytes;
+  const uint32_t* XS = reinterpret_cast<const uint32_t*>(st + kXBytes + kWBytes);
+  const uint32_t* WS = XS + BM;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    u32x4 a[2];
+    uint32_t sa[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      a[f] = *reinterpret_cast<const u32x4*>(W + wswz(wrow[f], 2 * ks + half));
+      sa[f] = (WS[wrow[f]] >> (8 * (2 * ks + half))) & 0xFFu;
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int row = srow[j];
+      const int key = (row ^ (row >> 3)) & 7;
+      const u32x4 b0 = *reinterpret_cast<const u32x4*>(X + row * 128 + (((4 * ks + half) ^ key) << 4));
+      const u32x4 b1 = *reinterpret_cast<const u32x4*>(X + row * 128 + (((4 * ks + 2 + half) ^ key) << 4));
+      const uint32_t sb = (XS[row] >> (8 * (2 * ks + half))) & 0xFFu;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) acc[f][j] = mfma_mx(a[f], b0, b1, acc[f][j], sa[f], sb);
+    }
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
+    const uint8_t* __restrict__ xq,      // gate/up: xq [T,H]; down: hq [S,I]  (E4M3)
+    const uint8_t* __restrict__ xs,      // their E8M0 bytes [rows, K/32]
+    const uint8_t* __restrict__ w,       // W_gu [E,2I,H/2] or W_d [E,H,I/2] (E2M1 pairs)
+    const uint8_t* __restrict__ ws,      // [E,2I,H/32] or [E,H,I/32]
+    float* __restrict__ out,             // gate/up: h [S,I]; down: y [S,H]  (fp32)
+    const int32_t* __restrict__ slot_token, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off,
+    const int32_t* __restrict__ meta, int E, int H, int I, int n_nt) {
+  __shared__ __attribute__((aligned(16))) Lds lds;
+  Coords tc;
+  if (!tile_coords(counts, offsets, tile_off, meta, E, n_nt, tc)) return;
+  const int e = tc.e, nt = tc.nt, row0 = tc.row0, row_end = tc.row_end;
+  const int K = (MODE == kGateUp) ? H : I;
+  const int nkb = K / 128;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int wm = wave / 4, wn = wave % 4, r = lane % 32, half = lane / 32;
+  const int m_valid = min(BM, row_end - row0);
+  const int64_t nrows = (MODE == kGateUp) ? 2 * I : H;
+  const uint8_t* wb = w + static_cast<int64_t>(e) * nrows * (K / 2);
+  const uint8_t* wsb = ws + static_cast<int64_t>(e) * nrows * (K / 32);
+  auto wrow_of = [&](int t) {  // weight row of tile row t
+    return (MODE == kGateUp) ? ((t < 128) ? nt * 128 + t : I + nt * 128 + (t - 128))
+                             : min(nt * BN + t, H - 1);
+  };
+  auto slot_src = [&](int t) {  // activation row of tile row t (padded rows: a valid one)
+    const int slot = min(row0 + t, row_end - 1);
+    return (MODE == kGateUp) ? slot_token[slot] : slot;
+  };
+  // copy sources: activations 4 x 1 KiB regions per wave (8 rows of 128 B),
+  // weights 2 x 1 KiB (16 rows of 64 B); scale bytes: waves 0-3 the
+  // activation rows 64 w + lane, waves 4-7 the weight rows 64 (w-4) + lane
+  uint32_t x_off[kLoads], w_off[2];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int t = dma_row(wave, lane, i);
+    x_off[i] = static_cast<uint32_t>(slot_src(t)) * K + dma_chunk(t, lane) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = 16 * (wave + 8 * i) + lane / 4;
+    const int c = (lane % 4) ^ ((t >> 2) & 3);
+    w_off[i] = static_cast<uint32_t>(wrow_of(t)) * (K / 2) + c * 16;
+  }
+  const uint8_t* s_src = (wave < 4)
+      ? xs + static_cast<int64_t>(slot_src(64 * wave + lane)) * (K / 32)
+      : wsb + static_cast<int64_t>(wrow_of(64 * (wave - 4) + lane)) * (K / 32);
+  const int s_dst = kXBytes + kWBytes + ((wave < 4) ? 0 : BM * 4) + 256 * (wave % 4);
+  auto dma = [&](int buf, int kb) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+      dma16(xq + (x_off[i] + kb * 128), &lds[buf][dma_row(wave, 0, i) * 128]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(wb + (w_off[i] + kb * 64), &lds[buf][kXBytes + (wave + 8 * i) * 1024]);
+    dma4(s_src + kb * 4, &lds[buf][s_dst]);
+  };
+  // fragment rows: weights (A) and slots (B)
+  int wrow[2], srow[4];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+    wrow[f] = (MODE == kGateUp) ? (f * 128 + wn * 32 + r) : (wn * 64 + f * 32 + r);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) srow[j] = wm * 128 + j * 32 + r;
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[f][j] = f32x16{};
+  const int nj = wave_frags(m_valid, wm);
+  dma(0, 0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    if (kb + 1 < nkb) dma(buf ^ 1, kb + 1);
+    switch (nj) {
+      case 4: stage_products<4, MODE>(&lds[buf][0], acc, wrow, srow, half); break;
+      case 3: stage_products<3, MODE>(&lds[buf][0], acc, wrow, srow, half); break;
+      case 2: stage_products<2, MODE>(&lds[buf][0], acc, wrow, srow, half); break;
+      case 1: stage_products<1, MODE>(&lds[buf][0], acc, wrow, srow, half); break;
+      default: break;
+    }
+    __syncthreads();  // waits for this wave's copies, then for every wave
+  }
+  // element q of acc[f][j]: channel row 8*(q/4) + 4*half + q%4 of fragment f,
+  // slot row0 + wm*128 + 32 j + r; elements 4g .. 4g+3 are 4 consecutive
+  // channels of the lane's slot, stored as one 16-byte vector
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (j >= nj) continue;
+    const int slot = row0 + wm * 128 + j * 32 + r;
+    if (slot >= row_end) continue;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int cr = 8 * g + 4 * half;
+      if (MODE == kGateUp) {
+        f32x4 v;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = silu(acc[0][j][4 * g + t]) * acc[1][j][4 * g + t];
+        *reinterpret_cast<f32x4*>(out + static_cast<int64_t>(slot) * I + nt * 128 + wn * 32 + cr) = v;
+      } else {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const int col = nt * BN + wn * 64 + f * 32 + cr;  // H % 128 == 0: all 4 or none
+          if (col < H) {
+            const f32x4 v = {acc[f][j][4 * g], acc[f][j][4 * g + 1], acc[f][j][4 * g + 2],
+                             acc[f][j][4 * g + 3]};
+            *reinterpret_cast<f32x4*>(out + static_cast<int64_t>(slot) * H + col) = v;
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace mxg
+
 }  // namespace
 
 hipError_t launch_quant_mxfp8(int64_t rows, int64_t cols, int32_t dtype, const void* v,
@@ -240,6 +409,20 @@ hipError_t launch_experts_mxfp4(const Plan& p, const void* x, const uint8_t* w_g
   const int64_t max_active = p.S < p.E ? p.S : p.E;
   hipError_t e = launch_quant_mxfp8(p.T, p.H, BEAM_BF16, x, xq, xs, s, tm);
   if (e != hipSuccess) return e;
+  if (!p.stream_path) {
+    const int32_t* toff = ws_at<int32_t>(ws, p.off_tile_off);
+    const int nt_gu = p.I / 128;
+    const int nt_dn = static_cast<int>(ceil_div(p.H, tile::BN));
+    BEAM_LAUNCH(tm, "grouped_gate_up_mx", mxg::grouped_gemm_mx<mxg::kGateUp>,
+                tile::grid_for(p, nt_gu), dim3(tile::kThreads), 0, s, xq, xs, w_gate_up,
+                s_gate_up, h, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_gu);
+    e = launch_quant_mxfp8(p.S, p.I, BEAM_F32, h, hq, hs, s, tm);
+    if (e != hipSuccess) return e;
+    BEAM_LAUNCH(tm, "grouped_down_mx", mxg::grouped_gemm_mx<mxg::kDown>,
+                tile::grid_for(p, nt_dn), dim3(tile::kThreads), 0, s, hq, hs, w_down, s_down,
+                y, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_dn);
+    return hipGetLastError();
+  }
   BEAM_LAUNCH(tm, "stream_gate_up_mx", stream_gate_up_mx,
               dim3(static_cast<unsigned>(ceil_div(max_active * (p.I / 16), kWaves))),
               dim3(kThreads), 0, s, xq, xs, w_gate_up, s_gate_up, h, slot_token, counts,

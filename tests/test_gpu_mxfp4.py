@@ -42,8 +42,8 @@ def test_quant_mxfp8_bit_exact(dtype):
     np.testing.assert_array_equal(s.cpu().numpy(), os_)
 
 
-def _check(inp, shape, tokens, label):
-    d = desc_for(WORKLOADS["mxfp4_8k"], shape)
+def _check(inp, shape, tokens, label, path=0):
+    d = desc_for(WORKLOADS["mxfp4_8k"], shape, path)
     out, idx, w, lg = gl.forward(d, inp.x, inp.w_router, inp.bias, inp.w_gate_up,
                                  inp.w_down, inp.s_gate_up, inp.s_down,
                                  return_routing=True)
@@ -80,3 +80,18 @@ def test_mxfp4_odd_widths_skewed():
 def test_mxfp4_beam_decode64():
     inp = inputs("mxfp4_decode64")
     _check(inp, BEAM, np.arange(64), "mxfp4_decode64")
+
+
+@pytest.mark.parametrize("path", [gl.PATH_STREAM, gl.PATH_GROUPED])
+def test_mxfp4_both_paths(path):
+    sh = small_shape()
+    inp = make_inputs(WORKLOADS["mxfp4_8k"], device=device(), tokens=333, shape=sh, seed=88)
+    _check(inp, sh, np.arange(0, 333, 2), f"mxfp4 T=333 path={path}", path)
+
+
+def test_mxfp4_beam_8k_sampled():
+    inp = inputs("mxfp4_8k")
+    T = inp.x.shape[0]
+    rows = np.sort(np.random.default_rng(3).choice(T, 16, replace=False))
+    rows[-1] = T - 1
+    _check(inp, BEAM, rows, "mxfp4_8k sampled")

@@ -365,8 +365,9 @@ int beam_moe_forward_residual(const beam_moe_desc* d, int64_t T, const void* x,
   int st = make_plan(d, T, &p);
   if (st != BEAM_OK) return st;
   if (step < 1 || !(eps >= 0.0f) || !isfinite(eps)) return BEAM_ERR_INVALID_ARG;
-  // the token's fp32 row is held in LDS between the norm's two passes
-  if (static_cast<int64_t>(d->hidden) * 4 > 160 * 1024) return BEAM_ERR_UNSUPPORTED;
+  // the token's fp32 row is held in dynamic LDS between the norm's two
+  // passes; 64 KiB is the dynamic size every launch gets without attributes
+  if (static_cast<int64_t>(d->hidden) * 4 > 64 * 1024) return BEAM_ERR_UNSUPPORTED;
   if (T == 0) return BEAM_OK;
   if (!norm_weight || !residual || !aligned16(norm_weight) || !aligned16(residual))
     return BEAM_ERR_INVALID_ARG;

@@ -196,7 +196,8 @@ int beam_moe_forward(const beam_moe_desc* desc, int64_t T, const void* x,
  *   residual     device [T, H] fp32, read and written in place
  *   out          device [T, H] act_dtype block output, or NULL to skip it
  * Other arguments as beam_moe_forward (routing outputs are not returned).
- * Requires H * 4 <= 160 KiB (BEAM_ERR_UNSUPPORTED otherwise). */
+ * Requires H <= 16384 (the token's fp32 row is held in 64 KiB of LDS;
+ * BEAM_ERR_UNSUPPORTED otherwise). */
 int beam_moe_forward_residual(const beam_moe_desc* desc, int64_t T, const void* x,
                               const float* w_router, const float* bias,
                               const void* w_gate_up, const void* s_gate_up,

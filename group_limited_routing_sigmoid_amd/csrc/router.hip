@@ -48,8 +48,9 @@ __device__ __forceinline__ void split3(const float* w, bf16x8& hi, bf16x8& mid,
   }
 }
 
-// grid (ceil(T/32), E/64, ks), one wave: 32 tokens x 64 experts over
-// columns [z*kchunk, (z+1)*kchunk) of H.
+// grid (ceil(T/32), ceil(E/64), ks), one wave: 32 tokens x 64 experts (32
+// in the last block when E % 64 == 32) over columns [z*kchunk, (z+1)*kchunk)
+// of H.
 __global__ __launch_bounds__(64) void router_logits_mfma(
     const uint16_t* __restrict__ x, const float* __restrict__ wr,
     float* __restrict__ part, int64_t T, int H, int E, int kchunk) {
@@ -61,8 +62,9 @@ __global__ __launch_bounds__(64) void router_logits_mfma(
   int64_t tr = t0 + (lane % 32);
   if (tr > T - 1) tr = T - 1;
   const uint16_t* xp = x + tr * H + kb;
+  const bool has1 = e0 + 32 < E;  // second 32 experts of the block (wave-uniform)
   const float* wp0 = wr + static_cast<int64_t>(e0 + lane % 32) * H + kb;
-  const float* wp1 = wp0 + static_cast<int64_t>(32) * H;
+  const float* wp1 = wr + static_cast<int64_t>(has1 ? e0 + 32 + lane % 32 : e0 + lane % 32) * H + kb;
   f32x16 acc0 = {}, acc1 = {};
 #pragma unroll 2
   for (int k = 0; k < kchunk; k += 16) {
@@ -70,17 +72,20 @@ __global__ __launch_bounds__(64) void router_logits_mfma(
     float w0[8], w1[8];
     *reinterpret_cast<u32x4*>(w0) = ld16(wp0 + k);
     *reinterpret_cast<u32x4*>(w0 + 4) = ld16(wp0 + k + 4);
-    *reinterpret_cast<u32x4*>(w1) = ld16(wp1 + k);
-    *reinterpret_cast<u32x4*>(w1 + 4) = ld16(wp1 + k + 4);
-    bf16x8 h0, m0, l0, h1, m1, l1;
+    bf16x8 h0, m0, l0;
     split3(w0, h0, m0, l0);
-    split3(w1, h1, m1, l1);
     acc0 = mfma32x32x16(a, l0, acc0);
-    acc1 = mfma32x32x16(a, l1, acc1);
     acc0 = mfma32x32x16(a, m0, acc0);
-    acc1 = mfma32x32x16(a, m1, acc1);
     acc0 = mfma32x32x16(a, h0, acc0);
-    acc1 = mfma32x32x16(a, h1, acc1);
+    if (has1) {
+      *reinterpret_cast<u32x4*>(w1) = ld16(wp1 + k);
+      *reinterpret_cast<u32x4*>(w1 + 4) = ld16(wp1 + k + 4);
+      bf16x8 h1, m1, l1;
+      split3(w1, h1, m1, l1);
+      acc1 = mfma32x32x16(a, l1, acc1);
+      acc1 = mfma32x32x16(a, m1, acc1);
+      acc1 = mfma32x32x16(a, h1, acc1);
+    }
   }
   float* out = part + static_cast<int64_t>(z) * T * E;
 #pragma unroll
@@ -88,7 +93,7 @@ __global__ __launch_bounds__(64) void router_logits_mfma(
     const int64_t t = t0 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
     if (t < T) {
       out[t * E + e0 + lane % 32] = acc0[r];
-      out[t * E + e0 + 32 + lane % 32] = acc1[r];
+      if (has1) out[t * E + e0 + 32 + lane % 32] = acc1[r];
     }
   }
 }
@@ -301,8 +306,8 @@ hipError_t launch_router(const Plan& p, const void* x, const float* w_router,
                   dim3(256), 0, s, w_router, w3, p.E, p.H);
       const hipError_t e = launch_router_gemm(p, x, w3, buf, s, tm);
       if (e != hipSuccess) return e;
-    } else if (p.act == BEAM_BF16 && p.E % 64 == 0) {
-      dim3 grid(static_cast<unsigned>(ceil_div(p.T, 32)), p.E / 64, ks);
+    } else if (p.act == BEAM_BF16 && p.E % 32 == 0) {
+      dim3 grid(static_cast<unsigned>(ceil_div(p.T, 32)), static_cast<unsigned>(ceil_div(p.E, 64)), ks);
       BEAM_LAUNCH(tm, "router_logits_mfma", router_logits_mfma, grid, dim3(64), 0, s,
                          static_cast<const uint16_t*>(x), w_router, buf, p.T,
                          p.H, p.E, kchunk);

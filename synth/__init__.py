@@ -47,6 +47,11 @@ class Shape:
 
 BEAM = Shape(hidden=5120, intermediate=2560, n_experts=256, n_groups=8,
              topk_groups=4, top_k=8)
+# One GPU's share under expert parallelism over 8 GPUs: one group of 32
+# experts at the Beam widths; 16K tokens x top-8 over 32 experts gives about
+# 4K rows per expert.
+EP8_SHARE = Shape(hidden=5120, intermediate=2560, n_experts=32, n_groups=1,
+                  topk_groups=1, top_k=8)
 TINY = Shape(hidden=256, intermediate=128, n_experts=16, n_groups=4,
              topk_groups=2, top_k=4)
 
@@ -72,6 +77,8 @@ WORKLOADS = {
     "prefill16k_skew": Workload("prefill16k_skew", 16384, BEAM, BF16, BF16,
                                 "skew:0.5:0,1,2,3,32,33,34,35", 3),
     "fp8_8k": Workload("fp8_8k", 8192, BEAM, BF16, FP8, "zero", 4),
+    # the per-GPU share of an expert-parallel layer (32 local experts)
+    "ep8_share16k": Workload("ep8_share16k", 16384, EP8_SHARE, BF16, BF16, "zero", 7),
     # the 4-bit checkpoint form (MXFP4 stands in for the pages' NVFP4)
     "mxfp4_decode64": Workload("mxfp4_decode64", 64, BEAM, BF16, MXFP4, "zero", 5),
     "mxfp4_8k": Workload("mxfp4_8k", 8192, BEAM, BF16, MXFP4, "zero", 6),

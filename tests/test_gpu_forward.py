@@ -88,14 +88,14 @@ def test_beam_decode64(path):
            f"decode64 path={path}")
 
 
-@pytest.mark.parametrize("name", ["prefill4k", "prefill16k_skew"])
+@pytest.mark.parametrize("name", ["prefill4k", "prefill16k_skew", "ep8_share16k"])
 def test_beam_prefill_sampled(name):
     w = WORKLOADS[name]
     inp = inputs(name)
     T = inp.x.shape[0]
     rows = np.sort(np.random.default_rng(1).choice(T, 24, replace=False))
     rows[-1] = T - 1                       # last token of the ragged tail
-    _check(inp, BEAM, desc_for(w, BEAM), rows, BF16_TOL, f"{name} sampled")
+    _check(inp, w.shape, desc_for(w, w.shape), rows, BF16_TOL, f"{name} sampled")
 
 
 def test_forward_deterministic_and_permutation():

@@ -31,6 +31,10 @@ def _route_and_check(inp, shape, desc):
     ("prefill4k", 333, small_shape()),
     ("prefill4k", None, None),
     ("prefill16k_skew", None, None),
+    # expert counts that are multiples of 32 but not of 64 (partial blocks)
+    ("prefill4k", 300, small_shape(n_experts=32, n_groups=1, topk_groups=1)),
+    ("prefill4k", 300, small_shape(n_experts=96, n_groups=3, topk_groups=2)),
+    ("ep8_share16k", None, None),
 ])
 def test_route_bit_exact_from_gpu_logits(name, tokens, shape):
     w = WORKLOADS[name]

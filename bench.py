@@ -49,12 +49,20 @@ def parse():
 def kernel_bytes_flops(name, T, S, H, I, E, touched, wbytes):
     """Algorithmic bytes and flops of one launch of a kernel.  Weights of
     touched experts are read once; activations once; outputs written once."""
-    if name in ("stream_gate_up_bf16", "grouped_gate_up_bf16", "gate_up_fp8"):
+    if name in ("stream_gate_up_bf16", "grouped_gate_up_bf16"):
         return (touched * 2 * I * H * wbytes + T * H * 2 + S * I * 2,
                 2.0 * S * 2 * I * H)
-    if name in ("stream_down_bf16", "grouped_down_bf16", "down_fp8"):
+    if name in ("stream_down_bf16", "grouped_down_bf16"):
         ybytes = 4 if name.startswith("stream") else 2
         return (touched * H * I * wbytes + S * I * 2 + S * H * ybytes,
+                2.0 * S * H * I)
+    # e4m3 codes with fp32 scales per 128x128 weight block and per 128
+    # activation channels; gate/up writes h as codes + scales
+    if name == "gate_up_fp8":
+        return (touched * 2 * I * H * (1 + 4 / 16384) + T * H * (1 + 4 / 128)
+                + S * I * (1 + 4 / 128), 2.0 * S * 2 * I * H)
+    if name == "down_fp8":
+        return (touched * H * I * (1 + 4 / 16384) + S * I * (1 + 4 / 128) + S * H * 2,
                 2.0 * S * H * I)
     # MXFP4 weights (wbytes includes the E8M0 bytes), MXFP8 activations
     if name == "stream_gate_up_mx":
@@ -63,8 +71,8 @@ def kernel_bytes_flops(name, T, S, H, I, E, touched, wbytes):
     if name == "stream_down_mx":
         return (touched * H * I * wbytes + S * I * (1 + 1 / 32) + S * H * 4,
                 2.0 * S * H * I)
-    if name == "grouped_gate_up_mx":
-        return (touched * 2 * I * H * wbytes + T * H * (1 + 1 / 32) + S * I * 4,
+    if name == "grouped_gate_up_mx":  # writes h as MXFP8 codes + E8M0 bytes
+        return (touched * 2 * I * H * wbytes + T * H * (1 + 1 / 32) + S * I * (1 + 1 / 32),
                 2.0 * S * 2 * I * H)
     if name == "grouped_down_mx":
         return (touched * H * I * wbytes + S * I * (1 + 1 / 32) + S * H * 4,

@@ -207,6 +207,195 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(
   }
 }
 
+// ---- 128-row tiles with a ring of three copy stages -------------------------
+// For batches whose experts hold few rows the products are bound by the
+// weight bytes, and the 256-row tile's single stage in flight leaves HBM
+// under-used.  This form takes 128 x 256 tiles with three 48 KiB stages (two
+// in flight while one is consumed; 144 KiB of LDS).  (A 64-row form with four
+// 40 KiB stages measured no faster.)  A wave copies the same
+// c = 4 + n_a regions every stage (n_a: its A regions, 8 rows each, that hold
+// a valid row; rows past the last valid one inside such a region copy a
+// valid row), so "stage s has landed" is a count of the wave's outstanding
+// vector-memory operations: c times the stages issued after s.  8 waves:
+// 2 along M (BMS/2 rows each) x 4 along N, B rows as in the 256-row form.
+namespace small {
+
+template <int BMS>
+struct Geo {
+  static constexpr int kABytes = BMS * kRowBytes;
+  static constexpr int kStage = kABytes + kTileBytes;
+  static constexpr int kStages = 3;
+  static constexpr int kALoads = kABytes / (16 * kThreads);     // 2
+  static constexpr int kBLoads = kTileBytes / (16 * kThreads);  // 4
+  static constexpr int kWaveRows = BMS / 2;
+  static constexpr int kFrags = kWaveRows / 32;                 // 2
+};
+
+// Wait until at most n of this wave's vector-memory operations are
+// outstanding and its LDS reads are done, then meet every wave.  n is
+// wave-uniform; any count not listed waits for all (always safe).
+#define BEAM_RING_BARRIER(n) \
+  asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
+__device__ __forceinline__ void ring_barrier(int n) {
+  switch (n) {
+    case 4: BEAM_RING_BARRIER(4); break;
+    case 5: BEAM_RING_BARRIER(5); break;
+    case 6: BEAM_RING_BARRIER(6); break;
+    default: BEAM_RING_BARRIER(0); break;
+  }
+}
+#undef BEAM_RING_BARRIER
+
+template <int BMS, int NF>
+__device__ __forceinline__ void ring_mainloop(
+    const uint16_t* __restrict__ a_base, const uint32_t* a_off, const bool* a_ok, int c,
+    const uint16_t* __restrict__ b_base, const uint32_t* b_off, int nk,
+    unsigned char (&ring)[Geo<BMS>::kStages][Geo<BMS>::kStage],
+    f32x16 (&acc)[Geo<BMS>::kFrags][2], const int* arow, const int* brow) {
+  using G = Geo<BMS>;
+  constexpr int S = G::kStages, P = S - 1;  // ring size, stages in flight
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  auto dma = [&](int st, int k) {
+#pragma unroll
+    for (int i = 0; i < G::kALoads; ++i)
+      if (a_ok[i]) dma16(a_base + (a_off[i] + k), &ring[st][(wave + 8 * i) * 1024]);
+#pragma unroll
+    for (int i = 0; i < G::kBLoads; ++i)
+      dma16(b_base + (b_off[i] + k), &ring[st][G::kABytes + (wave + 8 * i) * 1024]);
+  };
+  struct Frags {
+    bf16x8 a[G::kFrags], b[2];
+  };
+  auto load_frags = [&](Frags& f, int st, int kk) {
+    const int ch = kk * 2 + lane / 32;
+#pragma unroll
+    for (int i = 0; i < NF; ++i)
+      f.a[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&ring[st][swz(arow[i], ch)]));
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+      f.b[n] = as_bf16x8(
+          *reinterpret_cast<const u32x4*>(&ring[st][G::kABytes + swz(brow[n], ch)]));
+  };
+  auto mfmas = [&](const Frags& f) {
+#pragma unroll
+    for (int i = 0; i < NF; ++i)
+#pragma unroll
+      for (int n = 0; n < 2; ++n) acc[i][n] = mfma32x32x16(f.a[i], f.b[n], acc[i][n]);
+  };
+  auto compute = [&](int st) {
+    Frags f0, f1;
+    load_frags(f0, st, 0);
+    load_frags(f1, st, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(f0, st, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(f1, st, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f1);
+  };
+#pragma unroll
+  for (int s = 0; s < P; ++s)
+    if (s < nk) dma(s, s * BK);
+  ring_barrier(c * (min(P, nk) - 1));  // stage 0 landed
+  int st = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt+P goes to the buffer last read in step kt-1 (ended by a barrier)
+    const int kn = kt + P;
+    if (kn < nk) dma(st == 0 ? S - 1 : st - 1, kn * BK);
+    if (NF > 0) compute(st);
+    ring_barrier(c * max(0, min(kn, nk - 1) - (kt + 1)));  // stage kt+1 landed
+    st = (st == S - 1) ? 0 : st + 1;
+  }
+}
+
+template <int BMS, int MODE>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_small(
+    const uint16_t* __restrict__ a_src, const uint16_t* __restrict__ w,
+    uint16_t* __restrict__ out, const int32_t* __restrict__ slot_token,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ meta, int E, int H,
+    int I, int n_nt) {
+  using G = Geo<BMS>;
+  __shared__ __attribute__((aligned(16))) unsigned char ring[G::kStages][G::kStage];
+  Coords tc;
+  if (!tile_coords(counts, offsets, tile_off, meta, E, n_nt, tc, BMS)) return;
+  const int e = tc.e, nt = tc.nt, row0 = tc.row0, row_end = tc.row_end;
+  const int K = (MODE == kGateUp) ? H : I;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int wm = wave / 4, wn = wave % 4;
+  const uint16_t* wbase = (MODE == kGateUp) ? w + static_cast<int64_t>(e) * 2 * I * H
+                                            : w + static_cast<int64_t>(e) * H * I;
+  const int m_valid = min(BMS, row_end - row0);
+  uint32_t a_off[G::kALoads], b_off[G::kBLoads];
+  bool a_ok[G::kALoads];
+  int c = G::kBLoads;
+  const int uwave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy
+#pragma unroll
+  for (int i = 0; i < G::kALoads; ++i) {
+    const int r = dma_row(wave, lane, i);
+    a_ok[i] = 8 * (uwave + 8 * i) < m_valid;  // the region's first row is valid
+    c += a_ok[i];
+    const int slot = min(row0 + r, row_end - 1);  // padding rows: a valid row
+    a_off[i] = ((MODE == kGateUp) ? static_cast<uint32_t>(slot_token[slot]) * H
+                                  : static_cast<uint32_t>(slot) * I) +
+               dma_chunk(r, lane) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < G::kBLoads; ++i) {
+    const int r = dma_row(wave, lane, i);
+    const int wrow = (MODE == kGateUp) ? ((r < 128) ? nt * 128 + r : I + nt * 128 + (r - 128))
+                                       : min(nt * BN + r, H - 1);
+    b_off[i] = static_cast<uint32_t>(wrow) * K + dma_chunk(r, lane) * 8;
+  }
+  int arow[G::kFrags], brow[2];
+#pragma unroll
+  for (int i = 0; i < G::kFrags; ++i) arow[i] = wm * G::kWaveRows + i * 32 + lane % 32;
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+    brow[n] = (MODE == kGateUp) ? (n * 128 + wn * 32 + lane % 32)
+                                : (wn * 64 + n * 32 + lane % 32);
+  f32x16 acc[G::kFrags][2];
+#pragma unroll
+  for (int i = 0; i < G::kFrags; ++i)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) acc[i][n] = f32x16{};
+  const int nf = min(G::kFrags, max(0, (m_valid - wm * G::kWaveRows + 31) / 32));
+  if (G::kFrags == 2 && nf == 2)
+    ring_mainloop<BMS, G::kFrags>(a_src, a_off, a_ok, c, wbase, b_off, K / BK, ring, acc, arow, brow);
+  else if (nf >= 1)
+    ring_mainloop<BMS, 1>(a_src, a_off, a_ok, c, wbase, b_off, K / BK, ring, acc, arow, brow);
+  else
+    ring_mainloop<BMS, 0>(a_src, a_off, a_ok, c, wbase, b_off, K / BK, ring, acc, arow, brow);
+#pragma unroll
+  for (int i = 0; i < G::kFrags; ++i) {
+    if (i >= nf) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = row0 + wm * G::kWaveRows + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+      if (row >= row_end) continue;
+      if (MODE == kGateUp) {
+        const int ch = nt * 128 + wn * 32 + lane % 32;
+        const float h = silu(acc[i][0][r]) * acc[i][1][r];
+        out[static_cast<int64_t>(row) * I + ch] = f32_to_bf16_bits(h);
+      } else {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const int col = nt * BN + wn * 64 + n * 32 + lane % 32;
+          if (col < H) out[static_cast<int64_t>(row) * H + col] = f32_to_bf16_bits(acc[i][n][r]);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace small
+
 // Router logits partials: part[z][t][e] = sum over k' in [z c, (z+1) c) of
 // x[t, k' mod H] W3[e, k'] with c = 3H/ks (W3 [E, 3H] holds the three bf16
 // terms of W_r one after another along k').  grid = ceil(T/256) * E/256 * ks.
@@ -287,6 +476,18 @@ hipError_t launch_grouped_bf16(const Plan& p, const void* x,
   uint16_t* y = ws_at<uint16_t>(ws, p.off_y);
   const int nt_gu = p.I / 128;
   const int nt_dn = static_cast<int>(ceil_div(p.H, BN));
+#define BEAM_SMALL_TILES(BMS)                                                                \
+  BEAM_LAUNCH(tm, "grouped_gate_up_bf16", (small::grouped_gemm_bf16_small<BMS, kGateUp>),    \
+              grid_for(p, nt_gu), dim3(kThreads), 0, s, static_cast<const uint16_t*>(x),      \
+              static_cast<const uint16_t*>(w_gate_up), h, slot_token, counts, offsets, toff,  \
+              meta, p.E, p.H, p.I, nt_gu);                                                    \
+  BEAM_LAUNCH(tm, "grouped_down_bf16", (small::grouped_gemm_bf16_small<BMS, kDown>),         \
+              grid_for(p, nt_dn), dim3(kThreads), 0, s, h,                                    \
+              static_cast<const uint16_t*>(w_down), y, slot_token, counts, offsets, toff,     \
+              meta, p.E, p.H, p.I, nt_dn);                                                    \
+  return hipGetLastError()
+  if (p.bm == 128) { BEAM_SMALL_TILES(128); }
+#undef BEAM_SMALL_TILES
   BEAM_LAUNCH(tm, "grouped_gate_up_bf16", grouped_gemm_bf16<kGateUp>, grid_for(p, nt_gu),
               dim3(kThreads), 0, s, static_cast<const uint16_t*>(x),
               static_cast<const uint16_t*>(w_gate_up), h, slot_token, counts,

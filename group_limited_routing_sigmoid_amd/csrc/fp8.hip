@@ -9,34 +9,48 @@
 namespace beam {
 namespace {
 
-// One wave per (row, 128-column block); lane i handles columns 2i, 2i+1.
+// 16 lanes per (row, 128-column block), 8 consecutive columns per lane (one
+// 16-byte load of bf16, two of fp32); a wave covers 4 blocks.  The block's
+// amax is reduced over its 16 lanes; scale = amax / 448 (1 for a zero block),
+// code = e4m3(v / scale) with binary32 division, as in the recipe.
 template <bool BF16>
 __global__ __launch_bounds__(256) void quant_e4m3_rows(
     const void* __restrict__ v, int64_t rows, int64_t cols,
     uint8_t* __restrict__ q, float* __restrict__ scales) {
-  const int lane = threadIdx.x % kWave;
-  const int64_t blk = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // 8-column group
   const int64_t nbc = cols / 128;
-  if (blk >= rows * nbc) return;
-  const int64_t r = blk / nbc, c = (blk % nbc) * 128 + 2 * lane;
-  float a0, a1;
+  const int64_t blk = g / 16;
+  const bool live = blk < rows * nbc;
+  const int64_t at = live ? (blk / nbc) * cols + (blk % nbc) * 128 + (g % 16) * 8 : 0;
+  float a[8];
   if (BF16) {
-    const uint32_t pair = *reinterpret_cast<const uint32_t*>(
-        static_cast<const uint16_t*>(v) + r * cols + c);
-    a0 = __uint_as_float(pair << 16);
-    a1 = __uint_as_float(pair & 0xFFFF0000u);
-  } else {
-    const float* p = static_cast<const float*>(v) + r * cols + c;
-    a0 = p[0];
-    a1 = p[1];
-  }
-  float m = fmaxf(fabsf(a0), fabsf(a1));
+    const u32x4 w = live ? ld16(static_cast<const uint16_t*>(v) + at) : u32x4{0, 0, 0, 0};
 #pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    for (int j = 0; j < 4; ++j) {
+      a[2 * j] = __uint_as_float(w[j] << 16);
+      a[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  } else {
+    const float* p = static_cast<const float*>(v) + at;
+    const u32x4 w0 = live ? ld16(p) : u32x4{0, 0, 0, 0};
+    const u32x4 w1 = live ? ld16(p + 4) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a[j] = __uint_as_float(w0[j]);
+      a[4 + j] = __uint_as_float(w1[j]);
+    }
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(a[j]));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));  // within 16 lanes
   const float sc = (m > 0.0f) ? m / 448.0f : 1.0f;
-  const uint32_t c0 = e4m3_rne(a0 / sc), c1 = e4m3_rne(a1 / sc);
-  *reinterpret_cast<uint16_t*>(q + r * cols + c) = static_cast<uint16_t>(c0 | (c1 << 8));
-  if (lane == 0) scales[blk] = sc;
+  const uint32_t lo = e4m3x4(a[0] / sc, a[1] / sc, a[2] / sc, a[3] / sc);
+  const uint32_t hi = e4m3x4(a[4] / sc, a[5] / sc, a[6] / sc, a[7] / sc);
+  if (!live) return;
+  *reinterpret_cast<uint2*>(q + at) = make_uint2(lo, hi);
+  if (g % 16 == 0) scales[blk] = sc;
 }
 
 }  // namespace
@@ -44,8 +58,8 @@ __global__ __launch_bounds__(256) void quant_e4m3_rows(
 hipError_t launch_quant_e4m3(int64_t rows, int64_t cols, int32_t dtype,
                              const void* v, uint8_t* q, float* scales,
                              hipStream_t s, Timer* tm) {
-  const int64_t blocks = rows * (cols / 128);
-  const dim3 grid(static_cast<unsigned>(ceil_div(blocks, 4)));
+  const int64_t groups = rows * (cols / 128) * 16;
+  const dim3 grid(static_cast<unsigned>(ceil_div(groups, 256)));
   if (dtype == BEAM_BF16)
     BEAM_LAUNCH(tm, "quant_e4m3", quant_e4m3_rows<true>, grid, dim3(256), 0, s, v, rows, cols, q, scales);
   else
@@ -203,14 +217,17 @@ __device__ __forceinline__ float fp8_mainloop(
 // 128 codes deep per stage, 8 waves of 128x64.  Each wave's 64 columns lie in
 // one 128-row block of weight scales: waves 0-1 hold gate channels and 2-3
 // the matching up channels of a gate/up tile (128 channels), whose up values
-// reach the gate waves through LDS for silu(g)*u.
+// reach the gate waves through LDS for silu(g)*u.  A gate/up tile holds one
+// whole 128-channel block of h for each of its rows, so it also quantises h
+// (bf16 value, then the activation recipe) and writes codes and scales.
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
     const uint8_t* __restrict__ a_src,   // gate/up: xq [T,H]; down: hq [S,I]
     const float* __restrict__ a_scale,   // gate/up: xs [T,H/128]; down: hs [S,I/128]
     const uint8_t* __restrict__ w,       // W_gu [E,2I,H] or W_d [E,H,I] codes
     const float* __restrict__ w_scale,   // [E,2I/128,H/128] or [E,H/128,I/128]
-    uint16_t* __restrict__ out,          // gate/up: h [S,I] bf16; down: y [S,H] bf16
+    void* __restrict__ out,              // gate/up: hq [S,I] codes; down: y [S,H] bf16
+    float* __restrict__ out_scale,       // gate/up: hs [S,I/128]; down: unused
     const int32_t* __restrict__ slot_token, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off,
     const int32_t* __restrict__ meta, int E, int H, int I, int n_nt) {
@@ -300,6 +317,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
       }
     }
     __syncthreads();
+    // h = bf16(silu(g) * u), written over the up value it was made from
     if (wn < 2) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -307,14 +325,35 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int rl = wm * 128 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
-          if (row0 + rl >= row_end) continue;
 #pragma unroll
           for (int n = 0; n < 2; ++n) {
-            const int ch = wn * 64 + n * 32 + lane % 32;
-            const float h = silu(acc[i][n][r]) * ex[rl * 128 + ch];
-            out[static_cast<int64_t>(row0 + rl) * I + nt * 128 + ch] = f32_to_bf16_bits(h);
+            const int at = rl * 128 + wn * 64 + n * 32 + lane % 32;
+            const float h = silu(acc[i][n][r]) * ex[at];
+            ex[at] = __uint_as_float(static_cast<uint32_t>(f32_to_bf16_bits(h)) << 16);
           }
         }
+      }
+    }
+    __syncthreads();
+    // 16 lanes per row, 8 channels each; amax over the row's 16 lanes
+    uint8_t* hq = static_cast<uint8_t*>(out);
+#pragma unroll 1
+    for (int rl = tid / 16; rl < BM; rl += kThreads / 16) {
+      const int c8 = 8 * (tid % 16);
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(&ex[rl * 128 + c8]);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(&ex[rl * 128 + c8 + 4]);
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(v0[j]), fabsf(v1[j])));
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      const float sc = (m > 0.0f) ? m / 448.0f : 1.0f;
+      const uint32_t lo = e4m3x4(v0[0] / sc, v0[1] / sc, v0[2] / sc, v0[3] / sc);
+      const uint32_t hi = e4m3x4(v1[0] / sc, v1[1] / sc, v1[2] / sc, v1[3] / sc);
+      if (row0 + rl < row_end) {
+        const int64_t row = row0 + rl;
+        *reinterpret_cast<uint2*>(hq + row * I + nt * 128 + c8) = make_uint2(lo, hi);
+        if (tid % 16 == 0) out_scale[row * (I / 128) + nt] = sc;
       }
     }
   } else {
@@ -328,7 +367,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
           const int col = nt * BN + wn * 64 + n * 32 + lane % 32;
-          if (col < H) out[static_cast<int64_t>(row) * H + col] = f32_to_bf16_bits(acc[i][n][r]);
+          if (col < H)
+            static_cast<uint16_t*>(out)[static_cast<int64_t>(row) * H + col] =
+                f32_to_bf16_bits(acc[i][n][r]);
         }
       }
     }
@@ -337,8 +378,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
 
 }  // namespace
 
-// x -> e4m3 (per token, per 128 channels); gate/up GEMM with SwiGLU -> h
-// (bf16); h -> e4m3 (per slot, per 128 channels); down GEMM -> y (bf16).
+// x -> e4m3 (per token, per 128 channels); gate/up GEMM with SwiGLU, h
+// rounded to bf16 and quantised to e4m3 (per slot, per 128 channels) in its
+// epilogue; down GEMM -> y (bf16).
 hipError_t launch_experts_fp8(const Plan& p, const void* x,
                               const uint8_t* w_gate_up, const float* s_gate_up,
                               const uint8_t* w_down, const float* s_down,
@@ -347,7 +389,6 @@ hipError_t launch_experts_fp8(const Plan& p, const void* x,
   float* xs = ws_at<float>(ws, p.off_xs);
   uint8_t* hq = ws_at<uint8_t>(ws, p.off_hq);
   float* hs = ws_at<float>(ws, p.off_hs);
-  uint16_t* h = ws_at<uint16_t>(ws, p.off_h);
   uint16_t* y = ws_at<uint16_t>(ws, p.off_y);
   const int32_t* slot_token = ws_at<int32_t>(ws, p.off_slot_token);
   const int32_t* counts = ws_at<int32_t>(ws, p.off_counts);
@@ -359,12 +400,10 @@ hipError_t launch_experts_fp8(const Plan& p, const void* x,
   const int nt_gu = p.I / 128;
   const int nt_dn = static_cast<int>(ceil_div(p.H, BN));
   BEAM_LAUNCH(tm, "gate_up_fp8", grouped_gemm_fp8<kGateUp>, grid_for(p, nt_gu),
-              dim3(kThreads), 0, s, xq, xs, w_gate_up, s_gate_up, h, slot_token,
+              dim3(kThreads), 0, s, xq, xs, w_gate_up, s_gate_up, hq, hs, slot_token,
               counts, offsets, toff, meta, p.E, p.H, p.I, nt_gu);
-  e = launch_quant_e4m3(p.S, p.I, BEAM_BF16, h, hq, hs, s, tm);
-  if (e != hipSuccess) return e;
   BEAM_LAUNCH(tm, "down_fp8", grouped_gemm_fp8<kDown>, grid_for(p, nt_dn),
-              dim3(kThreads), 0, s, hq, hs, w_down, s_down, y, slot_token,
+              dim3(kThreads), 0, s, hq, hs, w_down, s_down, y, nullptr, slot_token,
               counts, offsets, toff, meta, p.E, p.H, p.I, nt_dn);
   return hipGetLastError();
 }

@@ -66,7 +66,7 @@ struct Coords {
 // Returns false for workgroups past the last logical tile.
 __device__ __forceinline__ bool tile_coords(const int32_t* counts, const int32_t* offsets,
                                             const int32_t* tile_off, const int32_t* meta,
-                                            int E, int n_nt, Coords& c) {
+                                            int E, int n_nt, Coords& c, int bm = BM) {
   const int n_log = meta[kMetaTiles] * n_nt;
   const int per_xcd = (n_log + kXcds - 1) / kXcds;
   const int local = blockIdx.x / kXcds;
@@ -80,7 +80,7 @@ __device__ __forceinline__ bool tile_coords(const int32_t* counts, const int32_t
   const int jj = j - g * kGroupM * n_nt;
   c.e = e;
   c.nt = jj / gm;
-  c.row0 = offsets[e] + (g * kGroupM + jj % gm) * BM;
+  c.row0 = offsets[e] + (g * kGroupM + jj % gm) * bm;
   c.row_end = offsets[e] + counts[e];
   return true;
 }

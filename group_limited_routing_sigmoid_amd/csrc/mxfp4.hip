@@ -32,7 +32,8 @@ __device__ __forceinline__ int mx8_exponent(float amax) {
 }
 
 // One thread per 32-value block of a row: E4M3 codes of v * 2^-x (exact
-// scaling, round to nearest even, saturating) and the E8M0 code x + 127.
+// scaling, round to nearest even; |v * 2^-x| <= 448 by the choice of x) and
+// the E8M0 code x + 127.
 template <bool BF16>
 __global__ __launch_bounds__(256) void quant_mxfp8_rows(
     const void* __restrict__ v, int64_t rows, int64_t cols, uint8_t* __restrict__ q,
@@ -67,10 +68,8 @@ __global__ __launch_bounds__(256) void quant_mxfp8_rows(
   u32x4 out[2];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) word |= e4m3_rne(ldexpf(a[4 * i + j], -x)) << (8 * j);
-    out[i / 4][i % 4] = word;
+    out[i / 4][i % 4] = e4m3x4(ldexpf(a[4 * i], -x), ldexpf(a[4 * i + 1], -x),
+                               ldexpf(a[4 * i + 2], -x), ldexpf(a[4 * i + 3], -x));
   }
   st16(q + at, out[0]);
   st16(q + at + 16, out[1]);
@@ -268,7 +267,8 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
     const uint8_t* __restrict__ xs,      // their E8M0 bytes [rows, K/32]
     const uint8_t* __restrict__ w,       // W_gu [E,2I,H/2] or W_d [E,H,I/2] (E2M1 pairs)
     const uint8_t* __restrict__ ws,      // [E,2I,H/32] or [E,H,I/32]
-    float* __restrict__ out,             // gate/up: h [S,I]; down: y [S,H]  (fp32)
+    void* __restrict__ out,              // gate/up: hq [S,I] (E4M3); down: y [S,H] (fp32)
+    uint8_t* __restrict__ out_scale,     // gate/up: hs [S,I/32] (E8M0); down: unused
     const int32_t* __restrict__ slot_token, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off,
     const int32_t* __restrict__ meta, int E, int H, int I, int n_nt) {
@@ -348,28 +348,45 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
   }
   // element q of acc[f][j]: channel row 8*(q/4) + 4*half + q%4 of fragment f,
   // slot row0 + wm*128 + 32 j + r; elements 4g .. 4g+3 are 4 consecutive
-  // channels of the lane's slot, stored as one 16-byte vector
+  // channels of the lane's slot.  A gate/up wave's 32 channels are one MXFP8
+  // block of h, split over lanes r and r + 32: h is quantised here (fp32
+  // value, block exponent from the amax over both lanes) and only its codes
+  // and E8M0 byte are written.
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     if (j >= nj) continue;
     const int slot = row0 + wm * 128 + j * 32 + r;
-    if (slot >= row_end) continue;
+    if (MODE == kGateUp) {
+      float hv[16];
+      float m = 0.0f;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int cr = 8 * g + 4 * half;
-      if (MODE == kGateUp) {
-        f32x4 v;
+      for (int q = 0; q < 16; ++q) {
+        hv[q] = silu(acc[0][j][q]) * acc[1][j][q];
+        m = fmaxf(m, fabsf(hv[q]));
+      }
+      m = fmaxf(m, __shfl_xor(m, 32));
+      const int x = mx8_exponent(m);
+      if (slot >= row_end) continue;
+      uint8_t* hq = static_cast<uint8_t*>(out) + static_cast<int64_t>(slot) * I + nt * 128 + wn * 32;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) v[t] = silu(acc[0][j][4 * g + t]) * acc[1][j][4 * g + t];
-        *reinterpret_cast<f32x4*>(out + static_cast<int64_t>(slot) * I + nt * 128 + wn * 32 + cr) = v;
-      } else {
+      for (int g = 0; g < 4; ++g) {
+        *reinterpret_cast<uint32_t*>(hq + 8 * g + 4 * half) =
+            e4m3x4(ldexpf(hv[4 * g], -x), ldexpf(hv[4 * g + 1], -x), ldexpf(hv[4 * g + 2], -x),
+                   ldexpf(hv[4 * g + 3], -x));
+      }
+      if (half == 0) out_scale[static_cast<int64_t>(slot) * (I / 32) + nt * 4 + wn] = static_cast<uint8_t>(x + 127);
+    } else {
+      if (slot >= row_end) continue;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int cr = 8 * g + 4 * half;
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
           const int col = nt * BN + wn * 64 + f * 32 + cr;  // H % 128 == 0: all 4 or none
           if (col < H) {
             const f32x4 v = {acc[f][j][4 * g], acc[f][j][4 * g + 1], acc[f][j][4 * g + 2],
                              acc[f][j][4 * g + 3]};
-            *reinterpret_cast<f32x4*>(out + static_cast<int64_t>(slot) * H + col) = v;
+            *reinterpret_cast<f32x4*>(static_cast<float*>(out) + static_cast<int64_t>(slot) * H + col) = v;
           }
         }
       }
@@ -392,6 +409,8 @@ hipError_t launch_quant_mxfp8(int64_t rows, int64_t cols, int32_t dtype, const v
 }
 
 // x -> MXFP8; gate/up with SwiGLU -> h (fp32); h -> MXFP8; down -> y (fp32).
+// The grouped gate/up GEMM quantises h in its epilogue; the streaming one
+// writes fp32 h for the separate quantiser.
 hipError_t launch_experts_mxfp4(const Plan& p, const void* x, const uint8_t* w_gate_up,
                                 const uint8_t* s_gate_up, const uint8_t* w_down,
                                 const uint8_t* s_down, void* ws, hipStream_t s, Timer* tm) {
@@ -415,12 +434,10 @@ hipError_t launch_experts_mxfp4(const Plan& p, const void* x, const uint8_t* w_g
     const int nt_dn = static_cast<int>(ceil_div(p.H, tile::BN));
     BEAM_LAUNCH(tm, "grouped_gate_up_mx", mxg::grouped_gemm_mx<mxg::kGateUp>,
                 tile::grid_for(p, nt_gu), dim3(tile::kThreads), 0, s, xq, xs, w_gate_up,
-                s_gate_up, h, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_gu);
-    e = launch_quant_mxfp8(p.S, p.I, BEAM_F32, h, hq, hs, s, tm);
-    if (e != hipSuccess) return e;
+                s_gate_up, hq, hs, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_gu);
     BEAM_LAUNCH(tm, "grouped_down_mx", mxg::grouped_gemm_mx<mxg::kDown>,
                 tile::grid_for(p, nt_dn), dim3(tile::kThreads), 0, s, hq, hs, w_down, s_down,
-                y, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_dn);
+                y, nullptr, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_dn);
     return hipGetLastError();
   }
   BEAM_LAUNCH(tm, "stream_gate_up_mx", stream_gate_up_mx,

@@ -166,7 +166,7 @@ hipError_t launch_permute(const Plan& p, const int32_t* idx, int32_t* counts,
   BEAM_LAUNCH(tm, "perm_rank", perm_rank, dim3(nb), dim3(kPermBlock), 0, s, idx, p.T,
                      p.K, p.E, hist, rank);
   BEAM_LAUNCH(tm, "perm_scan", perm_scan, dim3(1), dim3(kMaxE), 0, s, hist, p.nb, p.E,
-                     kGemmBM, base, counts, offsets,
+                     p.bm, base, counts, offsets,
                      ws_at<int32_t>(ws, p.off_tile_expert),
                      ws_at<int32_t>(ws, p.off_tile_row0),
                      ws_at<int32_t>(ws, p.off_meta),

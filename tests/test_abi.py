@@ -38,6 +38,8 @@ def test_validate_accepts_layer_shapes():
     assert gl.validate(gl.make_desc(TINY, gl.F32, gl.F32), 16) == gl.OK
     assert gl.validate(_desc(weight_dtype=gl.FP8_E4M3), 8192) == gl.OK
     assert gl.validate(_desc(), 0) == gl.OK
+    assert gl.validate(_desc(flags=gl.PATH_GROUPED | gl.TILE_128), 64) == gl.OK
+    assert gl.validate(_desc(flags=gl.TILE_256), 64) == gl.OK
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -59,6 +61,7 @@ def test_validate_accepts_layer_shapes():
     ("weight_dtype", 9, gl.ERR_INVALID_ARG),
     ("flags", 1 << 9, gl.ERR_INVALID_ARG),
     ("flags", gl.PATH_STREAM | gl.PATH_GROUPED, gl.ERR_INVALID_ARG),
+    ("flags", gl.TILE_128 | gl.TILE_256, gl.ERR_INVALID_ARG),
 ])
 def test_validate_rejects(field, value, status):
     assert gl.validate(_desc(**{field: value}), 64) == status

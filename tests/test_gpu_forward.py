@@ -60,16 +60,34 @@ def test_small_bf16_both_paths(T, path):
 
 def test_small_bf16_skewed_long_chunks():
     # hot experts with hundreds of tokens: several 16-token chunks on the
-    # streaming path and several 128-row tiles on the grouped path
+    # streaming path and several M tiles of either height on the grouped path
     sh = small_shape()
     w = WORKLOADS["prefill16k_skew"]
     inp = make_inputs(w, device=device(), tokens=700, shape=sh, seed=77)
-    for path in (gl.PATH_STREAM, gl.PATH_GROUPED):
+    for path in (gl.PATH_STREAM, gl.PATH_GROUPED | gl.TILE_128,
+                 gl.PATH_GROUPED | gl.TILE_256):
         _check(inp, sh, desc_for(w, sh, path), np.arange(0, 700, 3), BF16_TOL,
                f"small skew path={path}")
 
 
-@pytest.mark.parametrize("path", [gl.PATH_STREAM, gl.PATH_GROUPED])
+@pytest.mark.parametrize("T", [1, 37, 700, 2100])
+def test_tile_heights_bitwise_equal(T):
+    # 128- and 256-row tiles add the same products in the same order: equal
+    # bits, including tails of 1..255 rows and experts with many tiles
+    sh = small_shape()
+    w = WORKLOADS["prefill16k_skew"]
+    inp = make_inputs(w, device=device(), tokens=T, shape=sh, seed=500 + T)
+    outs = []
+    for tile in (gl.TILE_128, gl.TILE_256):
+        d = desc_for(w, sh, gl.PATH_GROUPED | tile)
+        outs.append(gl.forward(d, inp.x, inp.w_router, inp.bias, inp.w_gate_up,
+                               inp.w_down))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("path", [gl.PATH_STREAM, gl.PATH_GROUPED | gl.TILE_128,
+                                  gl.PATH_GROUPED | gl.TILE_256])
 def test_odd_widths_skewed(path):
     # hidden and intermediate multiples of 128 but not of 256: the last
     # 256-wide down tile of the grouped path is half outside H
@@ -90,6 +108,7 @@ def test_beam_decode64(path):
 
 @pytest.mark.parametrize("name", ["prefill4k", "prefill16k_skew", "ep8_share16k"])
 def test_beam_prefill_sampled(name):
+    # in the launch configuration the bench times (default tile choice)
     w = WORKLOADS[name]
     inp = inputs(name)
     T = inp.x.shape[0]

@@ -88,24 +88,28 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
     p->stream_path = 2 * p->S < static_cast<int64_t>(p->E);
   // streaming kernels exist for bf16 weights only
   if (p->wdt != BEAM_BF16) p->stream_path = false;
-  // 4-bit MX weights: the grouped tiles win from 2 tokens per expert on
-  // (measured T = 64: 1.56 ms vs 1.60 ms streaming), the streaming kernels
-  // below that
-  if (p->wdt == BEAM_MXFP4) {
-    if (p->flags & BEAM_PATH_STREAM) p->stream_path = true;
-    else if (p->flags & BEAM_PATH_GROUPED) p->stream_path = false;
-    else p->stream_path = p->S < 2 * static_cast<int64_t>(p->E);
-  }
+  // 4-bit MX weights: the grouped tiles with their copy rings are ahead at
+  // every batch measured (T = 1: 0.189 vs 0.215 ms streaming, T = 8: 0.437
+  // vs 0.500, T = 64: 1.25 vs 1.60); the streaming kernels run when asked for
+  if (p->wdt == BEAM_MXFP4) p->stream_path = (p->flags & BEAM_PATH_STREAM) != 0;
   const int64_t S = p->S, E = p->E, H = p->H, I = p->I;
-  // bf16 grouped tiles: 128 rows (two copy stages in flight) while the
-  // experts average fewer than 128 rows, 256 rows from there on (measured,
-  // Beam layer: 128-row tiles 12% faster at 1K and 2K tokens, equal at 4K,
-  // 10% slower at 6K)
+  // Grouped tiles of 128 (or, bf16, 160) rows with a deeper copy ring while
+  // the experts hold few rows, 256 rows above; measured on the Beam layer.
+  // bf16, 128 / 160 / 256 rows: 3.93 / 3.94 / 4.46 ms at 2K tokens, 4.20 /
+  // 4.18 / 4.82 at 3K, 5.30 / 4.72 / 5.00 at 4K, 6.27 / 6.06 / 5.42 at 5K;
+  // so 128 below T*K = 96E, 160 below 144E.  MXFP4, 128 / 256 rows: 1.57 /
+  // 1.61 ms at 1K tokens, 2.77 / 2.38 at 4K; so 128 below T*K = 32E.
   p->bm = kGemmBM;
   if (p->wdt == BEAM_BF16) {
     if (p->flags & BEAM_TILE_128) p->bm = 128;
+    else if (p->flags & BEAM_TILE_160) p->bm = 160;
     else if (p->flags & BEAM_TILE_256) p->bm = kGemmBM;
-    else if (S < 128 * E) p->bm = 128;
+    else if (S < 96 * E) p->bm = 128;
+    else if (S < 144 * E) p->bm = 160;
+  } else if (p->wdt == BEAM_MXFP4) {
+    if (p->flags & BEAM_TILE_128) p->bm = 128;
+    else if (p->flags & (BEAM_TILE_160 | BEAM_TILE_256)) p->bm = kGemmBM;
+    else if (S < 32 * E) p->bm = 128;
   }
   p->max_tiles = S / p->bm + (S < E ? S : E) + 1;
   const bool f32 = p->wdt == BEAM_F32;
@@ -172,10 +176,11 @@ const char* beam_status_string(int status) {
 
 int beam_moe_validate(const beam_moe_desc* d, int64_t T) {
   if (!d || T < 0) return BEAM_ERR_INVALID_ARG;
-  const uint32_t known = BEAM_ROUTE_LOGITS_IN | BEAM_PATH_STREAM | BEAM_PATH_GROUPED |
-                         BEAM_TILE_128 | BEAM_TILE_256;
+  const uint32_t tiles = BEAM_TILE_128 | BEAM_TILE_160 | BEAM_TILE_256;
+  const uint32_t known = BEAM_ROUTE_LOGITS_IN | BEAM_PATH_STREAM | BEAM_PATH_GROUPED | tiles;
   if (d->flags & ~known) return BEAM_ERR_INVALID_ARG;
-  if ((d->flags & BEAM_TILE_128) && (d->flags & BEAM_TILE_256)) return BEAM_ERR_INVALID_ARG;
+  const uint32_t tf = d->flags & tiles;
+  if (tf & (tf - 1)) return BEAM_ERR_INVALID_ARG;  // at most one tile height
   if ((d->flags & BEAM_PATH_STREAM) && (d->flags & BEAM_PATH_GROUPED))
     return BEAM_ERR_INVALID_ARG;
   if (d->act_dtype != BEAM_F32 && d->act_dtype != BEAM_BF16) return BEAM_ERR_INVALID_ARG;

@@ -207,17 +207,19 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(
   }
 }
 
-// ---- 128-row tiles with a ring of three copy stages -------------------------
+// ---- 128- and 160-row tiles with a ring of three copy stages ----------------
 // For batches whose experts hold few rows the products are bound by the
 // weight bytes, and the 256-row tile's single stage in flight leaves HBM
-// under-used.  This form takes 128 x 256 tiles with three 48 KiB stages (two
-// in flight while one is consumed; 144 KiB of LDS).  (A 64-row form with four
-// 40 KiB stages measured no faster.)  A wave copies the same
-// c = 4 + n_a regions every stage (n_a: its A regions, 8 rows each, that hold
-// a valid row; rows past the last valid one inside such a region copy a
-// valid row), so "stage s has landed" is a count of the wave's outstanding
-// vector-memory operations: c times the stages issued after s.  8 waves:
-// 2 along M (BMS/2 rows each) x 4 along N, B rows as in the 256-row form.
+// under-used.  These forms take 128 x 256 or 160 x 256 tiles with three 48 /
+// 52 KiB stages (two in flight while one is consumed; 144 / 156 KiB of LDS).
+// (A 64-row form with four 40 KiB stages measured no faster.)  A wave copies
+// the same c = 4 + n_a regions every stage (n_a: its A regions, 8 rows each,
+// that hold a valid row; rows past the last valid one inside such a region
+// copy a valid row), so "stage s has landed" is a count of the wave's
+// outstanding vector-memory operations: c times the stages issued after s
+// (tile::ring_barrier).  8 waves:
+// 2 along M (64 + 64 or 96 + 64 rows) x 4 along N, B rows as in the 256-row
+// form.
 namespace small {
 
 template <int BMS>
@@ -225,26 +227,15 @@ struct Geo {
   static constexpr int kABytes = BMS * kRowBytes;
   static constexpr int kStage = kABytes + kTileBytes;
   static constexpr int kStages = 3;
-  static constexpr int kALoads = kABytes / (16 * kThreads);     // 2
+  static constexpr int kRegions = BMS / 8;                     // 8-row A regions
+  static constexpr int kALoads = (kRegions + 7) / 8;            // per wave: 2 or 3
   static constexpr int kBLoads = kTileBytes / (16 * kThreads);  // 4
-  static constexpr int kWaveRows = BMS / 2;
-  static constexpr int kFrags = kWaveRows / 32;                 // 2
+  // rows of the waves with wm = 0 (the rest belong to wm = 1); a SIMD holds
+  // one wave of each, so 160 rows split 96 + 64 still balance per SIMD
+  static constexpr int kWaveRows = (BMS == 160) ? 96 : BMS / 2;
+  static constexpr int kFrags = kWaveRows / 32;                 // wm = 0: 2 or 3
+  static constexpr int kFrags1 = (BMS - kWaveRows) / 32;        // wm = 1: 2
 };
-
-// Wait until at most n of this wave's vector-memory operations are
-// outstanding and its LDS reads are done, then meet every wave.  n is
-// wave-uniform; any count not listed waits for all (always safe).
-#define BEAM_RING_BARRIER(n) \
-  asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
-__device__ __forceinline__ void ring_barrier(int n) {
-  switch (n) {
-    case 4: BEAM_RING_BARRIER(4); break;
-    case 5: BEAM_RING_BARRIER(5); break;
-    case 6: BEAM_RING_BARRIER(6); break;
-    default: BEAM_RING_BARRIER(0); break;
-  }
-}
-#undef BEAM_RING_BARRIER
 
 template <int BMS, int NF>
 __device__ __forceinline__ void ring_mainloop(
@@ -339,7 +330,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_small(
 #pragma unroll
   for (int i = 0; i < G::kALoads; ++i) {
     const int r = dma_row(wave, lane, i);
-    a_ok[i] = 8 * (uwave + 8 * i) < m_valid;  // the region's first row is valid
+    // the region exists and its first row is valid
+    a_ok[i] = uwave + 8 * i < G::kRegions && 8 * (uwave + 8 * i) < m_valid;
     c += a_ok[i];
     const int slot = min(row0 + r, row_end - 1);  // padding rows: a valid row
     a_off[i] = ((MODE == kGateUp) ? static_cast<uint32_t>(slot_token[slot]) * H
@@ -365,9 +357,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16_small(
   for (int i = 0; i < G::kFrags; ++i)
 #pragma unroll
     for (int n = 0; n < 2; ++n) acc[i][n] = f32x16{};
-  const int nf = min(G::kFrags, max(0, (m_valid - wm * G::kWaveRows + 31) / 32));
-  if (G::kFrags == 2 && nf == 2)
-    ring_mainloop<BMS, G::kFrags>(a_src, a_off, a_ok, c, wbase, b_off, K / BK, ring, acc, arow, brow);
+  const int nf = min(wm == 0 ? G::kFrags : G::kFrags1,
+                     max(0, (m_valid - wm * G::kWaveRows + 31) / 32));
+  if (G::kFrags == 3 && nf == 3)
+    ring_mainloop<BMS, 3>(a_src, a_off, a_ok, c, wbase, b_off, K / BK, ring, acc, arow, brow);
+  else if (nf >= 2)
+    ring_mainloop<BMS, 2>(a_src, a_off, a_ok, c, wbase, b_off, K / BK, ring, acc, arow, brow);
   else if (nf >= 1)
     ring_mainloop<BMS, 1>(a_src, a_off, a_ok, c, wbase, b_off, K / BK, ring, acc, arow, brow);
   else
@@ -487,6 +482,7 @@ hipError_t launch_grouped_bf16(const Plan& p, const void* x,
               meta, p.E, p.H, p.I, nt_dn);                                                    \
   return hipGetLastError()
   if (p.bm == 128) { BEAM_SMALL_TILES(128); }
+  if (p.bm == 160) { BEAM_SMALL_TILES(160); }
 #undef BEAM_SMALL_TILES
   BEAM_LAUNCH(tm, "grouped_gate_up_bf16", grouped_gemm_bf16<kGateUp>, grid_for(p, nt_gu),
               dim3(kThreads), 0, s, static_cast<const uint16_t*>(x),

@@ -91,6 +91,35 @@ __device__ __forceinline__ int wave_frags(int m_valid, int wm) {
   return min(4, max(0, (m_valid - wm * 128 + 31) / 32));
 }
 
+// Copy rings: wait until at most n (0..15, wave-uniform) of this wave's
+// vector-memory operations are outstanding and its LDS reads are done, then
+// meet every wave.  Loads complete in issue order, so after a wave has issued
+// the copies of the stages after s, "stage s has landed" is n = the number of
+// those later copies.  Any other n waits for all (always safe).
+#define BEAM_RING_BARRIER(n) \
+  asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
+__device__ __forceinline__ void ring_barrier(int n) {
+  switch (n) {
+    case 1: BEAM_RING_BARRIER(1); break;
+    case 2: BEAM_RING_BARRIER(2); break;
+    case 3: BEAM_RING_BARRIER(3); break;
+    case 4: BEAM_RING_BARRIER(4); break;
+    case 5: BEAM_RING_BARRIER(5); break;
+    case 6: BEAM_RING_BARRIER(6); break;
+    case 7: BEAM_RING_BARRIER(7); break;
+    case 8: BEAM_RING_BARRIER(8); break;
+    case 9: BEAM_RING_BARRIER(9); break;
+    case 10: BEAM_RING_BARRIER(10); break;
+    case 11: BEAM_RING_BARRIER(11); break;
+    case 12: BEAM_RING_BARRIER(12); break;
+    case 13: BEAM_RING_BARRIER(13); break;
+    case 14: BEAM_RING_BARRIER(14); break;
+    case 15: BEAM_RING_BARRIER(15); break;
+    default: BEAM_RING_BARRIER(0); break;
+  }
+}
+#undef BEAM_RING_BARRIER
+
 // Grid of a grouped launch: an upper bound on the logical tiles, rounded to
 // whole XCD rounds.
 inline dim3 grid_for(const Plan& p, int n_nt) {

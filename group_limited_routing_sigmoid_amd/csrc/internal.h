@@ -11,7 +11,7 @@
 namespace beam {
 
 // Grouped-GEMM row tile: rows (slots) per M tile of one expert (the bf16
-// kernels also have a 128-row form).
+// kernels also have 128- and 160-row forms, the MXFP4 kernels a 128-row form).
 constexpr int kGemmBM = 256;
 // Tokens routed per workgroup by the permutation kernels.
 constexpr int kPermBlock = 256;
@@ -26,7 +26,7 @@ struct Plan {
   int32_t ks;          // partial logits the router selection sums
   bool router_gemm;    // logits by the dense tile GEMM (many tokens)
   bool stream_path;    // weight-streaming experts (few tokens per expert)
-  int32_t bm;          // rows per grouped-GEMM M tile: 256, or 128 (bf16 only)
+  int32_t bm;          // rows per grouped-GEMM M tile: 256, 160 (bf16), 128 (bf16, MXFP4)
   int64_t max_tiles;   // upper bound on grouped-GEMM M tiles
   // byte offsets into the workspace
   size_t off_part, off_idx, off_w, off_hist, off_base, off_rank, off_counts,

@@ -208,23 +208,33 @@ __global__ __launch_bounds__(kThreads) void stream_down_mx(
   }
 }
 
-// ---- grouped E2M1 x E4M3 GEMM for prefill-sized batches -------------------
-// Same work list and XCD order as the bf16 grouped GEMM (256-slot M tiles x
-// 256-row N tiles), 128 k per stage, two stages copied straight into LDS:
-// activation tile (E4M3, 256 slots x 128 bytes, the bf16 tiles' layout and
-// swizzle), weight tile (E2M1, 256 rows x 64 bytes), and both tiles' E8M0
-// bytes (4 per row per stage).  The weights are the MFMA A side, the slots
-// the B side, so a wave's accumulators are channels x slots; a wave owns 32
-// channels x 128 slots twice (gate and the matching up channels for gate/up,
-// 64 consecutive output columns for down).
+// ---- grouped E2M1 x E4M3 GEMM -----------------------------------------------
+// Same work list and XCD order as the bf16 grouped GEMM (M tiles of BMS = 256
+// or 128 slots x 256-row N tiles), 128 k per stage, stages copied straight
+// into LDS: activation tile (E4M3, BMS slots x 128 bytes, the bf16 tiles'
+// layout and swizzle), weight tile (E2M1, 256 rows x 64 bytes), and both
+// tiles' E8M0 bytes (4 per row per stage).  The stages form a ring (2 or 3
+// of 50 KiB for 256 slots, 4 of 33.5 KiB for 128): the copies of all but the
+// stage being consumed are in flight, and a wave copies the same number of
+// regions every stage, so each wait is a count of its outstanding copies
+// (tile::ring_barrier).  The weights are the MFMA A side, the slots the B
+// side, so a wave's accumulators are channels x slots; a wave owns 32
+// channels x BMS/2 slots twice (gate and the matching up channels for
+// gate/up, 64 consecutive output columns for down).
 namespace mxg {
 
 using namespace tile;
 
-constexpr int kXBytes = BM * 128;            // activation tile per stage
-constexpr int kWBytes = BN * 64;             // weight tile per stage
-constexpr int kStage = kXBytes + kWBytes + 2 * BM * 4;
-typedef unsigned char Lds[2][kStage];
+template <int BMS, int STAGES>
+struct Geo {
+  static constexpr int kXBytes = BMS * 128;  // activation tile per stage
+  static constexpr int kWBytes = BN * 64;    // weight tile per stage
+  static constexpr int kStage = kXBytes + kWBytes + (BMS + BN) * 4;
+  static constexpr int kStages = STAGES;
+  static constexpr int kXLoads = kXBytes / (16 * tile::kThreads);  // 4 or 2
+  static constexpr int kXsWaves = BMS / 64;  // waves copying activation scale words
+  static constexpr int kJ = BMS / 64;        // 32-slot fragments per wave
+};
 
 __device__ __forceinline__ int wswz(int row, int chunk) {  // 64-byte weight rows
   return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
@@ -232,13 +242,15 @@ __device__ __forceinline__ int wswz(int row, int chunk) {  // 64-byte weight row
 
 enum Mode { kGateUp = 0, kDown = 1 };
 
-template <int NJ, int MODE>
-__device__ __forceinline__ void stage_products(const unsigned char* st, f32x16 (&acc)[2][4],
+template <int BMS, int NJ>
+__device__ __forceinline__ void stage_products(const unsigned char* st,
+                                               f32x16 (&acc)[2][BMS / 64],
                                                const int* wrow, const int* srow, int half) {
+  using G = Geo<BMS, 2>;
   const unsigned char* X = st;
-  const unsigned char* W = st + kXBytes;
-  const uint32_t* XS = reinterpret_cast<const uint32_t*>(st + kXBytes + kWBytes);
-  const uint32_t* WS = XS + BM;
+  const unsigned char* W = st + G::kXBytes;
+  const uint32_t* XS = reinterpret_cast<const uint32_t*>(st + G::kXBytes + G::kWBytes);
+  const uint32_t* WS = XS + BMS;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     u32x4 a[2];
@@ -261,7 +273,7 @@ __device__ __forceinline__ void stage_products(const unsigned char* st, f32x16 (
   }
 }
 
-template <int MODE>
+template <int BMS, int STAGES, int MODE>
 __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
     const uint8_t* __restrict__ xq,      // gate/up: xq [T,H]; down: hq [S,I]  (E4M3)
     const uint8_t* __restrict__ xs,      // their E8M0 bytes [rows, K/32]
@@ -272,15 +284,18 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
     const int32_t* __restrict__ slot_token, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off,
     const int32_t* __restrict__ meta, int E, int H, int I, int n_nt) {
-  __shared__ __attribute__((aligned(16))) Lds lds;
+  using G = Geo<BMS, STAGES>;
+  constexpr int S = G::kStages, P = S - 1;  // ring size, stages in flight
+  __shared__ __attribute__((aligned(16))) unsigned char lds[S][G::kStage];
   Coords tc;
-  if (!tile_coords(counts, offsets, tile_off, meta, E, n_nt, tc)) return;
+  if (!tile_coords(counts, offsets, tile_off, meta, E, n_nt, tc, BMS)) return;
   const int e = tc.e, nt = tc.nt, row0 = tc.row0, row_end = tc.row_end;
   const int K = (MODE == kGateUp) ? H : I;
-  const int nkb = K / 128;
+  const int nk = K / 128;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int uwave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy
   const int wm = wave / 4, wn = wave % 4, r = lane % 32, half = lane / 32;
-  const int m_valid = min(BM, row_end - row0);
+  const int m_valid = min(BMS, row_end - row0);
   const int64_t nrows = (MODE == kGateUp) ? 2 * I : H;
   const uint8_t* wb = w + static_cast<int64_t>(e) * nrows * (K / 2);
   const uint8_t* wsb = ws + static_cast<int64_t>(e) * nrows * (K / 32);
@@ -292,70 +307,83 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
     const int slot = min(row0 + t, row_end - 1);
     return (MODE == kGateUp) ? slot_token[slot] : slot;
   };
-  // copy sources: activations 4 x 1 KiB regions per wave (8 rows of 128 B),
-  // weights 2 x 1 KiB (16 rows of 64 B); scale bytes: waves 0-3 the
-  // activation rows 64 w + lane, waves 4-7 the weight rows 64 (w-4) + lane
-  uint32_t x_off[kLoads], w_off[2];
+  // copy sources: activations kXLoads x 1 KiB regions per wave (8 rows of
+  // 128 B; regions whose first row is padding are not copied), weights
+  // 2 x 1 KiB (16 rows of 64 B); scale words: waves 0 .. kXsWaves-1 the
+  // activation rows 64 w + lane, the next 4 waves the weight rows
+  uint32_t x_off[G::kXLoads], w_off[2];
+  bool x_ok[G::kXLoads];
+  int c = 2;  // this wave's copies per stage
 #pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
+  for (int i = 0; i < G::kXLoads; ++i) {
     const int t = dma_row(wave, lane, i);
+    x_ok[i] = 8 * (uwave + 8 * i) < m_valid;
+    c += x_ok[i];
     x_off[i] = static_cast<uint32_t>(slot_src(t)) * K + dma_chunk(t, lane) * 16;
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int t = 16 * (wave + 8 * i) + lane / 4;
-    const int c = (lane % 4) ^ ((t >> 2) & 3);
-    w_off[i] = static_cast<uint32_t>(wrow_of(t)) * (K / 2) + c * 16;
+    const int ch = (lane % 4) ^ ((t >> 2) & 3);
+    w_off[i] = static_cast<uint32_t>(wrow_of(t)) * (K / 2) + ch * 16;
   }
-  const uint8_t* s_src = (wave < 4)
-      ? xs + static_cast<int64_t>(slot_src(64 * wave + lane)) * (K / 32)
-      : wsb + static_cast<int64_t>(wrow_of(64 * (wave - 4) + lane)) * (K / 32);
-  const int s_dst = kXBytes + kWBytes + ((wave < 4) ? 0 : BM * 4) + 256 * (wave % 4);
-  auto dma = [&](int buf, int kb) {
+  const bool s_x = uwave < G::kXsWaves, s_any = uwave < G::kXsWaves + 4;
+  c += s_any;
+  const uint8_t* s_src = s_x ? xs + static_cast<int64_t>(slot_src(64 * wave + lane)) * (K / 32)
+                             : wsb + static_cast<int64_t>(wrow_of(64 * ((s_any ? wave : G::kXsWaves) - G::kXsWaves) + lane)) * (K / 32);
+  const int s_dst = G::kXBytes + G::kWBytes +
+                    (s_x ? 256 * wave : BMS * 4 + 256 * ((s_any ? wave : G::kXsWaves) - G::kXsWaves));
+  auto dma = [&](int st, int kb) {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i)
-      dma16(xq + (x_off[i] + kb * 128), &lds[buf][dma_row(wave, 0, i) * 128]);
+    for (int i = 0; i < G::kXLoads; ++i)
+      if (x_ok[i]) dma16(xq + (x_off[i] + kb * 128), &lds[st][dma_row(wave, 0, i) * 128]);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(wb + (w_off[i] + kb * 64), &lds[buf][kXBytes + (wave + 8 * i) * 1024]);
-    dma4(s_src + kb * 4, &lds[buf][s_dst]);
+    for (int i = 0; i < 2; ++i)
+      dma16(wb + (w_off[i] + kb * 64), &lds[st][G::kXBytes + (wave + 8 * i) * 1024]);
+    if (s_any) dma4(s_src + kb * 4, &lds[st][s_dst]);
   };
   // fragment rows: weights (A) and slots (B)
-  int wrow[2], srow[4];
+  int wrow[2], srow[G::kJ];
 #pragma unroll
   for (int f = 0; f < 2; ++f)
     wrow[f] = (MODE == kGateUp) ? (f * 128 + wn * 32 + r) : (wn * 64 + f * 32 + r);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) srow[j] = wm * 128 + j * 32 + r;
-  f32x16 acc[2][4];
+  for (int j = 0; j < G::kJ; ++j) srow[j] = wm * (BMS / 2) + j * 32 + r;
+  f32x16 acc[2][G::kJ];
 #pragma unroll
   for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[f][j] = f32x16{};
-  const int nj = wave_frags(m_valid, wm);
-  dma(0, 0);
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nkb) dma(buf ^ 1, kb + 1);
+    for (int j = 0; j < G::kJ; ++j) acc[f][j] = f32x16{};
+  const int nj = min(G::kJ, max(0, (m_valid - wm * (BMS / 2) + 31) / 32));
+#pragma unroll
+  for (int s0 = 0; s0 < P; ++s0)
+    if (s0 < nk) dma(s0, s0);
+  ring_barrier(c * (min(P, nk) - 1));  // stage 0 landed
+  int st = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt+P goes to the buffer last read in step kt-1 (ended by a barrier)
+    const int kn = kt + P;
+    if (kn < nk) dma(st == 0 ? S - 1 : st - 1, kn);
     switch (nj) {
-      case 4: stage_products<4, MODE>(&lds[buf][0], acc, wrow, srow, half); break;
-      case 3: stage_products<3, MODE>(&lds[buf][0], acc, wrow, srow, half); break;
-      case 2: stage_products<2, MODE>(&lds[buf][0], acc, wrow, srow, half); break;
-      case 1: stage_products<1, MODE>(&lds[buf][0], acc, wrow, srow, half); break;
+      case 4: stage_products<BMS, (G::kJ >= 4 ? 4 : G::kJ)>(&lds[st][0], acc, wrow, srow, half); break;
+      case 3: stage_products<BMS, (G::kJ >= 3 ? 3 : G::kJ)>(&lds[st][0], acc, wrow, srow, half); break;
+      case 2: stage_products<BMS, 2>(&lds[st][0], acc, wrow, srow, half); break;
+      case 1: stage_products<BMS, 1>(&lds[st][0], acc, wrow, srow, half); break;
       default: break;
     }
-    __syncthreads();  // waits for this wave's copies, then for every wave
+    ring_barrier(c * max(0, min(kn, nk - 1) - (kt + 1)));  // stage kt+1 landed
+    st = (st == S - 1) ? 0 : st + 1;
   }
   // element q of acc[f][j]: channel row 8*(q/4) + 4*half + q%4 of fragment f,
-  // slot row0 + wm*128 + 32 j + r; elements 4g .. 4g+3 are 4 consecutive
+  // slot row0 + wm*BMS/2 + 32 j + r; elements 4g .. 4g+3 are 4 consecutive
   // channels of the lane's slot.  A gate/up wave's 32 channels are one MXFP8
   // block of h, split over lanes r and r + 32: h is quantised here (fp32
   // value, block exponent from the amax over both lanes) and only its codes
   // and E8M0 byte are written.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < G::kJ; ++j) {
     if (j >= nj) continue;
-    const int slot = row0 + wm * 128 + j * 32 + r;
+    const int slot = row0 + wm * (BMS / 2) + j * 32 + r;
     if (MODE == kGateUp) {
       float hv[16];
       float m = 0.0f;
@@ -369,11 +397,10 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
       if (slot >= row_end) continue;
       uint8_t* hq = static_cast<uint8_t*>(out) + static_cast<int64_t>(slot) * I + nt * 128 + wn * 32;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < 4; ++g)
         *reinterpret_cast<uint32_t*>(hq + 8 * g + 4 * half) =
             e4m3x4(ldexpf(hv[4 * g], -x), ldexpf(hv[4 * g + 1], -x), ldexpf(hv[4 * g + 2], -x),
                    ldexpf(hv[4 * g + 3], -x));
-      }
       if (half == 0) out_scale[static_cast<int64_t>(slot) * (I / 32) + nt * 4 + wn] = static_cast<uint8_t>(x + 127);
     } else {
       if (slot >= row_end) continue;
@@ -432,12 +459,24 @@ hipError_t launch_experts_mxfp4(const Plan& p, const void* x, const uint8_t* w_g
     const int32_t* toff = ws_at<int32_t>(ws, p.off_tile_off);
     const int nt_gu = p.I / 128;
     const int nt_dn = static_cast<int>(ceil_div(p.H, tile::BN));
-    BEAM_LAUNCH(tm, "grouped_gate_up_mx", mxg::grouped_gemm_mx<mxg::kGateUp>,
-                tile::grid_for(p, nt_gu), dim3(tile::kThreads), 0, s, xq, xs, w_gate_up,
-                s_gate_up, hq, hs, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_gu);
-    BEAM_LAUNCH(tm, "grouped_down_mx", mxg::grouped_gemm_mx<mxg::kDown>,
-                tile::grid_for(p, nt_dn), dim3(tile::kThreads), 0, s, hq, hs, w_down, s_down,
-                y, nullptr, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_dn);
+#define BEAM_MX_TILES(BMS, STAGES)                                                            \
+  BEAM_LAUNCH(tm, "grouped_gate_up_mx", (mxg::grouped_gemm_mx<BMS, STAGES, mxg::kGateUp>),     \
+              tile::grid_for(p, nt_gu), dim3(tile::kThreads), 0, s, xq, xs, w_gate_up,         \
+              s_gate_up, hq, hs, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_gu); \
+  BEAM_LAUNCH(tm, "grouped_down_mx", (mxg::grouped_gemm_mx<BMS, STAGES, mxg::kDown>),          \
+              tile::grid_for(p, nt_dn), dim3(tile::kThreads), 0, s, hq, hs, w_down, s_down, y, \
+              nullptr, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_dn)
+    // measured on the Beam layer: 128-slot tiles (four stages) ahead below
+    // 1K tokens; 256-slot tiles with three stages ahead at 1K-4K tokens
+    // (2.38 vs 2.46 ms at 4K), with two at 8K (4.24 vs 4.36 ms)
+    if (p.bm == 128) {
+      BEAM_MX_TILES(128, 4);
+    } else if (p.S < 192 * static_cast<int64_t>(p.E)) {
+      BEAM_MX_TILES(256, 3);
+    } else {
+      BEAM_MX_TILES(256, 2);
+    }
+#undef BEAM_MX_TILES
     return hipGetLastError();
   }
   BEAM_LAUNCH(tm, "stream_gate_up_mx", stream_gate_up_mx,

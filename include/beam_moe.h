@@ -69,8 +69,9 @@ typedef enum {
 #define BEAM_ROUTE_LOGITS_IN (1u << 0) /* route from caller-supplied fp32 logits */
 #define BEAM_PATH_STREAM (1u << 1)     /* force the weight-streaming expert path */
 #define BEAM_PATH_GROUPED (1u << 2)    /* force the tiled grouped-GEMM expert path */
-#define BEAM_TILE_128 (1u << 3)        /* bf16 grouped path: force 128-row M tiles */
-#define BEAM_TILE_256 (1u << 4)        /* bf16 grouped path: force 256-row M tiles */
+#define BEAM_TILE_128 (1u << 3)        /* bf16 / MXFP4 grouped path: force 128-row M tiles */
+#define BEAM_TILE_256 (1u << 4)        /* bf16 / MXFP4 grouped path: force 256-row M tiles */
+#define BEAM_TILE_160 (1u << 5)        /* bf16 grouped path: force 160-row M tiles (MXFP4: 256) */
 
 typedef struct {
   int32_t hidden;           /* H: 5120 for Beam */

@@ -62,6 +62,7 @@ def test_validate_accepts_layer_shapes():
     ("flags", 1 << 9, gl.ERR_INVALID_ARG),
     ("flags", gl.PATH_STREAM | gl.PATH_GROUPED, gl.ERR_INVALID_ARG),
     ("flags", gl.TILE_128 | gl.TILE_256, gl.ERR_INVALID_ARG),
+    ("flags", gl.TILE_160 | gl.TILE_256, gl.ERR_INVALID_ARG),
 ])
 def test_validate_rejects(field, value, status):
     assert gl.validate(_desc(**{field: value}), 64) == status

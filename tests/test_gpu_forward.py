@@ -65,29 +65,29 @@ def test_small_bf16_skewed_long_chunks():
     w = WORKLOADS["prefill16k_skew"]
     inp = make_inputs(w, device=device(), tokens=700, shape=sh, seed=77)
     for path in (gl.PATH_STREAM, gl.PATH_GROUPED | gl.TILE_128,
-                 gl.PATH_GROUPED | gl.TILE_256):
+                 gl.PATH_GROUPED | gl.TILE_160, gl.PATH_GROUPED | gl.TILE_256):
         _check(inp, sh, desc_for(w, sh, path), np.arange(0, 700, 3), BF16_TOL,
                f"small skew path={path}")
 
 
 @pytest.mark.parametrize("T", [1, 37, 700, 2100])
 def test_tile_heights_bitwise_equal(T):
-    # 128- and 256-row tiles add the same products in the same order: equal
-    # bits, including tails of 1..255 rows and experts with many tiles
+    # 128-, 160- and 256-row tiles add the same products in the same order:
+    # equal bits, including tails of 1..255 rows and experts with many tiles
     sh = small_shape()
     w = WORKLOADS["prefill16k_skew"]
     inp = make_inputs(w, device=device(), tokens=T, shape=sh, seed=500 + T)
     outs = []
-    for tile in (gl.TILE_128, gl.TILE_256):
+    for tile in (gl.TILE_128, gl.TILE_160, gl.TILE_256):
         d = desc_for(w, sh, gl.PATH_GROUPED | tile)
         outs.append(gl.forward(d, inp.x, inp.w_router, inp.bias, inp.w_gate_up,
                                inp.w_down))
     torch.cuda.synchronize()
-    assert torch.equal(outs[0], outs[1])
+    assert torch.equal(outs[0], outs[2]) and torch.equal(outs[1], outs[2])
 
 
 @pytest.mark.parametrize("path", [gl.PATH_STREAM, gl.PATH_GROUPED | gl.TILE_128,
-                                  gl.PATH_GROUPED | gl.TILE_256])
+                                  gl.PATH_GROUPED | gl.TILE_160, gl.PATH_GROUPED | gl.TILE_256])
 def test_odd_widths_skewed(path):
     # hidden and intermediate multiples of 128 but not of 256: the last
     # 256-wide down tile of the grouped path is half outside H

@@ -82,7 +82,8 @@ def test_mxfp4_beam_decode64():
     _check(inp, BEAM, np.arange(64), "mxfp4_decode64")
 
 
-@pytest.mark.parametrize("path", [gl.PATH_STREAM, gl.PATH_GROUPED])
+@pytest.mark.parametrize("path", [gl.PATH_STREAM, gl.PATH_GROUPED,
+                                  gl.PATH_GROUPED | gl.TILE_128, gl.PATH_GROUPED | gl.TILE_256])
 def test_mxfp4_both_paths(path):
     sh = small_shape()
     inp = make_inputs(WORKLOADS["mxfp4_8k"], device=device(), tokens=333, shape=sh, seed=88)
@@ -95,3 +96,20 @@ def test_mxfp4_beam_8k_sampled():
     rows = np.sort(np.random.default_rng(3).choice(T, 16, replace=False))
     rows[-1] = T - 1
     _check(inp, BEAM, rows, "mxfp4_8k sampled")
+
+
+@pytest.mark.parametrize("T", [3, 700, 2100])
+def test_mxfp4_tile_forms_bitwise_equal(T):
+    # 128-slot tiles (4-stage ring) and 256-slot tiles (3-stage ring below
+    # T*K = 192E, 2-stage above: T = 2100 on this shape) add the same
+    # products in the same order and quantise h alike: equal bits
+    sh = small_shape()
+    inp = make_inputs(WORKLOADS["mxfp4_8k"], device=device(), tokens=T, shape=sh,
+                      seed=900 + T, bias="skew:0.5:0,1,2,3,32,33,34,35")
+    outs = []
+    for tile in (gl.TILE_128, gl.TILE_256):
+        d = desc_for(WORKLOADS["mxfp4_8k"], sh, gl.PATH_GROUPED | tile)
+        outs.append(gl.forward(d, inp.x, inp.w_router, inp.bias, inp.w_gate_up, inp.w_down,
+                               inp.s_gate_up, inp.s_down))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])

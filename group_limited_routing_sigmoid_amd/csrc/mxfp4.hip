@@ -9,8 +9,10 @@
 // 32 k-values by 2^(scale - 127) for both operands, so the block scales are
 // exact and no vector work rescales the sums.
 //
-// The streaming kernels serve decode-sized batches: weights are the 32-row A
-// side (fp4), up to 32 tokens the B side (fp8).  Gate/up: a wave owns 16 gate
+// Two expert paths: grouped tiles with copy rings (the default at every batch
+// size; measured ahead of streaming down to one token) and weight-streaming
+// kernels (on request).  Streaming: weights are the 32-row A side (fp4), up
+// to 32 tokens the B side (fp8).  Gate/up: a wave owns 16 gate
 // and the 16 matching up rows, whose products land in the same lane (rows r
 // and r + 16 are accumulator elements q and q + 8).  Down: a wave owns 32
 // rows of W_d.  Experts with more than 32 tokens are handled in chunks.

@@ -75,6 +75,13 @@ using namespace tile;
 
 enum Mode { kGateUp = 0, kDown = 1 };
 
+// An expert's last M tile may hold 32 extension rows past the 256 (tile rows
+// 256..287): their A rows get a 4 KiB tile of their own after the A and B
+// tiles of each stage.
+constexpr int kXRows = 32;
+constexpr int BMX = BM + kXRows;
+typedef unsigned char TileLdsX[2][2 * kTileBytes + kXRows * kRowBytes];
+
 // D = A(32x64) * B(64x32) + C on e4m3 codes (format 0, unit E8M0 scales).
 // Lane l supplies row (l % 32) of A and column (l % 32) of B, codes
 // 32*(l/32) .. +32 of the 64-deep slice; C as for the bf16 32x32 MFMA.
@@ -90,8 +97,10 @@ __device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c) 
 // per-lane row offset, one of four per-lane chunk offsets and a constant.
 struct FragAddr {
   uint32_t a_row, b_row;  // byte offsets of the lane's A row (f = 0) and B row (n = 0)
+  uint32_t x_row;         // byte offset of its row in the extension rows' tile
   uint32_t p[2][2];       // p[j][flip]: chunk byte offset
   uint32_t r_row;         // byte offset of the lane's first ratio (per-row factor)
+  uint32_t r_row_x;       // the same for the extension rows (tile rows 256..)
 };
 
 __device__ __forceinline__ FragAddr frag_addr(int wm, int wn, int lane) {
@@ -100,12 +109,14 @@ __device__ __forceinline__ FragAddr frag_addr(int wm, int wn, int lane) {
   const int key = (l ^ (l >> 3)) & 7;
   fa.a_row = static_cast<uint32_t>(wm * 128 + l) * kRowBytes;
   fa.b_row = static_cast<uint32_t>(wn * 64 + l) * kRowBytes;
+  fa.x_row = static_cast<uint32_t>(l) * kRowBytes;
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int f = 0; f < 2; ++f)
       fa.p[j][f] = static_cast<uint32_t>((((2 * (lane / 32) + j) ^ key) ^ (4 * f)) << 4);
   fa.r_row = static_cast<uint32_t>(wm * 128 + 4 * (lane / 32)) * 4;
+  fa.r_row_x = static_cast<uint32_t>(BM + 4 * (lane / 32)) * 4;
   return fa;
 }
 
@@ -121,7 +132,7 @@ __device__ __forceinline__ i32x8 frag8(const unsigned char* t, uint32_t row, con
 }
 
 // acc[i][n] *= v[row of element] for the 16 rows fragment i holds in this
-// lane (v: the 256 per-row factors of the wave's weight block, in LDS).
+// lane (v: the per-row factors of the wave's weight block, in LDS).
 __device__ __forceinline__ void scale_rows(f32x16 (&acc)[4][2], int i, const float* v,
                                            const FragAddr& fa) {
   const unsigned char* base = reinterpret_cast<const unsigned char*>(v) + fa.r_row;
@@ -135,19 +146,39 @@ __device__ __forceinline__ void scale_rows(f32x16 (&acc)[4][2], int i, const flo
   }
 }
 
+// The same for the extension rows' accumulator.
+__device__ __forceinline__ void scale_rows_x(f32x16& accx, const float* v, const FragAddr& fa) {
+  const unsigned char* base = reinterpret_cast<const unsigned char*>(v) + fa.r_row_x;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(base + 8 * q * 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) accx[4 * q + j] *= t[j];
+  }
+}
+
 // One 128-deep stage for the wave's first NF fragments: rescale the
 // accumulators to this stage's scale and add the stage's exact products, one
 // 64-deep half at a time (B fragments of the half held, A fragments read one
 // ahead).  Fragment i is rescaled just before its first product of the
 // stage, so the multiplies overlap the matrix-core work of fragment i-1.
-template <int NF>
+// XT: the tile also holds extension rows (tile rows 256..287, their own
+// 4 KiB tile xt); wave (wm, wn) adds their products with its B fragment wm,
+// i.e. columns wn*64 + wm*32 .. +32, into accx.
+template <int NF, bool XT>
 __device__ __forceinline__ void fp8_stage(const unsigned char* at, const unsigned char* bt,
-                                          const float* ratio, f32x16 (&acc)[4][2],
+                                          const unsigned char* xt, const float* ratio,
+                                          f32x16 (&acc)[4][2], f32x16& accx, int wm,
                                           const FragAddr& fa) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const i32x8 b0 = frag8(bt, fa.b_row, fa, 0, h);
     const i32x8 b1 = frag8(bt, fa.b_row, fa, 1, h);
+    if (XT) {
+      const i32x8 ax = frag8(xt, fa.x_row, fa, 0, h);
+      if (h == 0) scale_rows_x(accx, ratio, fa);
+      accx = mfma_fp8_32x32x64(ax, wm ? b1 : b0, accx);
+    }
     i32x8 a = frag8(at, fa.a_row, fa, 0, h);
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
@@ -165,15 +196,23 @@ __device__ __forceinline__ void fp8_stage(const unsigned char* at, const unsigne
 // 128-deep stage kb is P_kb (unit scales); the result is sum_kb s_kb * P_kb
 // with s_kb = s_a[row, kb] * s_w[block, kb].  The accumulator is kept in units
 // of the current stage's s: before adding P_kb it is multiplied by
-// s_{kb-1} / s_kb, and the epilogue multiplies by the last s.  Thread
-// (blk, srow) = (tid / 256, tid % 256) computes the factor of tile row srow
-// for weight block blk one stage ahead into rsc.  Returns that thread's last s.
-template <int NF>
-__device__ __forceinline__ float fp8_mainloop(
+// s_{kb-1} / s_kb, and the epilogue multiplies by the last s.  Each thread
+// computes the factors of its (weight block, tile row) items one stage ahead
+// into rsc: (tid / 256, tid % 256), and, in a tile with extension rows (XT),
+// for threads 0..63 also an extension row (tid / 32, 256 + tid % 32) (the
+// others repeat their first item).  s_last receives the items' last s.
+struct ScaleItems {
+  const float* sa[2];  // s_a of the item's row, one word per block
+  const float* sw[2];  // s_w of the item's weight block
+  int blk[2], row[2];
+};
+
+template <int NF, bool XT>
+__device__ __forceinline__ void fp8_mainloop(
     const uint8_t* __restrict__ a_src, const uint32_t* a_off, const bool* a_ok,
-    const uint8_t* __restrict__ wb, const uint32_t* b_off, const float* sa_src,
-    const float* sw_src, int nkb, TileLds& lds, float (&rsc)[2][2][BM], int blk, int srow,
-    f32x16 (&acc)[4][2], const FragAddr& fa, int wn) {
+    uint32_t x_off, bool x_ok, const uint8_t* __restrict__ wb, const uint32_t* b_off,
+    const ScaleItems& it, int nkb, TileLdsX& lds, float (&rsc)[2][2][BMX],
+    f32x16 (&acc)[4][2], f32x16& accx, const FragAddr& fa, int wm, int wn, float (&s_last)[2]) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   auto dma = [&](int buf, int kb) {
 #pragma unroll
@@ -182,12 +221,19 @@ __device__ __forceinline__ float fp8_mainloop(
       if (a_ok[i]) dma16(a_src + (a_off[i] + kb * 128), &lds[buf][region * 1024]);
       dma16(wb + (b_off[i] + kb * 128), &lds[buf][kTileBytes + region * 1024]);
     }
+    if (x_ok) dma16(a_src + (x_off + kb * 128), &lds[buf][2 * kTileBytes + wave * 1024]);
   };
+  constexpr int NI = XT ? 2 : 1;  // scale items per thread
   dma(0, 0);
-  float s_prev = sa_src[0] * sw_src[0];
-  // factors of stage 1, loaded a stage ahead of their use
-  float sa_n = sa_src[min(1, nkb - 1)], sw_n = sw_src[min(1, nkb - 1)];
-  rsc[0][blk][srow] = 1.0f;
+  float s_prev[NI], sa_n[NI], sw_n[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    s_prev[j] = it.sa[j][0] * it.sw[j][0];
+    // factors of stage 1, loaded a stage ahead of their use
+    sa_n[j] = it.sa[j][min(1, nkb - 1)];
+    sw_n[j] = it.sw[j][min(1, nkb - 1)];
+    rsc[0][it.blk[j]][it.row[j]] = 1.0f;
+  }
   __syncthreads();
   for (int kt = 0; kt < nkb; ++kt) {
     const int buf = kt & 1;
@@ -196,20 +242,34 @@ __device__ __forceinline__ float fp8_mainloop(
     if (kt + 1 < nkb) dma(buf ^ 1, kt + 1);
     // scale factors of stage kt+2 (consumed after the next barrier)
     const int k2 = min(kt + 2, nkb - 1);
-    const float sa2 = sa_src[k2], sw2 = sw_src[k2];
+    float sa2[NI], sw2[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      sa2[j] = it.sa[j][k2];
+      sw2[j] = it.sw[j][k2];
+    }
     // no branch from here to the barrier, so the compiler keeps the
     // stage's reads next to the products that use them
     if (NF > 0)
-      fp8_stage<NF>(&lds[buf][0], &lds[buf][kTileBytes], &rsc[buf][wn / 2][0], acc, fa);
-    // factor of stage kt+1 (after the last stage it lands in an unused buffer)
-    const float s = sa_n * sw_n;
-    rsc[buf ^ 1][blk][srow] = s_prev / s;
-    s_prev = (kt + 1 < nkb) ? s : s_prev;
-    sa_n = sa2;
-    sw_n = sw2;
+      fp8_stage<NF, XT>(&lds[buf][0], &lds[buf][kTileBytes], &lds[buf][2 * kTileBytes],
+                        &rsc[buf][wn / 2][0], acc, accx, wm, fa);
+    // The factor arithmetic waits for its inputs with the wave's whole
+    // vector-memory count, stage kt+1's copies included: keep it after the
+    // products (the barrier below waits for those copies anyway).
+    __builtin_amdgcn_sched_barrier(0);
+    // factors of stage kt+1 (after the last stage they land in an unused buffer)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const float s = sa_n[j] * sw_n[j];
+      rsc[buf ^ 1][it.blk[j]][it.row[j]] = s_prev[j] / s;
+      s_prev[j] = (kt + 1 < nkb) ? s : s_prev[j];
+      sa_n[j] = sa2[j];
+      sw_n[j] = sw2[j];
+    }
     __syncthreads();  // waits for this wave's loads, then for every wave
   }
-  return s_prev;
+  s_last[0] = s_prev[0];
+  s_last[1] = s_prev[NI - 1];
 }
 
 // Grouped e4m3 GEMM with per-128 block scales.  Same work list, tile
@@ -230,9 +290,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
     float* __restrict__ out_scale,       // gate/up: hs [S,I/128]; down: unused
     const int32_t* __restrict__ slot_token, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off,
-    const int32_t* __restrict__ meta, int E, int H, int I, int n_nt) {
-  __shared__ __attribute__((aligned(16))) TileLds lds;
-  __shared__ __attribute__((aligned(16))) float rsc[2][2][BM];
+    const int32_t* __restrict__ meta, int E, int H, int I, int n_nt, int xt) {
+  __shared__ __attribute__((aligned(16))) TileLdsX lds;
+  __shared__ __attribute__((aligned(16))) float rsc[2][2][BMX];
 
   Coords tc;
   if (!tile_coords(counts, offsets, tile_off, meta, E, n_nt, tc)) return;
@@ -242,6 +302,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int wm = wave / 4, wn = wave % 4;
   const int m_valid = min(BM, row_end - row0);
+  // extension rows: only in an expert's last tile, when tiles may extend
+  // (a tile with more than BM + xt rows left is not the last)
+  const int m_all = row_end - row0;
+  const int x_rows = (m_all > BM && m_all <= BM + xt) ? m_all - BM : 0;
+  const int uwave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy
 
   const uint8_t* wb = w + static_cast<int64_t>(e) * ((MODE == kGateUp) ? 2 * I : H) * K;
   uint32_t a_off[kLoads], b_off[kLoads];
@@ -260,15 +325,28 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
                                        : min(nt * BN + r, H - 1);
     b_off[i] = static_cast<uint32_t>(wrow) * K + c * 16;
   }
-  // scale thread: tile row srow, weight block blk of the tile
-  const int blk = tid / BM, srow = tid % BM;
-  const int sslot = min(row0 + srow, row_end - 1);
-  const float* sa_src = a_scale + static_cast<int64_t>(
-      (MODE == kGateUp) ? slot_token[sslot] : sslot) * nkb;
+  // extension rows' copies: waves 0..3, one 8-row region each
+  const int xr = 8 * uwave + lane / 8;
+  const bool x_ok = uwave < 4 && 8 * uwave < x_rows;
+  const uint32_t x_off =
+      ((MODE == kGateUp) ? static_cast<uint32_t>(slot_token[min(row0 + BM + xr, row_end - 1)]) * H
+                         : static_cast<uint32_t>(min(row0 + BM + xr, row_end - 1)) * I) +
+      dma_chunk(xr, lane) * 16;
+  // scale items: (weight block, tile row)
   const int nrb = (MODE == kGateUp) ? 2 * I / 128 : H / 128;
-  const int wblock = (MODE == kGateUp) ? (blk == 0 ? nt : I / 128 + nt)
-                                       : min(2 * nt + blk, nrb - 1);
-  const float* sw_src = w_scale + (static_cast<int64_t>(e) * nrb + wblock) * nkb;
+  ScaleItems it;
+  it.blk[0] = tid / BM;
+  it.row[0] = tid % BM;
+  it.blk[1] = (tid < 2 * kXRows) ? tid / kXRows : it.blk[0];
+  it.row[1] = (tid < 2 * kXRows) ? BM + tid % kXRows : it.row[0];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int sslot = min(row0 + it.row[j], row_end - 1);
+    it.sa[j] = a_scale + static_cast<int64_t>((MODE == kGateUp) ? slot_token[sslot] : sslot) * nkb;
+    const int wblock = (MODE == kGateUp) ? (it.blk[j] == 0 ? nt : I / 128 + nt)
+                                         : min(2 * nt + it.blk[j], nrb - 1);
+    it.sw[j] = w_scale + (static_cast<int64_t>(e) * nrb + wblock) * nkb;
+  }
 
   // A rows of this wave: wm*128 + 32 i + lane%32; B rows: wn*64 + 32 n + lane%32
   const FragAddr fa = frag_addr(wm, wn, lane);
@@ -278,27 +356,34 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int n = 0; n < 2; ++n) acc[i][n] = f32x16{};
+  f32x16 accx = f32x16{};
 
-  const int nf = wave_frags(m_valid, wm);
-  float s_last;
-#define BEAM_FP8_LOOP(NF)                                                                   \
-  s_last = fp8_mainloop<NF>(a_src, a_off, a_ok, wb, b_off, sa_src, sw_src, nkb, lds, rsc, \
-                            blk, srow, acc, fa, wn)
+  const int nf = wave_frags(m_valid, wm);  // 4 whenever there are extension rows
+  float s_last[2];
+#define BEAM_FP8_LOOP(NF, XT)                                                                 \
+  fp8_mainloop<NF, XT>(a_src, a_off, a_ok, x_off, x_ok, wb, b_off, it, nkb, lds, rsc, acc, \
+                       accx, fa, wm, wn, s_last)
   switch (nf) {
-    case 4: BEAM_FP8_LOOP(4); break;
-    case 3: BEAM_FP8_LOOP(3); break;
-    case 2: BEAM_FP8_LOOP(2); break;
-    case 1: BEAM_FP8_LOOP(1); break;
-    default: BEAM_FP8_LOOP(0); break;
+    case 4:
+      if (x_rows > 0) BEAM_FP8_LOOP(4, true);
+      else BEAM_FP8_LOOP(4, false);
+      break;
+    case 3: BEAM_FP8_LOOP(3, false); break;
+    case 2: BEAM_FP8_LOOP(2, false); break;
+    case 1: BEAM_FP8_LOOP(1, false); break;
+    default: BEAM_FP8_LOOP(0, false); break;
   }
 #undef BEAM_FP8_LOOP
 
   // ---- epilogue: last stage's scale, then store ---------------------------
-  rsc[0][blk][srow] = s_last;  // rsc is no longer read by the main loop
+  // rsc is no longer read by the main loop
+  rsc[0][it.blk[0]][it.row[0]] = s_last[0];
+  rsc[0][it.blk[1]][it.row[1]] = s_last[1];
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (i < nf) scale_rows(acc, i, &rsc[0][wn / 2][0], fa);
+  if (x_rows > 0) scale_rows_x(accx, &rsc[0][wn / 2][0], fa);
 
   if (MODE == kGateUp) {
     // up values, fp32, [256 rows][128 channels] over the two tile buffers
@@ -356,6 +441,45 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
         if (tid % 16 == 0) out_scale[row * (I / 128) + nt] = sc;
       }
     }
+    if (x_rows > 0) {
+      // extension rows (32 x 128 channels): wave (wm, wn) holds channels
+      // (wn % 2)*64 + wm*32 .. +32, gate for wn < 2 and up for wn >= 2
+      __syncthreads();  // every read of ex above is done
+      if (wn >= 2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+          ex[rl * 128 + (wn - 2) * 64 + wm * 32 + lane % 32] = accx[r];
+        }
+      }
+      __syncthreads();
+      if (wn < 2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+          const int at = rl * 128 + wn * 64 + wm * 32 + lane % 32;
+          const float h = silu(accx[r]) * ex[at];
+          ex[at] = __uint_as_float(static_cast<uint32_t>(f32_to_bf16_bits(h)) << 16);
+        }
+      }
+      __syncthreads();
+      const int rl = tid / 16, c8 = 8 * (tid % 16);  // 32 rows, one pass
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(&ex[rl * 128 + c8]);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(&ex[rl * 128 + c8 + 4]);
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(v0[j]), fabsf(v1[j])));
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      const float sc = (m > 0.0f) ? m / 448.0f : 1.0f;
+      const uint32_t lo = e4m3x4(v0[0] / sc, v0[1] / sc, v0[2] / sc, v0[3] / sc);
+      const uint32_t hi = e4m3x4(v1[0] / sc, v1[1] / sc, v1[2] / sc, v1[3] / sc);
+      if (rl < x_rows) {
+        const int64_t row = row0 + BM + rl;
+        *reinterpret_cast<uint2*>(hq + row * I + nt * 128 + c8) = make_uint2(lo, hi);
+        if (tid % 16 == 0) out_scale[row * (I / 128) + nt] = sc;
+      }
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -371,6 +495,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
             static_cast<uint16_t*>(out)[static_cast<int64_t>(row) * H + col] =
                 f32_to_bf16_bits(acc[i][n][r]);
         }
+      }
+    }
+    if (x_rows > 0) {
+      const int col = nt * BN + wn * 64 + wm * 32 + lane % 32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+        if (rl < x_rows && col < H)
+          static_cast<uint16_t*>(out)[static_cast<int64_t>(row0 + BM + rl) * H + col] =
+              f32_to_bf16_bits(accx[r]);
       }
     }
   }
@@ -401,10 +535,10 @@ hipError_t launch_experts_fp8(const Plan& p, const void* x,
   const int nt_dn = static_cast<int>(ceil_div(p.H, BN));
   BEAM_LAUNCH(tm, "gate_up_fp8", grouped_gemm_fp8<kGateUp>, grid_for(p, nt_gu),
               dim3(kThreads), 0, s, xq, xs, w_gate_up, s_gate_up, hq, hs, slot_token,
-              counts, offsets, toff, meta, p.E, p.H, p.I, nt_gu);
+              counts, offsets, toff, meta, p.E, p.H, p.I, nt_gu, p.xt);
   BEAM_LAUNCH(tm, "down_fp8", grouped_gemm_fp8<kDown>, grid_for(p, nt_dn),
               dim3(kThreads), 0, s, hq, hs, w_down, s_down, y, nullptr, slot_token,
-              counts, offsets, toff, meta, p.E, p.H, p.I, nt_dn);
+              counts, offsets, toff, meta, p.E, p.H, p.I, nt_dn, p.xt);
   return hipGetLastError();
 }
 

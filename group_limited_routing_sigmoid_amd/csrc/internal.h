@@ -27,6 +27,7 @@ struct Plan {
   bool router_gemm;    // logits by the dense tile GEMM (many tokens)
   bool stream_path;    // weight-streaming experts (few tokens per expert)
   int32_t bm;          // rows per grouped-GEMM M tile: 256, 160 (bf16), 128 (bf16, MXFP4)
+  int32_t xt;          // extra rows an expert's last M tile may hold (FP8: 32)
   int64_t max_tiles;   // upper bound on grouped-GEMM M tiles
   // byte offsets into the workspace
   size_t off_part, off_idx, off_w, off_hist, off_base, off_rank, off_counts,

@@ -73,7 +73,7 @@ __device__ int block_scan_incl(int v, int* sh) {
 
 // one block of 1024 threads; thread e handles expert e
 __global__ __launch_bounds__(kMaxE) void perm_scan(
-    const int32_t* __restrict__ hist, int64_t nb, int E, int bm,
+    const int32_t* __restrict__ hist, int64_t nb, int E, int bm, int xt,
     int32_t* __restrict__ base, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ tile_expert,
     int32_t* __restrict__ tile_row0, int32_t* __restrict__ meta,
@@ -88,7 +88,8 @@ __global__ __launch_bounds__(kMaxE) void perm_scan(
     }
   const int incl = block_scan_incl(c, sh);
   const int off = incl - c;
-  const int nt = (c + bm - 1) / bm;
+  // M tiles of bm rows; the last may hold up to xt more (bm + xt in all)
+  const int nt = (c <= 0) ? 0 : max(1, (c - xt + bm - 1) / bm);
   const int tincl = block_scan_incl(nt, sh);
   const int toff = tincl - nt;
   const int act = c > 0;
@@ -166,7 +167,7 @@ hipError_t launch_permute(const Plan& p, const int32_t* idx, int32_t* counts,
   BEAM_LAUNCH(tm, "perm_rank", perm_rank, dim3(nb), dim3(kPermBlock), 0, s, idx, p.T,
                      p.K, p.E, hist, rank);
   BEAM_LAUNCH(tm, "perm_scan", perm_scan, dim3(1), dim3(kMaxE), 0, s, hist, p.nb, p.E,
-                     p.bm, base, counts, offsets,
+                     p.bm, p.xt, base, counts, offsets,
                      ws_at<int32_t>(ws, p.off_tile_expert),
                      ws_at<int32_t>(ws, p.off_tile_row0),
                      ws_at<int32_t>(ws, p.off_meta),

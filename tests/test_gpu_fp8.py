@@ -35,8 +35,8 @@ def test_quant_bit_exact(dtype):
     np.testing.assert_array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
 
 
-def _check(inp, shape, tokens, label):
-    d = desc_for(WORKLOADS["fp8_8k"], shape)
+def _check(inp, shape, tokens, label, flags=0):
+    d = desc_for(WORKLOADS["fp8_8k"], shape, flags)
     out, idx, w, lg = gl.forward(d, inp.x, inp.w_router, inp.bias, inp.w_gate_up,
                                  inp.w_down, inp.s_gate_up, inp.s_down,
                                  return_routing=True)
@@ -52,6 +52,7 @@ def _check(inp, shape, tokens, label):
           f"{e_emu:.3e} vs e4m3 emulation oracle")
     assert e_ref <= FP8_TOL, e_ref
     assert e_emu <= EMU_TOL, e_emu
+    return out, idx
 
 
 @pytest.mark.parametrize("T", [1, 5, 300])
@@ -79,3 +80,23 @@ def test_fp8_odd_widths_skewed(T):
     inp = make_inputs(WORKLOADS["fp8_8k"], device=device(), tokens=T, shape=sh,
                       seed=40 + T, bias="skew:0.5:0,1,2,3,32,33,34,35")
     _check(inp, sh, np.arange(0, T, 2), f"fp8 H=I=384 skew T={T}")
+
+
+@pytest.mark.parametrize("T", [2100, 4300])
+@pytest.mark.parametrize("hidden", [512, 384])
+def test_fp8_extended_last_tiles(T, hidden):
+    # 262 / 537 rows per expert on average: many experts end in a tile of
+    # 257..288 rows (one 256-row tile extended by up to 32 rows), some in a
+    # plain one.  Against the oracle with and without the extension, and the
+    # two bit-identical (same products, same order, same scale steps).
+    sh = small_shape(hidden=hidden, intermediate=384 if hidden == 384 else 256)
+    inp = make_inputs(WORKLOADS["fp8_8k"], device=device(), tokens=T, shape=sh,
+                      seed=60 + T + hidden)
+    a, idx = _check(inp, sh, np.arange(0, T, 7), f"fp8 extended tiles T={T} H={hidden}")
+    b, _ = _check(inp, sh, np.arange(0, T, 7), f"fp8 256-row tiles T={T} H={hidden}",
+                  gl.TILE_256)
+    counts = torch.bincount(idx.flatten().long(), minlength=sh.n_experts).cpu()
+    ext = ((counts % 256 >= 1) & (counts % 256 <= 32) & (counts > 256)).sum().item()
+    print(f"experts whose last tile is extended: {ext} of {sh.n_experts}")
+    assert ext > 0
+    assert torch.equal(a, b)

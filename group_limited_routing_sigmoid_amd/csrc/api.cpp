@@ -133,8 +133,6 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
   p->off_offsets = take((E + 1) * 4);
   p->off_slot_token = take(S * 4);
   p->off_slot_of = take(S * 4);
-  p->off_tile_expert = take(p->max_tiles * 4);
-  p->off_tile_row0 = take(p->max_tiles * 4);
   p->off_meta = take(kMetaWords * 4);
   p->off_active = take(E * 4);
   p->off_tile_off = take((E + 1) * 4);

@@ -31,7 +31,7 @@ struct Plan {
   int64_t max_tiles;   // upper bound on grouped-GEMM M tiles
   // byte offsets into the workspace
   size_t off_part, off_idx, off_w, off_hist, off_base, off_rank, off_counts,
-      off_offsets, off_slot_token, off_slot_of, off_tile_expert, off_tile_row0,
+      off_offsets, off_slot_token, off_slot_of,
       off_meta, off_active, off_tile_off, off_w3, off_h, off_y, off_xq, off_xs,
       off_hq, off_hs;
   size_t total;

@@ -75,8 +75,7 @@ __device__ int block_scan_incl(int v, int* sh) {
 __global__ __launch_bounds__(kMaxE) void perm_scan(
     const int32_t* __restrict__ hist, int64_t nb, int E, int bm, int xt,
     int32_t* __restrict__ base, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ tile_expert,
-    int32_t* __restrict__ tile_row0, int32_t* __restrict__ meta,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ meta,
     int32_t* __restrict__ active, int32_t* __restrict__ tile_off) {
   __shared__ int sh[kMaxE];
   const int e = threadIdx.x;
@@ -97,10 +96,6 @@ __global__ __launch_bounds__(kMaxE) void perm_scan(
   if (e < E) {
     counts[e] = c;
     offsets[e] = off;
-    for (int i = 0; i < nt; ++i) {
-      tile_expert[toff + i] = e;
-      tile_row0[toff + i] = off + i * bm;
-    }
     if (act) active[aincl - 1] = e;
     tile_off[e] = toff;
   }
@@ -168,8 +163,6 @@ hipError_t launch_permute(const Plan& p, const int32_t* idx, int32_t* counts,
                      p.K, p.E, hist, rank);
   BEAM_LAUNCH(tm, "perm_scan", perm_scan, dim3(1), dim3(kMaxE), 0, s, hist, p.nb, p.E,
                      p.bm, p.xt, base, counts, offsets,
-                     ws_at<int32_t>(ws, p.off_tile_expert),
-                     ws_at<int32_t>(ws, p.off_tile_row0),
                      ws_at<int32_t>(ws, p.off_meta),
                      ws_at<int32_t>(ws, p.off_active),
                      ws_at<int32_t>(ws, p.off_tile_off));

@@ -111,9 +111,14 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
     else if (p->flags & (BEAM_TILE_160 | BEAM_TILE_256)) p->bm = kGemmBM;
     else if (S < 32 * E) p->bm = 128;
   }
-  // FP8: an expert's last tile takes up to 32 rows past 256 (experts near
-  // 256 rows then need one tile, not a full one plus a sliver)
-  p->xt = (p->wdt == BEAM_FP8_E4M3 && !(p->flags & BEAM_TILE_256)) ? 32 : 0;
+  // FP8, and MXFP4 where its 256-slot tiles run two stages (T*K >= 192E):
+  // an expert's last tile takes up to 32 rows past 256, so experts near 256
+  // rows need one tile, not a full one plus a sliver
+  p->xt = 0;
+  if (!(p->flags & BEAM_TILE_256) && p->bm == kGemmBM) {
+    if (p->wdt == BEAM_FP8_E4M3) p->xt = 32;
+    if (p->wdt == BEAM_MXFP4 && S >= 192 * E) p->xt = 32;
+  }
   p->max_tiles = S / p->bm + (S < E ? S : E) + 1;
   const bool f32 = p->wdt == BEAM_F32;
   size_t o = 0;

@@ -16,6 +16,8 @@
 // and the 16 matching up rows, whose products land in the same lane (rows r
 // and r + 16 are accumulator elements q and q + 8).  Down: a wave owns 32
 // rows of W_d.  Experts with more than 32 tokens are handled in chunks.
+#include <type_traits>
+
 #include "grouped_tile.h"
 
 namespace beam {
@@ -227,11 +229,17 @@ namespace mxg {
 
 using namespace tile;
 
+// With two stages (256 slots) an expert's last tile may hold 32 extension
+// slots past the 256: their activation rows and scale words get an area of
+// their own after each stage's tiles.
+constexpr int kXtRows = 32;
 template <int BMS, int STAGES>
 struct Geo {
   static constexpr int kXBytes = BMS * 128;  // activation tile per stage
   static constexpr int kWBytes = BN * 64;    // weight tile per stage
-  static constexpr int kStage = kXBytes + kWBytes + (BMS + BN) * 4;
+  static constexpr int kXtOff = kXBytes + kWBytes + (BMS + BN) * 4;
+  static constexpr bool kExt = STAGES == 2;  // room for extension slots
+  static constexpr int kStage = kXtOff + (kExt ? kXtRows * 128 + 256 : 0);
   static constexpr int kStages = STAGES;
   static constexpr int kXLoads = kXBytes / (16 * tile::kThreads);  // 4 or 2
   static constexpr int kXsWaves = BMS / 64;  // waves copying activation scale words
@@ -244,10 +252,14 @@ __device__ __forceinline__ int wswz(int row, int chunk) {  // 64-byte weight row
 
 enum Mode { kGateUp = 0, kDown = 1 };
 
-template <int BMS, int NJ>
+// XT: also the extension slots (B rows of the extension area) against the
+// wave's A fragment wm into accx (gate channels for wm = 0, up channels for
+// wm = 1 on gate/up; output columns wn*64 + wm*32 .. on down).
+template <int BMS, int NJ, bool XT>
 __device__ __forceinline__ void stage_products(const unsigned char* st,
-                                               f32x16 (&acc)[2][BMS / 64],
-                                               const int* wrow, const int* srow, int half) {
+                                               f32x16 (&acc)[2][BMS / 64], f32x16& accx,
+                                               const int* wrow, const int* srow, int half,
+                                               int wm) {
   using G = Geo<BMS, 2>;
   const unsigned char* X = st;
   const unsigned char* W = st + G::kXBytes;
@@ -272,6 +284,16 @@ __device__ __forceinline__ void stage_products(const unsigned char* st,
 #pragma unroll
       for (int f = 0; f < 2; ++f) acc[f][j] = mfma_mx(a[f], b0, b1, acc[f][j], sa[f], sb);
     }
+    if (XT) {
+      const unsigned char* XX = st + Geo<BMS, 2>::kXtOff;
+      const uint32_t* XXS = reinterpret_cast<const uint32_t*>(XX + kXtRows * 128);
+      const int row = srow[0] % 32;  // the lane's extension slot
+      const int key = (row ^ (row >> 3)) & 7;
+      const u32x4 b0 = *reinterpret_cast<const u32x4*>(XX + row * 128 + (((4 * ks + half) ^ key) << 4));
+      const u32x4 b1 = *reinterpret_cast<const u32x4*>(XX + row * 128 + (((4 * ks + 2 + half) ^ key) << 4));
+      const uint32_t sb = (XXS[row] >> (8 * (2 * ks + half))) & 0xFFu;
+      accx = mfma_mx(wm ? a[1] : a[0], b0, b1, accx, wm ? sa[1] : sa[0], sb);
+    }
   }
 }
 
@@ -285,7 +307,7 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
     uint8_t* __restrict__ out_scale,     // gate/up: hs [S,I/32] (E8M0); down: unused
     const int32_t* __restrict__ slot_token, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off,
-    const int32_t* __restrict__ meta, int E, int H, int I, int n_nt) {
+    const int32_t* __restrict__ meta, int E, int H, int I, int n_nt, int xt) {
   using G = Geo<BMS, STAGES>;
   constexpr int S = G::kStages, P = S - 1;  // ring size, stages in flight
   __shared__ __attribute__((aligned(16))) unsigned char lds[S][G::kStage];
@@ -298,6 +320,9 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
   const int uwave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy
   const int wm = wave / 4, wn = wave % 4, r = lane % 32, half = lane / 32;
   const int m_valid = min(BMS, row_end - row0);
+  // extension slots: only in an expert's last tile, when tiles may extend
+  const int m_all = row_end - row0;
+  const int x_rows = (G::kExt && m_all > BMS && m_all <= BMS + xt) ? m_all - BMS : 0;
   const int64_t nrows = (MODE == kGateUp) ? 2 * I : H;
   const uint8_t* wb = w + static_cast<int64_t>(e) * nrows * (K / 2);
   const uint8_t* wsb = ws + static_cast<int64_t>(e) * nrows * (K / 32);
@@ -335,6 +360,14 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
                              : wsb + static_cast<int64_t>(wrow_of(64 * ((s_any ? wave : G::kXsWaves) - G::kXsWaves) + lane)) * (K / 32);
   const int s_dst = G::kXBytes + G::kWBytes +
                     (s_x ? 256 * wave : BMS * 4 + 256 * ((s_any ? wave : G::kXsWaves) - G::kXsWaves));
+  // extension slots: waves 0..3 copy one 8-row region each, wave 0 their
+  // scale words (lanes 0-31; the others repeat slot 31 into spare words)
+  const int xr = 8 * uwave + lane / 8;
+  const bool xt_ok = uwave < 4 && 8 * uwave < x_rows;
+  const bool xs_ok = uwave == 0 && x_rows > 0;
+  c += xt_ok + xs_ok;
+  const uint32_t xt_off = static_cast<uint32_t>(slot_src(BMS + xr)) * K + dma_chunk(xr, lane) * 16;
+  const uint8_t* xs_src = xs + static_cast<int64_t>(slot_src(BMS + min(lane, kXtRows - 1))) * (K / 32);
   auto dma = [&](int st, int kb) {
 #pragma unroll
     for (int i = 0; i < G::kXLoads; ++i)
@@ -343,6 +376,10 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
     for (int i = 0; i < 2; ++i)
       dma16(wb + (w_off[i] + kb * 64), &lds[st][G::kXBytes + (wave + 8 * i) * 1024]);
     if (s_any) dma4(s_src + kb * 4, &lds[st][s_dst]);
+    if (G::kExt) {
+      if (xt_ok) dma16(xq + (xt_off + kb * 128), &lds[st][G::kXtOff + uwave * 1024]);
+      if (xs_ok) dma4(xs_src + kb * 4, &lds[st][G::kXtOff + kXtRows * 128]);
+    }
   };
   // fragment rows: weights (A) and slots (B)
   int wrow[2], srow[G::kJ];
@@ -356,26 +393,41 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
   for (int f = 0; f < 2; ++f)
 #pragma unroll
     for (int j = 0; j < G::kJ; ++j) acc[f][j] = f32x16{};
+  f32x16 accx = f32x16{};
+  // every fragment is full whenever there are extension slots
   const int nj = min(G::kJ, max(0, (m_valid - wm * (BMS / 2) + 31) / 32));
+  // the ring, with the fragment count (and whether extension slots take
+  // part) fixed per instantiation
+  auto run = [&](auto nj_c, auto xt_c) {
+    constexpr int NJ = decltype(nj_c)::value;
+    constexpr bool XT = decltype(xt_c)::value;
 #pragma unroll
-  for (int s0 = 0; s0 < P; ++s0)
-    if (s0 < nk) dma(s0, s0);
-  ring_barrier(c * (min(P, nk) - 1));  // stage 0 landed
-  int st = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt+P goes to the buffer last read in step kt-1 (ended by a barrier)
-    const int kn = kt + P;
-    if (kn < nk) dma(st == 0 ? S - 1 : st - 1, kn);
-    switch (nj) {
-      case 4: stage_products<BMS, (G::kJ >= 4 ? 4 : G::kJ)>(&lds[st][0], acc, wrow, srow, half); break;
-      case 3: stage_products<BMS, (G::kJ >= 3 ? 3 : G::kJ)>(&lds[st][0], acc, wrow, srow, half); break;
-      case 2: stage_products<BMS, 2>(&lds[st][0], acc, wrow, srow, half); break;
-      case 1: stage_products<BMS, 1>(&lds[st][0], acc, wrow, srow, half); break;
-      default: break;
+    for (int s0 = 0; s0 < P; ++s0)
+      if (s0 < nk) dma(s0, s0);
+    ring_barrier(c * (min(P, nk) - 1));  // stage 0 landed
+    int st = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      // stage kt+P goes to the buffer last read in step kt-1 (ended by a barrier)
+      const int kn = kt + P;
+      if (kn < nk) dma(st == 0 ? S - 1 : st - 1, kn);
+      if (NJ > 0) stage_products<BMS, NJ, XT>(&lds[st][0], acc, accx, wrow, srow, half, wm);
+      ring_barrier(c * max(0, min(kn, nk - 1) - (kt + 1)));  // stage kt+1 landed
+      st = (st == S - 1) ? 0 : st + 1;
     }
-    ring_barrier(c * max(0, min(kn, nk - 1) - (kt + 1)));  // stage kt+1 landed
-    st = (st == S - 1) ? 0 : st + 1;
-  }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using IJ = std::integral_constant<int, G::kJ>;
+  using I3 = std::integral_constant<int, (G::kJ >= 3 ? 3 : 2)>;
+  using NoX = std::integral_constant<bool, false>;
+  using ExtX = std::integral_constant<bool, G::kExt>;
+  if (nj == G::kJ && x_rows > 0) run(IJ{}, ExtX{});
+  else if (nj == G::kJ) run(IJ{}, NoX{});
+  else if (nj == 3) run(I3{}, NoX{});
+  else if (nj == 2) run(I2{}, NoX{});
+  else if (nj == 1) run(I1{}, NoX{});
+  else run(I0{}, NoX{});
   // element q of acc[f][j]: channel row 8*(q/4) + 4*half + q%4 of fragment f,
   // slot row0 + wm*BMS/2 + 32 j + r; elements 4g .. 4g+3 are 4 consecutive
   // channels of the lane's slot.  A gate/up wave's 32 channels are one MXFP8
@@ -418,6 +470,50 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
             *reinterpret_cast<f32x4*>(static_cast<float*>(out) + static_cast<int64_t>(slot) * H + col) = v;
           }
         }
+      }
+    }
+  }
+  if (!G::kExt || x_rows == 0) return;
+  // extension slots: accx holds, for slot row0 + BMS + r, channel rows
+  // 8*(q/4) + 4*half + q%4 of the wave's fragment wm
+  const int slot = row0 + BMS + r;
+  if (MODE == kGateUp) {
+    // up values (wm = 1) reach the gate waves (wm = 0) of the same channels
+    // through LDS, at the same (wn, lane, q) position
+    float* ex = reinterpret_cast<float*>(&lds[0][0]);
+    __syncthreads();  // every wave is past its last read of the stages
+    if (wm == 1) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) ex[(wn * 64 + lane) * 16 + q] = accx[q];
+    }
+    __syncthreads();
+    if (wm == 0) {
+      float hv[16];
+      float m = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        hv[q] = silu(accx[q]) * ex[(wn * 64 + lane) * 16 + q];
+        m = fmaxf(m, fabsf(hv[q]));
+      }
+      m = fmaxf(m, __shfl_xor(m, 32));
+      const int x = mx8_exponent(m);
+      if (r < x_rows) {
+        uint8_t* hq = static_cast<uint8_t*>(out) + static_cast<int64_t>(slot) * I + nt * 128 + wn * 32;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<uint32_t*>(hq + 8 * g + 4 * half) =
+              e4m3x4(ldexpf(hv[4 * g], -x), ldexpf(hv[4 * g + 1], -x), ldexpf(hv[4 * g + 2], -x),
+                     ldexpf(hv[4 * g + 3], -x));
+        if (half == 0) out_scale[static_cast<int64_t>(slot) * (I / 32) + nt * 4 + wn] = static_cast<uint8_t>(x + 127);
+      }
+    }
+  } else if (r < x_rows) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int col = nt * BN + wn * 64 + wm * 32 + 8 * g + 4 * half;
+      if (col < H) {
+        const f32x4 v = {accx[4 * g], accx[4 * g + 1], accx[4 * g + 2], accx[4 * g + 3]};
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + static_cast<int64_t>(slot) * H + col) = v;
       }
     }
   }
@@ -464,10 +560,11 @@ hipError_t launch_experts_mxfp4(const Plan& p, const void* x, const uint8_t* w_g
 #define BEAM_MX_TILES(BMS, STAGES)                                                            \
   BEAM_LAUNCH(tm, "grouped_gate_up_mx", (mxg::grouped_gemm_mx<BMS, STAGES, mxg::kGateUp>),     \
               tile::grid_for(p, nt_gu), dim3(tile::kThreads), 0, s, xq, xs, w_gate_up,         \
-              s_gate_up, hq, hs, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_gu); \
+              s_gate_up, hq, hs, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_gu, \
+              p.xt);                                                                            \
   BEAM_LAUNCH(tm, "grouped_down_mx", (mxg::grouped_gemm_mx<BMS, STAGES, mxg::kDown>),          \
               tile::grid_for(p, nt_dn), dim3(tile::kThreads), 0, s, hq, hs, w_down, s_down, y, \
-              nullptr, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_dn)
+              nullptr, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_dn, p.xt)
     // measured on the Beam layer: 128-slot tiles (four stages) ahead below
     // 1K tokens; 256-slot tiles with three stages ahead at 1K-4K tokens
     // (2.38 vs 2.46 ms at 4K), with two at 8K (4.24 vs 4.36 ms)

@@ -98,18 +98,35 @@ def test_mxfp4_beam_8k_sampled():
     _check(inp, BEAM, rows, "mxfp4_8k sampled")
 
 
-@pytest.mark.parametrize("T", [3, 700, 2100])
+@pytest.mark.parametrize("T", [3, 700, 2100, 4300])
 def test_mxfp4_tile_forms_bitwise_equal(T):
-    # 128-slot tiles (4-stage ring) and 256-slot tiles (3-stage ring below
-    # T*K = 192E, 2-stage above: T = 2100 on this shape) add the same
-    # products in the same order and quantise h alike: equal bits
+    # 128-slot tiles (4-stage ring), 256-slot tiles (3-stage ring below
+    # T*K = 192E, 2-stage above: T = 2100 and 4300 on this shape) and, by
+    # default on the 2-stage form, last tiles extended by up to 32 slots add
+    # the same products in the same order and quantise h alike: equal bits
     sh = small_shape()
     inp = make_inputs(WORKLOADS["mxfp4_8k"], device=device(), tokens=T, shape=sh,
                       seed=900 + T, bias="skew:0.5:0,1,2,3,32,33,34,35")
     outs = []
-    for tile in (gl.TILE_128, gl.TILE_256):
+    for tile in (gl.TILE_128, gl.TILE_256, 0):
         d = desc_for(WORKLOADS["mxfp4_8k"], sh, gl.PATH_GROUPED | tile)
         outs.append(gl.forward(d, inp.x, inp.w_router, inp.bias, inp.w_gate_up, inp.w_down,
                                inp.s_gate_up, inp.s_down))
     torch.cuda.synchronize()
-    assert torch.equal(outs[0], outs[1])
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("T", [2100, 4300])
+def test_mxfp4_extended_last_tiles(T):
+    # 262 / 537 slots per expert on average, 2-stage 256-slot tiles: many
+    # experts end in a tile extended by 1..32 slots
+    sh = small_shape()
+    inp = make_inputs(WORKLOADS["mxfp4_8k"], device=device(), tokens=T, shape=sh, seed=950 + T)
+    _check(inp, sh, np.arange(0, T, 7), f"mxfp4 extended tiles T={T}")
+    d = desc_for(WORKLOADS["mxfp4_8k"], sh)
+    _, idx, _, _ = gl.forward(d, inp.x, inp.w_router, inp.bias, inp.w_gate_up, inp.w_down,
+                              inp.s_gate_up, inp.s_down, return_routing=True)
+    counts = torch.bincount(idx.flatten().long(), minlength=sh.n_experts).cpu()
+    ext = ((counts % 256 >= 1) & (counts % 256 <= 32) & (counts > 256)).sum().item()
+    print(f"experts whose last tile is extended: {ext} of {sh.n_experts}")
+    assert ext > 0

@@ -117,6 +117,19 @@ def test_beam_prefill_sampled(name):
     _check(inp, w.shape, desc_for(w, w.shape), rows, BF16_TOL, f"{name} sampled")
 
 
+def test_beam_max_tokens_sampled():
+    # the largest batch the boundary accepts for the Beam layer
+    # (T*K*max(H, I) < 2^31: T = 52,428), sampled rows including the last
+    w = WORKLOADS["prefill16k_skew"]
+    T = (2**31 - 1) // (BEAM.top_k * max(BEAM.hidden, BEAM.intermediate))
+    assert gl.validate(desc_for(w, BEAM), T) == gl.OK
+    assert gl.validate(desc_for(w, BEAM), T + 1) != gl.OK
+    inp = make_inputs(w, device=device(), tokens=T)
+    rows = np.sort(np.random.default_rng(5).choice(T, 12, replace=False))
+    rows[-1] = T - 1
+    _check(inp, BEAM, desc_for(w, BEAM), rows, BF16_TOL, f"Beam T={T} sampled")
+
+
 def test_forward_deterministic_and_permutation():
     sh = small_shape()
     w = WORKLOADS["prefill4k"]

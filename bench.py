@@ -214,7 +214,7 @@ def main():
     a = parse()
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported: "
-              "this build has no multi-GPU path (the block runs whole on one "
+              "the library has no multi-GPU path (the block runs whole on one "
               "MI355X).", file=sys.stderr)
         sys.exit(2)
     if a.calibrate_copy:

@@ -98,7 +98,9 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
   // bf16, 128 / 160 / 256 rows: 3.93 / 3.94 / 4.46 ms at 2K tokens, 4.20 /
   // 4.18 / 4.82 at 3K, 5.30 / 4.72 / 5.00 at 4K, 6.27 / 6.06 / 5.42 at 5K;
   // so 128 below T*K = 96E, 160 below 144E.  MXFP4, 128 / 256 rows: 1.57 /
-  // 1.61 ms at 1K tokens, 2.77 / 2.38 at 4K; so 128 below T*K = 32E.
+  // 1.61 ms at 1K tokens, 2.77 / 2.38 at 4K; so 128 below T*K = 32E.  FP8,
+  // 128 / 256 (+32) rows: 1.63 / 1.99 ms at 64 tokens, 2.28 / 2.60 at 2K,
+  // 2.76 / 2.93 at 3.5K, 3.31 / 3.02 at 4K; so 128 below T*K = 120E.
   p->bm = kGemmBM;
   if (p->wdt == BEAM_BF16) {
     if (p->flags & BEAM_TILE_128) p->bm = 128;
@@ -110,6 +112,9 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
     if (p->flags & BEAM_TILE_128) p->bm = 128;
     else if (p->flags & (BEAM_TILE_160 | BEAM_TILE_256)) p->bm = kGemmBM;
     else if (S < 32 * E) p->bm = 128;
+  } else if (p->wdt == BEAM_FP8_E4M3) {
+    if (p->flags & BEAM_TILE_128) p->bm = 128;
+    else if (!(p->flags & (BEAM_TILE_160 | BEAM_TILE_256)) && S < 120 * E) p->bm = 128;
   }
   // FP8, and MXFP4 where its 256-slot tiles run two stages (T*K >= 192E):
   // an expert's last tile takes up to 32 rows past 256, so experts near 256

@@ -103,11 +103,12 @@ struct FragAddr {
   uint32_t r_row_x;       // the same for the extension rows (tile rows 256..)
 };
 
-__device__ __forceinline__ FragAddr frag_addr(int wm, int wn, int lane) {
+// wrows: A rows per wave along M (128, or 64 in the 128-row tiles).
+__device__ __forceinline__ FragAddr frag_addr(int wm, int wn, int lane, int wrows = 128) {
   FragAddr fa;
   const int l = lane % 32;
   const int key = (l ^ (l >> 3)) & 7;
-  fa.a_row = static_cast<uint32_t>(wm * 128 + l) * kRowBytes;
+  fa.a_row = static_cast<uint32_t>(wm * wrows + l) * kRowBytes;
   fa.b_row = static_cast<uint32_t>(wn * 64 + l) * kRowBytes;
   fa.x_row = static_cast<uint32_t>(l) * kRowBytes;
 #pragma unroll
@@ -115,7 +116,7 @@ __device__ __forceinline__ FragAddr frag_addr(int wm, int wn, int lane) {
 #pragma unroll
     for (int f = 0; f < 2; ++f)
       fa.p[j][f] = static_cast<uint32_t>((((2 * (lane / 32) + j) ^ key) ^ (4 * f)) << 4);
-  fa.r_row = static_cast<uint32_t>(wm * 128 + 4 * (lane / 32)) * 4;
+  fa.r_row = static_cast<uint32_t>(wm * wrows + 4 * (lane / 32)) * 4;
   fa.r_row_x = static_cast<uint32_t>(BM + 4 * (lane / 32)) * 4;
   return fa;
 }
@@ -510,6 +511,231 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
   }
 }
 
+// ---- 128-row tiles with a ring of three copy stages --------------------------
+// For batches whose experts hold few rows the e4m3 products are bound by the
+// weight bytes.  As in the bf16 128-row form, 128 x 256 tiles are copied
+// through a ring of three stages (two in flight while one is consumed),
+// each wave issuing the same count of copies per stage so that a stage's
+// arrival is a count of outstanding copies.  The per-128 scale words travel
+// in the same copies (no global load sits in the loop, whose wait would
+// drain the ring): stage kt's buffer also holds s_a of the tile's rows and
+// the two s_w words of block kt+1, from which the factors of block kt+1 are
+// formed during stage kt.  8 waves of 64 x 64.
+namespace small8 {
+
+constexpr int BMS = 128;
+constexpr int kABytes = BMS * kRowBytes;             // 16 KiB
+constexpr int kSaOff = kABytes + kTileBytes;         // s_a words of the tile's rows
+constexpr int kSwOff = kSaOff + BMS * 4;             // s_w words (2 used)
+constexpr int kStage = kSwOff + 256;                 // 49,920 bytes
+constexpr int kStages = 3;
+constexpr int kALoads = kABytes / (16 * kThreads);   // 2
+typedef unsigned char Ring[kStages][kStage];
+
+template <int NF>
+__device__ __forceinline__ float mainloop(
+    const uint8_t* __restrict__ a_src, const uint32_t* a_off, const bool* a_ok, int c,
+    const uint8_t* __restrict__ wb, const uint32_t* b_off, const float* sc_src, bool sc_wave,
+    int sc_dst, float s0, int nkb, Ring& ring, float (&rsc)[2][2][BMS], int blk, int srow,
+    f32x16 (&acc)[4][2], const FragAddr& fa, int wn) {
+  const int wave = threadIdx.x / kWave;
+  f32x16 accx = {};
+  auto dma = [&](int st, int kb) {
+#pragma unroll
+    for (int i = 0; i < kALoads; ++i)
+      if (a_ok[i]) dma16(a_src + (a_off[i] + kb * 128), &ring[st][(wave + 8 * i) * 1024]);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+      dma16(wb + (b_off[i] + kb * 128), &ring[st][kABytes + (wave + 8 * i) * 1024]);
+    // scale words of block kb+1 (the last stage repeats block nkb-1)
+    if (sc_wave) dma4(sc_src + min(kb + 1, nkb - 1), &ring[st][sc_dst]);
+  };
+  rsc[0][blk][srow] = 1.0f;
+  float s_prev = s0;
+#pragma unroll
+  for (int k0 = 0; k0 < 2; ++k0)
+    if (k0 < nkb) dma(k0, k0);
+  ring_barrier(c * (min(2, nkb) - 1));  // stage 0 landed, rsc[0] written
+  int st = 0;
+  for (int kt = 0; kt < nkb; ++kt) {
+    const int kn = kt + 2;
+    if (kn < nkb) dma(st == 0 ? 2 : st - 1, kn);  // the buffer read in step kt-1
+    if (NF > 0)
+      fp8_stage<NF, false>(&ring[st][0], &ring[st][kABytes], nullptr, &rsc[kt & 1][wn / 2][0],
+                           acc, accx, 0, fa);
+    __builtin_amdgcn_sched_barrier(0);
+    // factors of block kt+1 from this stage's scale words; rsc[(kt+1) & 1]
+    // was last read in step kt-1
+    const float* sa = reinterpret_cast<const float*>(&ring[st][kSaOff]);
+    const float* sw = reinterpret_cast<const float*>(&ring[st][kSwOff]);
+    const float s = sa[srow] * sw[blk];
+    rsc[(kt + 1) & 1][blk][srow] = s_prev / s;
+    s_prev = (kt + 1 < nkb) ? s : s_prev;
+    ring_barrier(c * max(0, min(kn, nkb - 1) - (kt + 1)));  // stage kt+1 landed
+    st = (st == 2) ? 0 : st + 1;
+  }
+  return s_prev;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_fp8_small(
+    const uint8_t* __restrict__ a_src, const float* __restrict__ a_scale,
+    const uint8_t* __restrict__ w, const float* __restrict__ w_scale, void* __restrict__ out,
+    float* __restrict__ out_scale, const int32_t* __restrict__ slot_token,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ meta, int E, int H, int I,
+    int n_nt) {
+  __shared__ __attribute__((aligned(16))) Ring ring;
+  __shared__ __attribute__((aligned(16))) float rsc[2][2][BMS];
+
+  Coords tc;
+  if (!tile_coords(counts, offsets, tile_off, meta, E, n_nt, tc, BMS)) return;
+  const int e = tc.e, nt = tc.nt, row0 = tc.row0, row_end = tc.row_end;
+  const int K = (MODE == kGateUp) ? H : I;
+  const int nkb = K / 128;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int uwave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy
+  const int wm = wave / 4, wn = wave % 4;
+  const int m_valid = min(BMS, row_end - row0);
+  const uint8_t* wb = w + static_cast<int64_t>(e) * ((MODE == kGateUp) ? 2 * I : H) * K;
+  auto arow_of = [&](int t) {  // activation row of tile row t (padding rows: a valid one)
+    const int sl = min(row0 + t, row_end - 1);
+    return (MODE == kGateUp) ? slot_token[sl] : sl;
+  };
+  const int nrb = (MODE == kGateUp) ? 2 * I / 128 : H / 128;
+  auto wblock_of = [&](int b) {
+    return (MODE == kGateUp) ? (b == 0 ? nt : I / 128 + nt) : min(2 * nt + b, nrb - 1);
+  };
+  uint32_t a_off[kALoads], b_off[kLoads];
+  bool a_ok[kALoads];
+  int c = kLoads;  // copies per stage: B regions, valid A regions, scale words
+#pragma unroll
+  for (int i = 0; i < kALoads; ++i) {
+    const int r = dma_row(wave, lane, i);
+    a_ok[i] = 8 * (uwave + 8 * i) < m_valid;  // the region's first row is valid
+    c += a_ok[i];
+    a_off[i] = static_cast<uint32_t>(arow_of(r)) * K + dma_chunk(r, lane) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int r = dma_row(wave, lane, i);
+    const int wrow = (MODE == kGateUp) ? ((r < 128) ? nt * 128 + r : I + nt * 128 + (r - 128))
+                                       : min(nt * BN + r, H - 1);
+    b_off[i] = static_cast<uint32_t>(wrow) * K + dma_chunk(r, lane) * 16;
+  }
+  // scale words: waves 0-1 s_a of tile rows 64 w + lane, wave 2 s_w of the
+  // two weight blocks (lanes 0-1; the others repeat block 1 into spare words)
+  const bool sc_wave = uwave < 3;
+  c += sc_wave;
+  const float* sc_src = (wave < 2)
+      ? a_scale + static_cast<int64_t>(arow_of(64 * wave + lane)) * nkb
+      : w_scale + (static_cast<int64_t>(e) * nrb + wblock_of(min(lane, 1))) * nkb;
+  const int sc_dst = (wave < 2) ? kSaOff + 256 * wave : kSwOff;
+  // scale items: threads 0..255 (weight block tid / 128, tile row tid % 128);
+  // threads 256.. repeat them
+  const int blk = (tid % 256) / BMS, srow = tid % BMS;
+  const float s0 = a_scale[static_cast<int64_t>(arow_of(srow)) * nkb] *
+                   w_scale[(static_cast<int64_t>(e) * nrb + wblock_of(blk)) * nkb];
+
+  const FragAddr fa = frag_addr(wm, wn, lane, 64);
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) acc[i][n] = f32x16{};
+  const int nf = min(2, max(0, (m_valid - wm * 64 + 31) / 32));
+  float s_last;
+  switch (nf) {
+    case 2: s_last = mainloop<2>(a_src, a_off, a_ok, c, wb, b_off, sc_src, sc_wave, sc_dst, s0, nkb, ring, rsc, blk, srow, acc, fa, wn); break;
+    case 1: s_last = mainloop<1>(a_src, a_off, a_ok, c, wb, b_off, sc_src, sc_wave, sc_dst, s0, nkb, ring, rsc, blk, srow, acc, fa, wn); break;
+    default: s_last = mainloop<0>(a_src, a_off, a_ok, c, wb, b_off, sc_src, sc_wave, sc_dst, s0, nkb, ring, rsc, blk, srow, acc, fa, wn); break;
+  }
+
+  // ---- epilogue: last block's scale, then store ---------------------------
+  rsc[0][blk][srow] = s_last;  // rsc is no longer read by the main loop
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    if (i < nf) scale_rows(acc, i, &rsc[0][wn / 2][0], fa);
+
+  if (MODE == kGateUp) {
+    // up values, fp32, [128 rows][128 channels] in the ring buffers
+    float* ex = reinterpret_cast<float*>(&ring[0][0]);
+    if (wn >= 2) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (i >= nf) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = wm * 64 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+#pragma unroll
+          for (int n = 0; n < 2; ++n)
+            ex[rl * 128 + (wn - 2) * 64 + n * 32 + lane % 32] = acc[i][n][r];
+        }
+      }
+    }
+    __syncthreads();
+    // h = bf16(silu(g) * u), written over the up value it was made from
+    if (wn < 2) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (i >= nf) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = wm * 64 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+#pragma unroll
+          for (int n = 0; n < 2; ++n) {
+            const int at = rl * 128 + wn * 64 + n * 32 + lane % 32;
+            const float h = silu(acc[i][n][r]) * ex[at];
+            ex[at] = __uint_as_float(static_cast<uint32_t>(f32_to_bf16_bits(h)) << 16);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // 16 lanes per row, 8 channels each; amax over the row's 16 lanes
+    uint8_t* hq = static_cast<uint8_t*>(out);
+#pragma unroll 1
+    for (int rl = tid / 16; rl < BMS; rl += kThreads / 16) {
+      const int c8 = 8 * (tid % 16);
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(&ex[rl * 128 + c8]);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(&ex[rl * 128 + c8 + 4]);
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(v0[j]), fabsf(v1[j])));
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      const float sc = (m > 0.0f) ? m / 448.0f : 1.0f;
+      const uint32_t lo = e4m3x4(v0[0] / sc, v0[1] / sc, v0[2] / sc, v0[3] / sc);
+      const uint32_t hi = e4m3x4(v1[0] / sc, v1[1] / sc, v1[2] / sc, v1[3] / sc);
+      if (row0 + rl < row_end) {
+        const int64_t row = row0 + rl;
+        *reinterpret_cast<uint2*>(hq + row * I + nt * 128 + c8) = make_uint2(lo, hi);
+        if (tid % 16 == 0) out_scale[row * (I / 128) + nt] = sc;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (i >= nf) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + wm * 64 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+        if (row >= row_end) continue;
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const int col = nt * BN + wn * 64 + n * 32 + lane % 32;
+          if (col < H)
+            static_cast<uint16_t*>(out)[static_cast<int64_t>(row) * H + col] =
+                f32_to_bf16_bits(acc[i][n][r]);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace small8
+
 }  // namespace
 
 // x -> e4m3 (per token, per 128 channels); gate/up GEMM with SwiGLU, h
@@ -533,6 +759,15 @@ hipError_t launch_experts_fp8(const Plan& p, const void* x,
   if (e != hipSuccess) return e;
   const int nt_gu = p.I / 128;
   const int nt_dn = static_cast<int>(ceil_div(p.H, BN));
+  if (p.bm == small8::BMS) {
+    BEAM_LAUNCH(tm, "gate_up_fp8", small8::grouped_gemm_fp8_small<kGateUp>, grid_for(p, nt_gu),
+                dim3(kThreads), 0, s, xq, xs, w_gate_up, s_gate_up, hq, hs, slot_token, counts,
+                offsets, toff, meta, p.E, p.H, p.I, nt_gu);
+    BEAM_LAUNCH(tm, "down_fp8", small8::grouped_gemm_fp8_small<kDown>, grid_for(p, nt_dn),
+                dim3(kThreads), 0, s, hq, hs, w_down, s_down, y, nullptr, slot_token, counts,
+                offsets, toff, meta, p.E, p.H, p.I, nt_dn);
+    return hipGetLastError();
+  }
   BEAM_LAUNCH(tm, "gate_up_fp8", grouped_gemm_fp8<kGateUp>, grid_for(p, nt_gu),
               dim3(kThreads), 0, s, xq, xs, w_gate_up, s_gate_up, hq, hs, slot_token,
               counts, offsets, toff, meta, p.E, p.H, p.I, nt_gu, p.xt);

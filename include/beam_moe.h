@@ -70,17 +70,18 @@ typedef enum {
 /* Expert path (default: bf16 streams its weights below T*K = E/2 and uses
  * grouped tiles above; MXFP4 and FP8 use grouped tiles; fp32 has one path).
  * Tile height of the grouped path (default: bf16 128 rows below T*K = 96E,
- * 160 below 144E, 256 above; MXFP4 128 below 32E, 256 above; FP8 256, an
- * expert's last tile holding up to 288).  Every tile
+ * 160 below 144E, 256 above; MXFP4 128 below 32E, 256 above; FP8 128 below
+ * 120E, 256 above, an expert's last tile holding up to 288).  Every tile
  * height gives bit-identical outputs; the two paths agree within the layer
  * tolerance (they sum in different orders, and bf16 streaming keeps y in
  * fp32).  The flags exist for measurement and tests. */
 #define BEAM_PATH_STREAM (1u << 1)     /* force the weight-streaming expert path (bf16, MXFP4) */
 #define BEAM_PATH_GROUPED (1u << 2)    /* force the tiled grouped-GEMM expert path */
-#define BEAM_TILE_128 (1u << 3)        /* bf16 / MXFP4 grouped path: force 128-row M tiles */
+#define BEAM_TILE_128 (1u << 3)        /* grouped path: force 128-row M tiles */
 #define BEAM_TILE_256 (1u << 4)        /* grouped path: force 256-row M tiles (FP8: no 32-row
                                           extension of an expert's last tile) */
-#define BEAM_TILE_160 (1u << 5)        /* bf16 grouped path: force 160-row M tiles (MXFP4: 256) */
+#define BEAM_TILE_160 (1u << 5)        /* bf16 grouped path: force 160-row M tiles (MXFP4 and
+                                          FP8: the 256-row form) */
 
 typedef struct {
   int32_t hidden;           /* H: 5120 for Beam */

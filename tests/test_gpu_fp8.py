@@ -100,3 +100,19 @@ def test_fp8_extended_last_tiles(T, hidden):
     print(f"experts whose last tile is extended: {ext} of {sh.n_experts}")
     assert ext > 0
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("T,hidden,skew", [(5, 256, False), (300, 256, False),
+                                           (700, 384, True), (2100, 512, False)])
+def test_fp8_128_row_tiles(T, hidden, skew):
+    # 128-row tiles with the three-stage copy ring: one, two and several
+    # tiles per expert, partial last tiles, a 256-wide down tile half outside
+    # H (H = 384); against the oracle and bit-identical to the 256-row form
+    sh = small_shape(hidden=hidden, intermediate=384 if hidden == 384 else 256)
+    inp = make_inputs(WORKLOADS["fp8_8k"], device=device(), tokens=T, shape=sh,
+                      seed=80 + T + hidden,
+                      bias="skew:0.5:0,1,2,3,32,33,34,35" if skew else None)
+    rows = np.arange(0, T, max(1, T // 300))
+    a, _ = _check(inp, sh, rows, f"fp8 128-row tiles T={T} H={hidden}", gl.TILE_128)
+    b, _ = _check(inp, sh, rows, f"fp8 256-row tiles T={T} H={hidden}", gl.TILE_256)
+    assert torch.equal(a, b)

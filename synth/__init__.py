@@ -77,6 +77,8 @@ WORKLOADS = {
     "prefill16k_skew": Workload("prefill16k_skew", 16384, BEAM, BF16, BF16,
                                 "skew:0.5:0,1,2,3,32,33,34,35", 3),
     "fp8_8k": Workload("fp8_8k", 8192, BEAM, BF16, FP8, "zero", 4),
+    # decode batch on the FP8 weights (the 128-row tiles with a copy ring)
+    "fp8_decode64": Workload("fp8_decode64", 64, BEAM, BF16, FP8, "zero", 8),
     # the per-GPU share of an expert-parallel layer (32 local experts)
     "ep8_share16k": Workload("ep8_share16k", 16384, EP8_SHARE, BF16, BF16, "zero", 7),
     # the 4-bit checkpoint form (MXFP4 stands in for the pages' NVFP4)

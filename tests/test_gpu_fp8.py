@@ -71,6 +71,13 @@ def test_fp8_beam_sampled():
     _check(inp, BEAM, rows, "fp8_8k sampled")
 
 
+def test_fp8_decode64():
+    # the Beam layer at 64 tokens: 128-row tiles with the three-stage copy
+    # ring, one to a few rows per expert; every row against the oracle
+    inp = inputs("fp8_decode64")
+    _check(inp, BEAM, np.arange(64), "fp8_decode64")
+
+
 @pytest.mark.parametrize("T", [300, 700])
 def test_fp8_odd_widths_skewed(T):
     # hidden and intermediate multiples of 128 but not of 256 (the last

@@ -233,14 +233,22 @@ using namespace tile;
 // slots past the 256: their activation rows and scale words get an area of
 // their own after each stage's tiles.
 constexpr int kXtRows = 32;
-template <int BMS, int STAGES>
+// PER (K a multiple of 512): the weight tile's E8M0 bytes do not travel in
+// the stages, 4 bytes of each of its 256 rows per stage (256 scattered
+// cache lines for 1 KiB), but in periods of kPer stages: 16 bytes of a row,
+// a quarter of the rows with each stage, into a ring of kPerSlots period
+// buffers after the stages (row-major, 16 bytes per row).
+constexpr int kPer = 4;
+constexpr int kPerSlots = 3;
+template <int BMS, int STAGES, bool PER>
 struct Geo {
   static constexpr int kXBytes = BMS * 128;  // activation tile per stage
   static constexpr int kWBytes = BN * 64;    // weight tile per stage
-  static constexpr int kXtOff = kXBytes + kWBytes + (BMS + BN) * 4;
+  static constexpr int kXtOff = kXBytes + kWBytes + (BMS + (PER ? 0 : BN)) * 4;
   static constexpr bool kExt = STAGES == 2;  // room for extension slots
   static constexpr int kStage = kXtOff + (kExt ? kXtRows * 128 + 256 : 0);
   static constexpr int kStages = STAGES;
+  static constexpr int kPerBytes = PER ? kPerSlots * BN * 16 : 0;
   static constexpr int kXLoads = kXBytes / (16 * tile::kThreads);  // 4 or 2
   static constexpr int kXsWaves = BMS / 64;  // waves copying activation scale words
   static constexpr int kJ = BMS / 64;        // 32-slot fragments per wave
@@ -254,17 +262,17 @@ enum Mode { kGateUp = 0, kDown = 1 };
 
 // XT: also the extension slots (B rows of the extension area) against the
 // wave's A fragment wm into accx (gate channels for wm = 0, up channels for
-// wm = 1 on gate/up; output columns wn*64 + wm*32 .. on down).
-template <int BMS, int NJ, bool XT>
-__device__ __forceinline__ void stage_products(const unsigned char* st,
+// wm = 1 on gate/up; output columns wn*64 + wm*32 .. on down).  WS: the
+// stage's scale word of weight row t at WS[t * (PER ? 4 : 1)].
+template <int BMS, int NJ, bool XT, bool PER>
+__device__ __forceinline__ void stage_products(const unsigned char* st, const uint32_t* WS,
                                                f32x16 (&acc)[2][BMS / 64], f32x16& accx,
                                                const int* wrow, const int* srow, int half,
                                                int wm) {
-  using G = Geo<BMS, 2>;
+  using G = Geo<BMS, 2, PER>;
   const unsigned char* X = st;
   const unsigned char* W = st + G::kXBytes;
   const uint32_t* XS = reinterpret_cast<const uint32_t*>(st + G::kXBytes + G::kWBytes);
-  const uint32_t* WS = XS + BMS;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     u32x4 a[2];
@@ -272,7 +280,7 @@ __device__ __forceinline__ void stage_products(const unsigned char* st,
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
       a[f] = *reinterpret_cast<const u32x4*>(W + wswz(wrow[f], 2 * ks + half));
-      sa[f] = (WS[wrow[f]] >> (8 * (2 * ks + half))) & 0xFFu;
+      sa[f] = (WS[wrow[f] * (PER ? 4 : 1)] >> (8 * (2 * ks + half))) & 0xFFu;
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -285,7 +293,7 @@ __device__ __forceinline__ void stage_products(const unsigned char* st,
       for (int f = 0; f < 2; ++f) acc[f][j] = mfma_mx(a[f], b0, b1, acc[f][j], sa[f], sb);
     }
     if (XT) {
-      const unsigned char* XX = st + Geo<BMS, 2>::kXtOff;
+      const unsigned char* XX = st + G::kXtOff;
       const uint32_t* XXS = reinterpret_cast<const uint32_t*>(XX + kXtRows * 128);
       const int row = srow[0] % 32;  // the lane's extension slot
       const int key = (row ^ (row >> 3)) & 7;
@@ -297,7 +305,7 @@ __device__ __forceinline__ void stage_products(const unsigned char* st,
   }
 }
 
-template <int BMS, int STAGES, int MODE>
+template <int BMS, int STAGES, int MODE, bool PER>
 __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
     const uint8_t* __restrict__ xq,      // gate/up: xq [T,H]; down: hq [S,I]  (E4M3)
     const uint8_t* __restrict__ xs,      // their E8M0 bytes [rows, K/32]
@@ -308,9 +316,12 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
     const int32_t* __restrict__ slot_token, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off,
     const int32_t* __restrict__ meta, int E, int H, int I, int n_nt, int xt) {
-  using G = Geo<BMS, STAGES>;
+  using G = Geo<BMS, STAGES, PER>;
   constexpr int S = G::kStages, P = S - 1;  // ring size, stages in flight
-  __shared__ __attribute__((aligned(16))) unsigned char lds[S][G::kStage];
+  // the stages, then (PER) the period buffers: one object, so the compiler
+  // sees the copies and the reads of both as one array
+  __shared__ __attribute__((aligned(16))) unsigned char lds[S * G::kStage + G::kPerBytes];
+  constexpr int kPerOff = S * G::kStage;
   Coords tc;
   if (!tile_coords(counts, offsets, tile_off, meta, E, n_nt, tc, BMS)) return;
   const int e = tc.e, nt = tc.nt, row0 = tc.row0, row_end = tc.row_end;
@@ -354,7 +365,9 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
     const int ch = (lane % 4) ^ ((t >> 2) & 3);
     w_off[i] = static_cast<uint32_t>(wrow_of(t)) * (K / 2) + ch * 16;
   }
-  const bool s_x = uwave < G::kXsWaves, s_any = uwave < G::kXsWaves + 4;
+  // PER: wave kXsWaves alone copies the weight scale bytes, 16 bytes of 64
+  // rows per stage
+  const bool s_x = uwave < G::kXsWaves, s_any = uwave < G::kXsWaves + (PER ? 1 : 4);
   c += s_any;
   const uint8_t* s_src = s_x ? xs + static_cast<int64_t>(slot_src(64 * wave + lane)) * (K / 32)
                              : wsb + static_cast<int64_t>(wrow_of(64 * ((s_any ? wave : G::kXsWaves) - G::kXsWaves) + lane)) * (K / 32);
@@ -368,18 +381,38 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
   c += xt_ok + xs_ok;
   const uint32_t xt_off = static_cast<uint32_t>(slot_src(BMS + xr)) * K + dma_chunk(xr, lane) * 16;
   const uint8_t* xs_src = xs + static_cast<int64_t>(slot_src(BMS + min(lane, kXtRows - 1))) * (K / 32);
+  // PER: with stage kb travel the bytes of period q = kb/kPer + 1 (stages
+  // kPer*q ..) of rows 64 g + lane, g = kb % kPer, into buffer q % kPerSlots.
+  // That buffer last held period q - 3, read up to stage kPer*(q-2) - 1,
+  // before the step that issues stage kb (kb - P >= kPer*(q-2), P <= kPer);
+  // periods past the last copy its bytes again into a free buffer.
+  const int nper = nk / kPer;
+  auto per_src = [&](int g, int q) {
+    return wsb + (static_cast<uint32_t>(wrow_of(64 * g + lane)) * (K / 32) + 16 * min(q, nper - 1));
+  };
+  auto per_dst = [&](int g, int q) { return &lds[kPerOff + (q % kPerSlots) * (BN * 16) + g * 1024]; };
   auto dma = [&](int st, int kb) {
+    unsigned char* sb = &lds[st * G::kStage];
 #pragma unroll
     for (int i = 0; i < G::kXLoads; ++i)
-      if (x_ok[i]) dma16(xq + (x_off[i] + kb * 128), &lds[st][dma_row(wave, 0, i) * 128]);
+      if (x_ok[i]) dma16(xq + (x_off[i] + kb * 128), sb + dma_row(wave, 0, i) * 128);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      dma16(wb + (w_off[i] + kb * 64), &lds[st][G::kXBytes + (wave + 8 * i) * 1024]);
-    if (s_any) dma4(s_src + kb * 4, &lds[st][s_dst]);
-    if (G::kExt) {
-      if (xt_ok) dma16(xq + (xt_off + kb * 128), &lds[st][G::kXtOff + uwave * 1024]);
-      if (xs_ok) dma4(xs_src + kb * 4, &lds[st][G::kXtOff + kXtRows * 128]);
+      dma16(wb + (w_off[i] + kb * 64), sb + G::kXBytes + (wave + 8 * i) * 1024);
+    if (s_any) {
+      if (PER && !s_x) dma16(per_src(kb % kPer, kb / kPer + 1), per_dst(kb % kPer, kb / kPer + 1));
+      else dma4(s_src + kb * 4, sb + s_dst);
     }
+    if (G::kExt) {
+      if (xt_ok) dma16(xq + (xt_off + kb * 128), sb + G::kXtOff + uwave * 1024);
+      if (xs_ok) dma4(xs_src + kb * 4, sb + G::kXtOff + kXtRows * 128);
+    }
+  };
+  // scale words of weight row t at stage kb: WS(kb, st)[t * (PER ? 4 : 1)]
+  auto ws_of = [&](int kb, int st) {
+    return PER ? reinterpret_cast<const uint32_t*>(
+                     &lds[kPerOff + ((kb / kPer) % kPerSlots) * (BN * 16)]) + kb % kPer
+               : reinterpret_cast<const uint32_t*>(&lds[st * G::kStage + G::kXBytes + G::kWBytes]) + BMS;
   };
   // fragment rows: weights (A) and slots (B)
   int wrow[2], srow[G::kJ];
@@ -401,6 +434,11 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
   auto run = [&](auto nj_c, auto xt_c) {
     constexpr int NJ = decltype(nj_c)::value;
     constexpr bool XT = decltype(xt_c)::value;
+    // period 0 of the weight scale bytes, ahead of stage 0's copies
+    if (PER && s_any && !s_x) {
+#pragma unroll
+      for (int g = 0; g < kPer; ++g) dma16(per_src(g, 0), per_dst(g, 0));
+    }
 #pragma unroll
     for (int s0 = 0; s0 < P; ++s0)
       if (s0 < nk) dma(s0, s0);
@@ -410,7 +448,9 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
       // stage kt+P goes to the buffer last read in step kt-1 (ended by a barrier)
       const int kn = kt + P;
       if (kn < nk) dma(st == 0 ? S - 1 : st - 1, kn);
-      if (NJ > 0) stage_products<BMS, NJ, XT>(&lds[st][0], acc, accx, wrow, srow, half, wm);
+      if (NJ > 0)
+        stage_products<BMS, NJ, XT, PER>(&lds[st * G::kStage], ws_of(kt, st), acc, accx, wrow,
+                                         srow, half, wm);
       ring_barrier(c * max(0, min(kn, nk - 1) - (kt + 1)));  // stage kt+1 landed
       st = (st == S - 1) ? 0 : st + 1;
     }
@@ -480,7 +520,7 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
   if (MODE == kGateUp) {
     // up values (wm = 1) reach the gate waves (wm = 0) of the same channels
     // through LDS, at the same (wn, lane, q) position
-    float* ex = reinterpret_cast<float*>(&lds[0][0]);
+    float* ex = reinterpret_cast<float*>(&lds[0]);
     __syncthreads();  // every wave is past its last read of the stages
     if (wm == 1) {
 #pragma unroll
@@ -557,14 +597,21 @@ hipError_t launch_experts_mxfp4(const Plan& p, const void* x, const uint8_t* w_g
     const int32_t* toff = ws_at<int32_t>(ws, p.off_tile_off);
     const int nt_gu = p.I / 128;
     const int nt_dn = static_cast<int>(ceil_div(p.H, tile::BN));
-#define BEAM_MX_TILES(BMS, STAGES)                                                            \
-  BEAM_LAUNCH(tm, "grouped_gate_up_mx", (mxg::grouped_gemm_mx<BMS, STAGES, mxg::kGateUp>),     \
+#define BEAM_MX_GATE_UP(BMS, STAGES, PER)                                                     \
+  BEAM_LAUNCH(tm, "grouped_gate_up_mx", (mxg::grouped_gemm_mx<BMS, STAGES, mxg::kGateUp, PER>), \
               tile::grid_for(p, nt_gu), dim3(tile::kThreads), 0, s, xq, xs, w_gate_up,         \
               s_gate_up, hq, hs, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_gu, \
-              p.xt);                                                                            \
-  BEAM_LAUNCH(tm, "grouped_down_mx", (mxg::grouped_gemm_mx<BMS, STAGES, mxg::kDown>),          \
+              p.xt)
+#define BEAM_MX_DOWN(BMS, STAGES, PER)                                                        \
+  BEAM_LAUNCH(tm, "grouped_down_mx", (mxg::grouped_gemm_mx<BMS, STAGES, mxg::kDown, PER>),     \
               tile::grid_for(p, nt_dn), dim3(tile::kThreads), 0, s, hq, hs, w_down, s_down, y, \
               nullptr, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_dn, p.xt)
+    // weight scale bytes in periods of four stages when K % 512 == 0
+#define BEAM_MX_TILES(BMS, STAGES)                                                            \
+  if (p.H % 512 == 0) BEAM_MX_GATE_UP(BMS, STAGES, true);                                      \
+  else BEAM_MX_GATE_UP(BMS, STAGES, false);                                                    \
+  if (p.I % 512 == 0) BEAM_MX_DOWN(BMS, STAGES, true);                                         \
+  else BEAM_MX_DOWN(BMS, STAGES, false)
     // measured on the Beam layer: 128-slot tiles (four stages) ahead below
     // 1K tokens; 256-slot tiles with three stages ahead at 1K-4K tokens
     // (2.38 vs 2.46 ms at 4K), with two at 8K (4.24 vs 4.36 ms)
@@ -576,6 +623,8 @@ hipError_t launch_experts_mxfp4(const Plan& p, const void* x, const uint8_t* w_g
       BEAM_MX_TILES(256, 2);
     }
 #undef BEAM_MX_TILES
+#undef BEAM_MX_GATE_UP
+#undef BEAM_MX_DOWN
     return hipGetLastError();
   }
   BEAM_LAUNCH(tm, "stream_gate_up_mx", stream_gate_up_mx,

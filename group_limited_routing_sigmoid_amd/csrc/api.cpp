@@ -159,8 +159,11 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
     p->off_hs = take(S * (I / 32));
   }
   if (p->wdt == BEAM_FP8_E4M3) {
+    // x's scales per token, then per slot and block-major ([H/128][S]), as
+    // are h's ([I/128][S]): a tile stage reads the words of consecutive slots
     p->off_xq = take(T * H);
     p->off_xs = take(T * (H / 128) * 4);
+    p->off_xss = take(S * (H / 128) * 4);
     p->off_hq = take(S * I);
     p->off_hs = take(S * (I / 128) * 4);
   }

@@ -71,6 +71,23 @@ bool fp8_experts_built() { return true; }
 
 namespace {
 
+// x's activation scales by slot, block-major: xss[kb * S + slot] =
+// xs[slot_token[slot] * nkb + kb], so that a tile stage of the grouped
+// products reads the scale words of consecutive slots (one 1 KiB run per
+// 256 rows rather than a cache line per row).
+__global__ __launch_bounds__(256) void slot_scales_fp8(const float* __restrict__ xs,
+                                                       const int32_t* __restrict__ slot_token,
+                                                       float* __restrict__ xss, int S, int nkb) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(S) * nkb) return;
+  const int64_t kb = i / S, slot = i % S;
+  xss[i] = xs[static_cast<int64_t>(slot_token[slot]) * nkb + kb];
+}
+
+}  // namespace
+
+namespace {
+
 using namespace tile;
 
 enum Mode { kGateUp = 0, kDown = 1 };
@@ -203,9 +220,10 @@ __device__ __forceinline__ void fp8_stage(const unsigned char* at, const unsigne
 // for threads 0..63 also an extension row (tid / 32, 256 + tid % 32) (the
 // others repeat their first item).  s_last receives the items' last s.
 struct ScaleItems {
-  const float* sa[2];  // s_a of the item's row, one word per block
-  const float* sw[2];  // s_w of the item's weight block
+  const float* sa[2];  // s_a of the item's slot at block 0; block kb at kb * S
+  const float* sw[2];  // s_w of the item's weight block, one word per block
   int blk[2], row[2];
+  int S;
 };
 
 template <int NF, bool XT>
@@ -231,7 +249,7 @@ __device__ __forceinline__ void fp8_mainloop(
   for (int j = 0; j < NI; ++j) {
     s_prev[j] = it.sa[j][0] * it.sw[j][0];
     // factors of stage 1, loaded a stage ahead of their use
-    sa_n[j] = it.sa[j][min(1, nkb - 1)];
+    sa_n[j] = it.sa[j][min(1, nkb - 1) * it.S];
     sw_n[j] = it.sw[j][min(1, nkb - 1)];
     rsc[0][it.blk[j]][it.row[j]] = 1.0f;
   }
@@ -246,7 +264,7 @@ __device__ __forceinline__ void fp8_mainloop(
     float sa2[NI], sw2[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      sa2[j] = it.sa[j][k2];
+      sa2[j] = it.sa[j][k2 * it.S];
       sw2[j] = it.sw[j][k2];
     }
     // no branch from here to the barrier, so the compiler keeps the
@@ -284,14 +302,14 @@ __device__ __forceinline__ void fp8_mainloop(
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
     const uint8_t* __restrict__ a_src,   // gate/up: xq [T,H]; down: hq [S,I]
-    const float* __restrict__ a_scale,   // gate/up: xs [T,H/128]; down: hs [S,I/128]
+    const float* __restrict__ a_scale,   // gate/up: xss [H/128,S]; down: hs [I/128,S]
     const uint8_t* __restrict__ w,       // W_gu [E,2I,H] or W_d [E,H,I] codes
     const float* __restrict__ w_scale,   // [E,2I/128,H/128] or [E,H/128,I/128]
     void* __restrict__ out,              // gate/up: hq [S,I] codes; down: y [S,H] bf16
-    float* __restrict__ out_scale,       // gate/up: hs [S,I/128]; down: unused
+    float* __restrict__ out_scale,       // gate/up: hs [I/128,S]; down: unused
     const int32_t* __restrict__ slot_token, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off,
-    const int32_t* __restrict__ meta, int E, int H, int I, int n_nt, int xt) {
+    const int32_t* __restrict__ meta, int E, int H, int I, int n_nt, int xt, int S) {
   __shared__ __attribute__((aligned(16))) TileLdsX lds;
   __shared__ __attribute__((aligned(16))) float rsc[2][2][BMX];
 
@@ -336,14 +354,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
   // scale items: (weight block, tile row)
   const int nrb = (MODE == kGateUp) ? 2 * I / 128 : H / 128;
   ScaleItems it;
+  it.S = S;
   it.blk[0] = tid / BM;
   it.row[0] = tid % BM;
   it.blk[1] = (tid < 2 * kXRows) ? tid / kXRows : it.blk[0];
   it.row[1] = (tid < 2 * kXRows) ? BM + tid % kXRows : it.row[0];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int sslot = min(row0 + it.row[j], row_end - 1);
-    it.sa[j] = a_scale + static_cast<int64_t>((MODE == kGateUp) ? slot_token[sslot] : sslot) * nkb;
+    it.sa[j] = a_scale + min(row0 + it.row[j], row_end - 1);
     const int wblock = (MODE == kGateUp) ? (it.blk[j] == 0 ? nt : I / 128 + nt)
                                          : min(2 * nt + it.blk[j], nrb - 1);
     it.sw[j] = w_scale + (static_cast<int64_t>(e) * nrb + wblock) * nkb;
@@ -439,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
       if (row0 + rl < row_end) {
         const int64_t row = row0 + rl;
         *reinterpret_cast<uint2*>(hq + row * I + nt * 128 + c8) = make_uint2(lo, hi);
-        if (tid % 16 == 0) out_scale[row * (I / 128) + nt] = sc;
+        if (tid % 16 == 0) out_scale[static_cast<int64_t>(nt) * S + row] = sc;
       }
     }
     if (x_rows > 0) {
@@ -478,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
       if (rl < x_rows) {
         const int64_t row = row0 + BM + rl;
         *reinterpret_cast<uint2*>(hq + row * I + nt * 128 + c8) = make_uint2(lo, hi);
-        if (tid % 16 == 0) out_scale[row * (I / 128) + nt] = sc;
+        if (tid % 16 == 0) out_scale[static_cast<int64_t>(nt) * S + row] = sc;
       }
     }
   } else {
@@ -535,8 +553,8 @@ typedef unsigned char Ring[kStages][kStage];
 template <int NF>
 __device__ __forceinline__ float mainloop(
     const uint8_t* __restrict__ a_src, const uint32_t* a_off, const bool* a_ok, int c,
-    const uint8_t* __restrict__ wb, const uint32_t* b_off, const float* sc_src, bool sc_wave,
-    int sc_dst, float s0, int nkb, Ring& ring, float (&rsc)[2][2][BMS], int blk, int srow,
+    const uint8_t* __restrict__ wb, const uint32_t* b_off, const float* sc_src, int sc_stride,
+    bool sc_wave, int sc_dst, float s0, int nkb, Ring& ring, float (&rsc)[2][2][BMS], int blk, int srow,
     f32x16 (&acc)[4][2], const FragAddr& fa, int wn) {
   const int wave = threadIdx.x / kWave;
   f32x16 accx = {};
@@ -548,7 +566,7 @@ __device__ __forceinline__ float mainloop(
     for (int i = 0; i < kLoads; ++i)
       dma16(wb + (b_off[i] + kb * 128), &ring[st][kABytes + (wave + 8 * i) * 1024]);
     // scale words of block kb+1 (the last stage repeats block nkb-1)
-    if (sc_wave) dma4(sc_src + min(kb + 1, nkb - 1), &ring[st][sc_dst]);
+    if (sc_wave) dma4(sc_src + min(kb + 1, nkb - 1) * sc_stride, &ring[st][sc_dst]);
   };
   rsc[0][blk][srow] = 1.0f;
   float s_prev = s0;
@@ -584,7 +602,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8_small(
     float* __restrict__ out_scale, const int32_t* __restrict__ slot_token,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tile_off, const int32_t* __restrict__ meta, int E, int H, int I,
-    int n_nt) {
+    int n_nt, int S) {
   __shared__ __attribute__((aligned(16))) Ring ring;
   __shared__ __attribute__((aligned(16))) float rsc[2][2][BMS];
 
@@ -627,14 +645,17 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8_small(
   // two weight blocks (lanes 0-1; the others repeat block 1 into spare words)
   const bool sc_wave = uwave < 3;
   c += sc_wave;
+  // (s_a: [K/128][S] by slot, stride S per block; s_w: one word per block)
+  auto slot_of = [&](int t) { return min(row0 + t, row_end - 1); };
   const float* sc_src = (wave < 2)
-      ? a_scale + static_cast<int64_t>(arow_of(64 * wave + lane)) * nkb
+      ? a_scale + slot_of(64 * wave + lane)
       : w_scale + (static_cast<int64_t>(e) * nrb + wblock_of(min(lane, 1))) * nkb;
+  const int sc_stride = (wave < 2) ? S : 1;
   const int sc_dst = (wave < 2) ? kSaOff + 256 * wave : kSwOff;
   // scale items: threads 0..255 (weight block tid / 128, tile row tid % 128);
   // threads 256.. repeat them
   const int blk = (tid % 256) / BMS, srow = tid % BMS;
-  const float s0 = a_scale[static_cast<int64_t>(arow_of(srow)) * nkb] *
+  const float s0 = a_scale[slot_of(srow)] *
                    w_scale[(static_cast<int64_t>(e) * nrb + wblock_of(blk)) * nkb];
 
   const FragAddr fa = frag_addr(wm, wn, lane, 64);
@@ -646,9 +667,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8_small(
   const int nf = min(2, max(0, (m_valid - wm * 64 + 31) / 32));
   float s_last;
   switch (nf) {
-    case 2: s_last = mainloop<2>(a_src, a_off, a_ok, c, wb, b_off, sc_src, sc_wave, sc_dst, s0, nkb, ring, rsc, blk, srow, acc, fa, wn); break;
-    case 1: s_last = mainloop<1>(a_src, a_off, a_ok, c, wb, b_off, sc_src, sc_wave, sc_dst, s0, nkb, ring, rsc, blk, srow, acc, fa, wn); break;
-    default: s_last = mainloop<0>(a_src, a_off, a_ok, c, wb, b_off, sc_src, sc_wave, sc_dst, s0, nkb, ring, rsc, blk, srow, acc, fa, wn); break;
+    case 2: s_last = mainloop<2>(a_src, a_off, a_ok, c, wb, b_off, sc_src, sc_stride, sc_wave, sc_dst, s0, nkb, ring, rsc, blk, srow, acc, fa, wn); break;
+    case 1: s_last = mainloop<1>(a_src, a_off, a_ok, c, wb, b_off, sc_src, sc_stride, sc_wave, sc_dst, s0, nkb, ring, rsc, blk, srow, acc, fa, wn); break;
+    default: s_last = mainloop<0>(a_src, a_off, a_ok, c, wb, b_off, sc_src, sc_stride, sc_wave, sc_dst, s0, nkb, ring, rsc, blk, srow, acc, fa, wn); break;
   }
 
   // ---- epilogue: last block's scale, then store ---------------------------
@@ -711,7 +732,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8_small(
       if (row0 + rl < row_end) {
         const int64_t row = row0 + rl;
         *reinterpret_cast<uint2*>(hq + row * I + nt * 128 + c8) = make_uint2(lo, hi);
-        if (tid % 16 == 0) out_scale[row * (I / 128) + nt] = sc;
+        if (tid % 16 == 0) out_scale[static_cast<int64_t>(nt) * S + row] = sc;
       }
     }
   } else {
@@ -755,25 +776,30 @@ hipError_t launch_experts_fp8(const Plan& p, const void* x,
   const int32_t* offsets = ws_at<int32_t>(ws, p.off_offsets);
   const int32_t* toff = ws_at<int32_t>(ws, p.off_tile_off);
   const int32_t* meta = ws_at<int32_t>(ws, p.off_meta);
+  float* xss = ws_at<float>(ws, p.off_xss);
   hipError_t e = launch_quant_e4m3(p.T, p.H, BEAM_BF16, x, xq, xs, s, tm);
   if (e != hipSuccess) return e;
+  const int S = static_cast<int>(p.S);
+  BEAM_LAUNCH(tm, "slot_scales_fp8", slot_scales_fp8,
+              dim3(static_cast<unsigned>(ceil_div(p.S * (p.H / 128), 256))), dim3(256), 0, s, xs,
+              slot_token, xss, S, p.H / 128);
   const int nt_gu = p.I / 128;
   const int nt_dn = static_cast<int>(ceil_div(p.H, BN));
   if (p.bm == small8::BMS) {
     BEAM_LAUNCH(tm, "gate_up_fp8", small8::grouped_gemm_fp8_small<kGateUp>, grid_for(p, nt_gu),
-                dim3(kThreads), 0, s, xq, xs, w_gate_up, s_gate_up, hq, hs, slot_token, counts,
-                offsets, toff, meta, p.E, p.H, p.I, nt_gu);
+                dim3(kThreads), 0, s, xq, xss, w_gate_up, s_gate_up, hq, hs, slot_token, counts,
+                offsets, toff, meta, p.E, p.H, p.I, nt_gu, S);
     BEAM_LAUNCH(tm, "down_fp8", small8::grouped_gemm_fp8_small<kDown>, grid_for(p, nt_dn),
                 dim3(kThreads), 0, s, hq, hs, w_down, s_down, y, nullptr, slot_token, counts,
-                offsets, toff, meta, p.E, p.H, p.I, nt_dn);
+                offsets, toff, meta, p.E, p.H, p.I, nt_dn, S);
     return hipGetLastError();
   }
   BEAM_LAUNCH(tm, "gate_up_fp8", grouped_gemm_fp8<kGateUp>, grid_for(p, nt_gu),
-              dim3(kThreads), 0, s, xq, xs, w_gate_up, s_gate_up, hq, hs, slot_token,
-              counts, offsets, toff, meta, p.E, p.H, p.I, nt_gu, p.xt);
+              dim3(kThreads), 0, s, xq, xss, w_gate_up, s_gate_up, hq, hs, slot_token,
+              counts, offsets, toff, meta, p.E, p.H, p.I, nt_gu, p.xt, S);
   BEAM_LAUNCH(tm, "down_fp8", grouped_gemm_fp8<kDown>, grid_for(p, nt_dn),
               dim3(kThreads), 0, s, hq, hs, w_down, s_down, y, nullptr, slot_token,
-              counts, offsets, toff, meta, p.E, p.H, p.I, nt_dn, p.xt);
+              counts, offsets, toff, meta, p.E, p.H, p.I, nt_dn, p.xt, S);
   return hipGetLastError();
 }
 

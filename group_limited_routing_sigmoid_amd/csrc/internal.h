@@ -33,7 +33,7 @@ struct Plan {
   size_t off_part, off_idx, off_w, off_hist, off_base, off_rank, off_counts,
       off_offsets, off_slot_token, off_slot_of,
       off_meta, off_active, off_tile_off, off_w3, off_h, off_y, off_xq, off_xs,
-      off_hq, off_hs;
+      off_hq, off_hs, off_xss;
   size_t total;
 };
 

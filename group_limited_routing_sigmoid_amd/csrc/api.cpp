@@ -153,8 +153,11 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
   p->off_h = take(h_codes_only ? 0 : S * I * ((f32 || p->wdt == BEAM_MXFP4) ? 4 : 2));
   p->off_y = take(S * H * ((f32 || p->stream_path || p->wdt == BEAM_MXFP4) ? 4 : 2));
   if (p->wdt == BEAM_MXFP4) {
+    // grouped path: x's E8M0 bytes also per slot, as one word per 128 k,
+    // block-major ([H/128][S] words), and h's the same ([I/128][S])
     p->off_xq = take(T * H);
     p->off_xs = take(T * (H / 32));
+    p->off_xss = p->stream_path ? 0 : take(S * (H / 32));
     p->off_hq = take(S * I);
     p->off_hs = take(S * (I / 32));
   }

@@ -212,6 +212,20 @@ __global__ __launch_bounds__(kThreads) void stream_down_mx(
   }
 }
 
+// x's E8M0 bytes per slot for the grouped products, one word (4 bytes, 128 k)
+// per stage, block-major: word kb * S + slot = bytes 4 kb .. 4 kb + 3 of
+// the slot's token row, so that a tile stage reads its rows' words as one
+// run rather than one cache line per row.
+__global__ __launch_bounds__(256) void slot_scales_mx(const uint8_t* __restrict__ xs,
+                                                      const int32_t* __restrict__ slot_token,
+                                                      uint8_t* __restrict__ xss, int S, int nkb) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(S) * nkb) return;
+  const int64_t kb = i / S, slot = i % S;
+  reinterpret_cast<uint32_t*>(xss)[i] = *reinterpret_cast<const uint32_t*>(
+      xs + static_cast<int64_t>(slot_token[slot]) * (nkb * 4) + 4 * kb);
+}
+
 // ---- grouped E2M1 x E4M3 GEMM -----------------------------------------------
 // Same work list and XCD order as the bf16 grouped GEMM (M tiles of BMS = 256
 // or 128 slots x 256-row N tiles), 128 k per stage, stages copied straight
@@ -308,14 +322,14 @@ __device__ __forceinline__ void stage_products(const unsigned char* st, const ui
 template <int BMS, int STAGES, int MODE, bool PER>
 __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
     const uint8_t* __restrict__ xq,      // gate/up: xq [T,H]; down: hq [S,I]  (E4M3)
-    const uint8_t* __restrict__ xs,      // their E8M0 bytes [rows, K/32]
+    const uint8_t* __restrict__ xs,      // their E8M0 bytes per slot: [K/128][S] words
     const uint8_t* __restrict__ w,       // W_gu [E,2I,H/2] or W_d [E,H,I/2] (E2M1 pairs)
     const uint8_t* __restrict__ ws,      // [E,2I,H/32] or [E,H,I/32]
     void* __restrict__ out,              // gate/up: hq [S,I] (E4M3); down: y [S,H] (fp32)
-    uint8_t* __restrict__ out_scale,     // gate/up: hs [S,I/32] (E8M0); down: unused
+    uint8_t* __restrict__ out_scale,     // gate/up: hs [I/128][S] words (E8M0); down: unused
     const int32_t* __restrict__ slot_token, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off,
-    const int32_t* __restrict__ meta, int E, int H, int I, int n_nt, int xt) {
+    const int32_t* __restrict__ meta, int E, int H, int I, int n_nt, int xt, int n_slots) {
   using G = Geo<BMS, STAGES, PER>;
   constexpr int S = G::kStages, P = S - 1;  // ring size, stages in flight
   // the stages, then (PER) the period buffers: one object, so the compiler
@@ -369,8 +383,12 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
   // rows per stage
   const bool s_x = uwave < G::kXsWaves, s_any = uwave < G::kXsWaves + (PER ? 1 : 4);
   c += s_any;
-  const uint8_t* s_src = s_x ? xs + static_cast<int64_t>(slot_src(64 * wave + lane)) * (K / 32)
+  // activation words: slot t's word of stage kb at xs + 4 (kb n_slots + t),
+  // so a stage's rows are one run; weight words: 4 bytes per stage of a row
+  auto slot_of = [&](int t) { return min(row0 + t, row_end - 1); };
+  const uint8_t* s_src = s_x ? xs + static_cast<int64_t>(slot_of(64 * wave + lane)) * 4
                              : wsb + static_cast<int64_t>(wrow_of(64 * ((s_any ? wave : G::kXsWaves) - G::kXsWaves) + lane)) * (K / 32);
+  const int s_step = s_x ? 4 * n_slots : 4;
   const int s_dst = G::kXBytes + G::kWBytes +
                     (s_x ? 256 * wave : BMS * 4 + 256 * ((s_any ? wave : G::kXsWaves) - G::kXsWaves));
   // extension slots: waves 0..3 copy one 8-row region each, wave 0 their
@@ -380,7 +398,7 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
   const bool xs_ok = uwave == 0 && x_rows > 0;
   c += xt_ok + xs_ok;
   const uint32_t xt_off = static_cast<uint32_t>(slot_src(BMS + xr)) * K + dma_chunk(xr, lane) * 16;
-  const uint8_t* xs_src = xs + static_cast<int64_t>(slot_src(BMS + min(lane, kXtRows - 1))) * (K / 32);
+  const uint8_t* xs_src = xs + static_cast<int64_t>(slot_of(BMS + min(lane, kXtRows - 1))) * 4;
   // PER: with stage kb travel the bytes of period q = kb/kPer + 1 (stages
   // kPer*q ..) of rows 64 g + lane, g = kb % kPer, into buffer q % kPerSlots.
   // That buffer last held period q - 3, read up to stage kPer*(q-2) - 1,
@@ -401,11 +419,11 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
       dma16(wb + (w_off[i] + kb * 64), sb + G::kXBytes + (wave + 8 * i) * 1024);
     if (s_any) {
       if (PER && !s_x) dma16(per_src(kb % kPer, kb / kPer + 1), per_dst(kb % kPer, kb / kPer + 1));
-      else dma4(s_src + kb * 4, sb + s_dst);
+      else dma4(s_src + kb * s_step, sb + s_dst);
     }
     if (G::kExt) {
       if (xt_ok) dma16(xq + (xt_off + kb * 128), sb + G::kXtOff + uwave * 1024);
-      if (xs_ok) dma4(xs_src + kb * 4, sb + G::kXtOff + kXtRows * 128);
+      if (xs_ok) dma4(xs_src + kb * (4 * n_slots), sb + G::kXtOff + kXtRows * 128);
     }
   };
   // scale words of weight row t at stage kb: WS(kb, st)[t * (PER ? 4 : 1)]
@@ -495,7 +513,7 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
         *reinterpret_cast<uint32_t*>(hq + 8 * g + 4 * half) =
             e4m3x4(ldexpf(hv[4 * g], -x), ldexpf(hv[4 * g + 1], -x), ldexpf(hv[4 * g + 2], -x),
                    ldexpf(hv[4 * g + 3], -x));
-      if (half == 0) out_scale[static_cast<int64_t>(slot) * (I / 32) + nt * 4 + wn] = static_cast<uint8_t>(x + 127);
+      if (half == 0) out_scale[(static_cast<int64_t>(nt) * n_slots + slot) * 4 + wn] = static_cast<uint8_t>(x + 127);
     } else {
       if (slot >= row_end) continue;
 #pragma unroll
@@ -544,7 +562,7 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
           *reinterpret_cast<uint32_t*>(hq + 8 * g + 4 * half) =
               e4m3x4(ldexpf(hv[4 * g], -x), ldexpf(hv[4 * g + 1], -x), ldexpf(hv[4 * g + 2], -x),
                      ldexpf(hv[4 * g + 3], -x));
-        if (half == 0) out_scale[static_cast<int64_t>(slot) * (I / 32) + nt * 4 + wn] = static_cast<uint8_t>(x + 127);
+        if (half == 0) out_scale[(static_cast<int64_t>(nt) * n_slots + slot) * 4 + wn] = static_cast<uint8_t>(x + 127);
       }
     }
   } else if (r < x_rows) {
@@ -597,15 +615,21 @@ hipError_t launch_experts_mxfp4(const Plan& p, const void* x, const uint8_t* w_g
     const int32_t* toff = ws_at<int32_t>(ws, p.off_tile_off);
     const int nt_gu = p.I / 128;
     const int nt_dn = static_cast<int>(ceil_div(p.H, tile::BN));
+    uint8_t* xss = ws_at<uint8_t>(ws, p.off_xss);
+    const int n_slots = static_cast<int>(p.S);
+    BEAM_LAUNCH(tm, "slot_scales_mx", slot_scales_mx,
+                dim3(static_cast<unsigned>(ceil_div(p.S * (p.H / 128), 256))), dim3(256), 0, s,
+                xs, slot_token, xss, n_slots, p.H / 128);
 #define BEAM_MX_GATE_UP(BMS, STAGES, PER)                                                     \
   BEAM_LAUNCH(tm, "grouped_gate_up_mx", (mxg::grouped_gemm_mx<BMS, STAGES, mxg::kGateUp, PER>), \
-              tile::grid_for(p, nt_gu), dim3(tile::kThreads), 0, s, xq, xs, w_gate_up,         \
+              tile::grid_for(p, nt_gu), dim3(tile::kThreads), 0, s, xq, xss, w_gate_up,        \
               s_gate_up, hq, hs, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_gu, \
-              p.xt)
+              p.xt, n_slots)
 #define BEAM_MX_DOWN(BMS, STAGES, PER)                                                        \
   BEAM_LAUNCH(tm, "grouped_down_mx", (mxg::grouped_gemm_mx<BMS, STAGES, mxg::kDown, PER>),     \
               tile::grid_for(p, nt_dn), dim3(tile::kThreads), 0, s, hq, hs, w_down, s_down, y, \
-              nullptr, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_dn, p.xt)
+              nullptr, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_dn, p.xt,    \
+              n_slots)
     // weight scale bytes in periods of four stages when K % 512 == 0
 #define BEAM_MX_TILES(BMS, STAGES)                                                            \
   if (p.H % 512 == 0) BEAM_MX_GATE_UP(BMS, STAGES, true);                                      \

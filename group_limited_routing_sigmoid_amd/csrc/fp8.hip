@@ -597,6 +597,8 @@ __device__ __forceinline__ float mainloop(
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8_small(
+    // arguments as for grouped_gemm_fp8: a_scale and out_scale [K/128][S]
+    // (S slots), per slot and block-major
     const uint8_t* __restrict__ a_src, const float* __restrict__ a_scale,
     const uint8_t* __restrict__ w, const float* __restrict__ w_scale, void* __restrict__ out,
     float* __restrict__ out_scale, const int32_t* __restrict__ slot_token,
@@ -641,11 +643,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8_small(
                                        : min(nt * BN + r, H - 1);
     b_off[i] = static_cast<uint32_t>(wrow) * K + dma_chunk(r, lane) * 16;
   }
-  // scale words: waves 0-1 s_a of tile rows 64 w + lane, wave 2 s_w of the
-  // two weight blocks (lanes 0-1; the others repeat block 1 into spare words)
+  // scale words: waves 0-1 s_a of tile rows 64 w + lane (the slots' words
+  // of a block are consecutive: stride S from block to block), wave 2 s_w of
+  // the two weight blocks (lanes 0-1; the others repeat block 1 into spare
+  // words; one word per block)
   const bool sc_wave = uwave < 3;
   c += sc_wave;
-  // (s_a: [K/128][S] by slot, stride S per block; s_w: one word per block)
   auto slot_of = [&](int t) { return min(row0 + t, row_end - 1); };
   const float* sc_src = (wave < 2)
       ? a_scale + slot_of(64 * wave + lane)

@@ -231,7 +231,9 @@ __global__ __launch_bounds__(256) void slot_scales_mx(const uint8_t* __restrict_
 // or 128 slots x 256-row N tiles), 128 k per stage, stages copied straight
 // into LDS: activation tile (E4M3, BMS slots x 128 bytes, the bf16 tiles'
 // layout and swizzle), weight tile (E2M1, 256 rows x 64 bytes), and both
-// tiles' E8M0 bytes (4 per row per stage).  The stages form a ring (2 or 3
+// tiles' E8M0 bytes (4 per row per stage: the activations' from words kept
+// per slot and block-major, one run per stage; the weights' in the stage or,
+// when K % 512 == 0, in periods of four stages, below).  The stages form a ring (2 or 3
 // of 50 KiB for 256 slots, 4 of 33.5 KiB for 128): the copies of all but the
 // stage being consumed are in flight, and a wave copies the same number of
 // regions every stage, so each wait is a count of its outstanding copies

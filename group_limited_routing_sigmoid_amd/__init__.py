@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libbeam_moe.so")
 
 F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
 ROUTE_LOGITS_IN, PATH_STREAM, PATH_GROUPED = 1 << 0, 1 << 1, 1 << 2
-TILE_128, TILE_256, TILE_160 = 1 << 3, 1 << 4, 1 << 5
+TILE_128, TILE_256, TILE_160, TILE_64 = 1 << 3, 1 << 4, 1 << 5, 1 << 6
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 SYMBOLS = ("beam_status_string", "beam_moe_validate", "beam_moe_workspace_bytes",

@@ -103,17 +103,23 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
   // 2.76 / 2.93 at 3.5K, 3.31 / 3.02 at 4K; so 128 below T*K = 120E.
   p->bm = kGemmBM;
   if (p->wdt == BEAM_BF16) {
-    if (p->flags & BEAM_TILE_128) p->bm = 128;
+    if (p->flags & (BEAM_TILE_64 | BEAM_TILE_128)) p->bm = 128;
     else if (p->flags & BEAM_TILE_160) p->bm = 160;
     else if (p->flags & BEAM_TILE_256) p->bm = kGemmBM;
     else if (S < 96 * E) p->bm = 128;
     else if (S < 144 * E) p->bm = 160;
   } else if (p->wdt == BEAM_MXFP4) {
-    if (p->flags & BEAM_TILE_128) p->bm = 128;
+    // 64-slot tiles with 256-deep stages (H, I multiples of 512) against the
+    // rest at default: 1.02 / 1.11 ms at 64 tokens, 1.33 / 1.46 at 1K, 1.44
+    // / 1.55 at 1.5K, 1.71 / 1.68 at 2K, 2.21 / 1.91 at 3K
+    const bool wide = H % 512 == 0 && I % 512 == 0;
+    if (p->flags & BEAM_TILE_64) p->bm = 64;
+    else if (p->flags & BEAM_TILE_128) p->bm = 128;
     else if (p->flags & (BEAM_TILE_160 | BEAM_TILE_256)) p->bm = kGemmBM;
+    else if (wide && S < 56 * E) p->bm = 64;
     else if (S < 32 * E) p->bm = 128;
   } else if (p->wdt == BEAM_FP8_E4M3) {
-    if (p->flags & BEAM_TILE_128) p->bm = 128;
+    if (p->flags & (BEAM_TILE_64 | BEAM_TILE_128)) p->bm = 128;
     else if (!(p->flags & (BEAM_TILE_160 | BEAM_TILE_256)) && S < 120 * E) p->bm = 128;
   }
   // FP8, and MXFP4 where its 256-slot tiles run two stages (T*K >= 192E):
@@ -193,7 +199,7 @@ const char* beam_status_string(int status) {
 
 int beam_moe_validate(const beam_moe_desc* d, int64_t T) {
   if (!d || T < 0) return BEAM_ERR_INVALID_ARG;
-  const uint32_t tiles = BEAM_TILE_128 | BEAM_TILE_160 | BEAM_TILE_256;
+  const uint32_t tiles = BEAM_TILE_64 | BEAM_TILE_128 | BEAM_TILE_160 | BEAM_TILE_256;
   const uint32_t known = BEAM_ROUTE_LOGITS_IN | BEAM_PATH_STREAM | BEAM_PATH_GROUPED | tiles;
   if (d->flags & ~known) return BEAM_ERR_INVALID_ARG;
   const uint32_t tf = d->flags & tiles;

@@ -477,9 +477,9 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
+  using I2 = std::integral_constant<int, (G::kJ >= 2 ? 2 : 1)>;
   using IJ = std::integral_constant<int, G::kJ>;
-  using I3 = std::integral_constant<int, (G::kJ >= 3 ? 3 : 2)>;
+  using I3 = std::integral_constant<int, (G::kJ >= 3 ? 3 : (G::kJ >= 2 ? 2 : 1))>;
   using NoX = std::integral_constant<bool, false>;
   using ExtX = std::integral_constant<bool, G::kExt>;
   if (nj == G::kJ && x_rows > 0) run(IJ{}, ExtX{});
@@ -581,6 +581,200 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
 
 }  // namespace mxg
 
+// ---- 64-slot tiles with 256-deep stages ---------------------------------------
+// For decode batches the 4-bit weights stream from HBM, and a 128-deep stage
+// reads each weight row as a 64-byte half of a cache line.  This form takes
+// 256 k per stage, so a weight row is one whole 128-byte line per stage (the
+// bf16 tiles' row layout, swizzle and copy pattern), with 64 slots x 256
+// bytes of activations, in a ring of three 48.5 KiB stages (two in flight)
+// with the counted waits of the other rings.  Scale bytes: the activations'
+// two words per slot per stage from the block-major slot words (waves 0-1);
+// the weights' in periods of two stages, 16 bytes of a row, half of the
+// rows with each stage (waves 2-3), in a ring of three 4 KiB buffers after
+// the stages (rewritten only after the period it held three periods
+// earlier has been read: period q is issued with stages 2(q-1) .. 2q-1 at
+// steps >= 2q-4, period q-3 was last read at step 2q-5).  The products
+// per 64-deep step are those of the 128-deep form (same operands, same
+// order): bit-identical.  K % 512 == 0.
+namespace mxw {
+
+using namespace tile;
+using mxg::kGateUp;
+
+constexpr int BMS = 64;
+constexpr int kXRow = 256;                     // activation bytes per slot per stage
+constexpr int kXBytes = BMS * kXRow;           // 16 KiB
+constexpr int kWBytes = BN * 128;              // 32 KiB: 256 rows x 128 bytes
+constexpr int kXsOff = kXBytes + kWBytes;      // activation scale words [2][64]
+constexpr int kStage = kXsOff + 2 * BMS * 4;   // 49,664 bytes
+constexpr int kStages = 3, P = kStages - 1;
+constexpr int kPerOff = kStages * kStage;
+constexpr int kPerSlots = 3;
+constexpr int kLds = kPerOff + kPerSlots * BN * 16;  // 161,280 bytes
+
+// 256-byte activation rows: chunk c of slot row t at t * 256 + ((c ^ (t % 16))
+// << 4), so 16 consecutive rows at one logical chunk hit distinct banks.
+__device__ __forceinline__ int xswz(int t, int c) { return t * kXRow + ((c ^ (t & 15)) << 4); }
+
+template <int MODE>
+__global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx_wide(
+    // arguments as for mxg::grouped_gemm_mx
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+    const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws, void* __restrict__ out,
+    uint8_t* __restrict__ out_scale, const int32_t* __restrict__ slot_token,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ meta, int E, int H, int I,
+    int n_nt, int n_slots) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
+  Coords tc;
+  if (!tile_coords(counts, offsets, tile_off, meta, E, n_nt, tc, BMS)) return;
+  const int e = tc.e, nt = tc.nt, row0 = tc.row0, row_end = tc.row_end;
+  const int K = (MODE == kGateUp) ? H : I;
+  const int nk = K / 256, nper = nk / 2;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int uwave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy
+  const int wm = wave / 4, wn = wave % 4, r = lane % 32, half = lane / 32;
+  const int m_valid = min(BMS, row_end - row0);
+  const int64_t nrows = (MODE == kGateUp) ? 2 * I : H;
+  const uint8_t* wb = w + static_cast<int64_t>(e) * nrows * (K / 2);
+  const uint8_t* wsb = ws + static_cast<int64_t>(e) * nrows * (K / 32);
+  auto wrow_of = [&](int t) {  // weight row of tile row t
+    return (MODE == kGateUp) ? ((t < 128) ? nt * 128 + t : I + nt * 128 + (t - 128))
+                             : min(nt * BN + t, H - 1);
+  };
+  auto slot_of = [&](int t) { return min(row0 + t, row_end - 1); };  // padding: a valid slot
+  // activations: two 1 KiB regions of 4 rows per wave (lane l writes physical
+  // chunk l % 16 of row 4 region + l / 16), copied when the region's first
+  // row is valid; weights: four regions of 8 rows (tile::dma_row / dma_chunk)
+  uint32_t x_off[2], w_off[4];
+  bool x_ok[2];
+  int c = 4;  // this wave's copies per stage
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = 4 * (wave + 8 * i) + lane / 16;
+    x_ok[i] = 4 * (uwave + 8 * i) < m_valid;
+    c += x_ok[i];
+    const int src = (MODE == kGateUp) ? slot_token[slot_of(t)] : slot_of(t);
+    x_off[i] = static_cast<uint32_t>(src) * K + (((lane % 16) ^ (t & 15)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = dma_row(wave, lane, i);
+    w_off[i] = static_cast<uint32_t>(wrow_of(t)) * (K / 2) + dma_chunk(t, lane) * 16;
+  }
+  // scale copies: wave 0 / 1 the slots' word 2 kb / 2 kb + 1 of stage kb;
+  // waves 2-3 the weight bytes of period kb/2 + 1 for rows 128 (kb % 2) +
+  // 64 (wave - 2) + lane
+  const bool s_x = uwave < 2, s_w = uwave == 2 || uwave == 3;
+  c += s_x || s_w;
+  const uint8_t* xs_src = xs + (static_cast<int64_t>(s_x ? wave : 0) * n_slots + slot_of(lane)) * 4;
+  const int wq = s_w ? wave - 2 : 0;
+  auto per_src = [&](int g, int q) {
+    return wsb + (static_cast<int64_t>(wrow_of(128 * g + 64 * wq + lane)) * (K / 32) +
+                  16 * min(q, nper - 1));
+  };
+  auto per_dst = [&](int g, int q) {
+    return &lds[kPerOff + (q % kPerSlots) * (BN * 16) + (128 * g + 64 * wq) * 16];
+  };
+  auto dma = [&](int st, int kb) {
+    unsigned char* sb = &lds[st * kStage];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (x_ok[i]) dma16(xq + (x_off[i] + kb * 256), sb + (wave + 8 * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dma16(wb + (w_off[i] + kb * 128), sb + kXBytes + (wave + 8 * i) * 1024);
+    if (s_x) dma4(xs_src + static_cast<int64_t>(kb) * (8 * n_slots), sb + kXsOff + wave * 256);
+    if (s_w) dma16(per_src(kb % 2, kb / 2 + 1), per_dst(kb % 2, kb / 2 + 1));
+  };
+  int wrow[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+    wrow[f] = (MODE == kGateUp) ? (f * 128 + wn * 32 + r) : (wn * 64 + f * 32 + r);
+  const int srow = wm * 32 + r;
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  const bool live = m_valid > wm * 32;  // the wave's 32 slots hold a valid one
+  // period 0 of the weight scale bytes, ahead of stage 0's copies
+  if (s_w) {
+    dma16(per_src(0, 0), per_dst(0, 0));
+    dma16(per_src(1, 0), per_dst(1, 0));
+  }
+#pragma unroll
+  for (int s0 = 0; s0 < P; ++s0)
+    if (s0 < nk) dma(s0, s0);
+  ring_barrier(c * (min(P, nk) - 1));  // stage 0 landed
+  int st = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int kn = kt + P;
+    if (kn < nk) dma(st == 0 ? kStages - 1 : st - 1, kn);
+    if (live) {
+      const unsigned char* X = &lds[st * kStage];
+      const unsigned char* W = X + kXBytes;
+      const uint32_t* XS = reinterpret_cast<const uint32_t*>(X + kXsOff);
+      const uint32_t* WS = reinterpret_cast<const uint32_t*>(
+          &lds[kPerOff + ((kt / 2) % kPerSlots) * (BN * 16)]) + 2 * (kt % 2);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        // scale byte 2 ks + half of the stage: word ks / 2, byte 2 (ks % 2) + half
+        const int sh = 8 * (2 * (ks % 2) + half);
+        u32x4 a[2];
+        uint32_t sa[2];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          a[f] = *reinterpret_cast<const u32x4*>(W + swz(wrow[f], 2 * ks + half));
+          sa[f] = (WS[wrow[f] * 4 + ks / 2] >> sh) & 0xFFu;
+        }
+        const u32x4 b0 = *reinterpret_cast<const u32x4*>(X + xswz(srow, 4 * ks + half));
+        const u32x4 b1 = *reinterpret_cast<const u32x4*>(X + xswz(srow, 4 * ks + 2 + half));
+        const uint32_t sb = (XS[(ks / 2) * BMS + srow] >> sh) & 0xFFu;
+#pragma unroll
+        for (int f = 0; f < 2; ++f) acc[f] = mfma_mx(a[f], b0, b1, acc[f], sa[f], sb);
+      }
+    }
+    ring_barrier(c * max(0, min(kn, nk - 1) - (kt + 1)));  // stage kt+1 landed
+    st = (st == kStages - 1) ? 0 : st + 1;
+  }
+  if (!live) return;
+  // epilogue as in mxg::grouped_gemm_mx (one 32-slot fragment per wave)
+  const int slot = row0 + srow;
+  if (MODE == kGateUp) {
+    float hv[16];
+    float m = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      hv[q] = silu(acc[0][q]) * acc[1][q];
+      m = fmaxf(m, fabsf(hv[q]));
+    }
+    m = fmaxf(m, __shfl_xor(m, 32));
+    const int x = mx8_exponent(m);
+    if (slot >= row_end) return;
+    uint8_t* hq = static_cast<uint8_t*>(out) + static_cast<int64_t>(slot) * I + nt * 128 + wn * 32;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<uint32_t*>(hq + 8 * g + 4 * half) =
+          e4m3x4(ldexpf(hv[4 * g], -x), ldexpf(hv[4 * g + 1], -x), ldexpf(hv[4 * g + 2], -x),
+                 ldexpf(hv[4 * g + 3], -x));
+    if (half == 0)
+      out_scale[(static_cast<int64_t>(nt) * n_slots + slot) * 4 + wn] = static_cast<uint8_t>(x + 127);
+  } else {
+    if (slot >= row_end) return;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int cr = 8 * g + 4 * half;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int col = nt * BN + wn * 64 + f * 32 + cr;  // H % 128 == 0: all 4 or none
+        if (col < H) {
+          const f32x4 v = {acc[f][4 * g], acc[f][4 * g + 1], acc[f][4 * g + 2], acc[f][4 * g + 3]};
+          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + static_cast<int64_t>(slot) * H + col) = v;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace mxw
+
 }  // namespace
 
 hipError_t launch_quant_mxfp8(int64_t rows, int64_t cols, int32_t dtype, const void* v,
@@ -641,7 +835,24 @@ hipError_t launch_experts_mxfp4(const Plan& p, const void* x, const uint8_t* w_g
     // measured on the Beam layer: 128-slot tiles (four stages) ahead below
     // 1K tokens; 256-slot tiles with three stages ahead at 1K-4K tokens
     // (2.38 vs 2.46 ms at 4K), with two at 8K (4.24 vs 4.36 ms)
-    if (p.bm == 128) {
+    if (p.bm == 64) {
+      // 64-slot tiles: 256-deep stages when K % 512 == 0, else 128-deep
+      // stages in a ring of five
+      if (p.H % 512 == 0)
+        BEAM_LAUNCH(tm, "grouped_gate_up_mx", mxw::grouped_gemm_mx_wide<mxg::kGateUp>,
+                    tile::grid_for(p, nt_gu), dim3(tile::kThreads), 0, s, xq, xss, w_gate_up,
+                    s_gate_up, hq, hs, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I,
+                    nt_gu, n_slots);
+      else
+        BEAM_MX_GATE_UP(64, 5, false);
+      if (p.I % 512 == 0)
+        BEAM_LAUNCH(tm, "grouped_down_mx", mxw::grouped_gemm_mx_wide<mxg::kDown>,
+                    tile::grid_for(p, nt_dn), dim3(tile::kThreads), 0, s, hq, hs, w_down, s_down,
+                    y, nullptr, slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_dn,
+                    n_slots);
+      else
+        BEAM_MX_DOWN(64, 5, false);
+    } else if (p.bm == 128) {
       BEAM_MX_TILES(128, 4);
     } else if (p.S < 192 * static_cast<int64_t>(p.E)) {
       BEAM_MX_TILES(256, 3);

@@ -70,8 +70,9 @@ typedef enum {
 /* Expert path (default: bf16 streams its weights below T*K = E/2 and uses
  * grouped tiles above; MXFP4 and FP8 use grouped tiles; fp32 has one path).
  * Tile height of the grouped path (default: bf16 128 rows below T*K = 96E,
- * 160 below 144E, 256 above; MXFP4 128 below 32E, 256 above; FP8 128 below
- * 120E, 256 above, an expert's last tile holding up to 288).  Every tile
+ * 160 below 144E, 256 above; MXFP4 64 below 56E when H and I are multiples
+ * of 512, else 128 below 32E, 256 above; FP8 128 below 120E, 256 above, an
+ * expert's last tile holding up to 288).  Every tile
  * height gives bit-identical outputs; the two paths agree within the layer
  * tolerance (they sum in different orders, and bf16 streaming keeps y in
  * fp32).  The flags exist for measurement and tests. */
@@ -82,6 +83,8 @@ typedef enum {
                                           extension of an expert's last tile) */
 #define BEAM_TILE_160 (1u << 5)        /* bf16 grouped path: force 160-row M tiles (MXFP4 and
                                           FP8: the 256-row form) */
+#define BEAM_TILE_64 (1u << 6)         /* MXFP4 grouped path: force 64-slot tiles (bf16 and
+                                          FP8: the 128-row form) */
 
 typedef struct {
   int32_t hidden;           /* H: 5120 for Beam */

@@ -40,6 +40,7 @@ def test_validate_accepts_layer_shapes():
     assert gl.validate(_desc(), 0) == gl.OK
     assert gl.validate(_desc(flags=gl.PATH_GROUPED | gl.TILE_128), 64) == gl.OK
     assert gl.validate(_desc(flags=gl.TILE_256), 64) == gl.OK
+    assert gl.validate(_desc(flags=gl.TILE_64), 64) == gl.OK
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -63,6 +64,7 @@ def test_validate_accepts_layer_shapes():
     ("flags", gl.PATH_STREAM | gl.PATH_GROUPED, gl.ERR_INVALID_ARG),
     ("flags", gl.TILE_128 | gl.TILE_256, gl.ERR_INVALID_ARG),
     ("flags", gl.TILE_160 | gl.TILE_256, gl.ERR_INVALID_ARG),
+    ("flags", gl.TILE_64 | gl.TILE_128, gl.ERR_INVALID_ARG),
 ])
 def test_validate_rejects(field, value, status):
     assert gl.validate(_desc(**{field: value}), 64) == status

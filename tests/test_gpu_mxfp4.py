@@ -59,6 +59,7 @@ def _check(inp, shape, tokens, label, path=0):
           f"{e_emu:.3e} vs MXFP8-activation emulation")
     assert e_ref <= MX_TOL, e_ref
     assert e_emu <= EMU_TOL, e_emu
+    return out
 
 
 @pytest.mark.parametrize("T", [1, 5, 40, 300])
@@ -100,20 +101,21 @@ def test_mxfp4_beam_8k_sampled():
 
 @pytest.mark.parametrize("T", [3, 700, 2100, 4300])
 def test_mxfp4_tile_forms_bitwise_equal(T):
-    # 128-slot tiles (4-stage ring), 256-slot tiles (3-stage ring below
-    # T*K = 192E, 2-stage above: T = 2100 and 4300 on this shape) and, by
+    # 64-slot tiles (256-deep stages for gate/up, H = 512; 128-deep for
+    # down, I = 256), 128-slot tiles (4-stage ring), 256-slot tiles (3-stage
+    # ring below T*K = 192E, 2-stage above: T = 2100 and 4300 on this shape) and, by
     # default on the 2-stage form, last tiles extended by up to 32 slots add
     # the same products in the same order and quantise h alike: equal bits
     sh = small_shape()
     inp = make_inputs(WORKLOADS["mxfp4_8k"], device=device(), tokens=T, shape=sh,
                       seed=900 + T, bias="skew:0.5:0,1,2,3,32,33,34,35")
     outs = []
-    for tile in (gl.TILE_128, gl.TILE_256, 0):
+    for tile in (gl.TILE_64, gl.TILE_128, gl.TILE_256, 0):
         d = desc_for(WORKLOADS["mxfp4_8k"], sh, gl.PATH_GROUPED | tile)
         outs.append(gl.forward(d, inp.x, inp.w_router, inp.bias, inp.w_gate_up, inp.w_down,
                                inp.s_gate_up, inp.s_down))
     torch.cuda.synchronize()
-    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
 
 
 @pytest.mark.parametrize("T", [2100, 4300])
@@ -130,3 +132,22 @@ def test_mxfp4_extended_last_tiles(T):
     ext = ((counts % 256 >= 1) & (counts % 256 <= 32) & (counts > 256)).sum().item()
     print(f"experts whose last tile is extended: {ext} of {sh.n_experts}")
     assert ext > 0
+
+
+@pytest.mark.parametrize("T,skew", [(5, False), (300, False), (700, True)])
+def test_mxfp4_wide_stages(T, skew):
+    # H and I multiples of 512: by default 64-slot tiles with 256-deep stages
+    # for both products (weight scale bytes in periods of two stages);
+    # against the oracle and bit-identical to the 128- and 256-slot forms
+    sh = small_shape(hidden=1024, intermediate=512)
+    inp = make_inputs(WORKLOADS["mxfp4_8k"], device=device(), tokens=T, shape=sh,
+                      seed=990 + T, bias="skew:0.5:0,1,2,3,32,33,34,35" if skew else None)
+    rows = np.arange(0, T, max(1, T // 200))
+    a = _check(inp, sh, rows, f"mxfp4 wide stages T={T}")
+    outs = [a]
+    for tile in (gl.TILE_64, gl.TILE_128, gl.TILE_256):
+        d = desc_for(WORKLOADS["mxfp4_8k"], sh, gl.PATH_GROUPED | tile)
+        outs.append(gl.forward(d, inp.x, inp.w_router, inp.bias, inp.w_gate_up, inp.w_down,
+                               inp.s_gate_up, inp.s_down))
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])

@@ -123,3 +123,16 @@ def test_fp8_128_row_tiles(T, hidden, skew):
     a, _ = _check(inp, sh, rows, f"fp8 128-row tiles T={T} H={hidden}", gl.TILE_128)
     b, _ = _check(inp, sh, rows, f"fp8 256-row tiles T={T} H={hidden}", gl.TILE_256)
     assert torch.equal(a, b)
+
+
+def test_fp8_max_tokens_sampled():
+    # the largest batch the boundary accepts for the Beam layer (T = 52,428:
+    # 419,424 slots, the slot-major scale words up to block 39), sampled rows
+    # including the last
+    w = WORKLOADS["fp8_8k"]
+    T = (2**31 - 1) // (BEAM.top_k * max(BEAM.hidden, BEAM.intermediate))
+    assert gl.validate(desc_for(w, BEAM), T) == gl.OK
+    inp = make_inputs(w, device=device(), tokens=T)
+    rows = np.sort(np.random.default_rng(6).choice(T, 12, replace=False))
+    rows[-1] = T - 1
+    _check(inp, BEAM, rows, f"fp8 Beam T={T} sampled")

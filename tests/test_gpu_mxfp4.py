@@ -151,3 +151,16 @@ def test_mxfp4_wide_stages(T, skew):
                                inp.s_gate_up, inp.s_down))
     torch.cuda.synchronize()
     assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+def test_mxfp4_max_tokens_sampled():
+    # the largest batch the boundary accepts for the Beam layer (T = 52,428:
+    # 256-slot tiles with two stages and extended last tiles, slot-major
+    # scale words of 419,424 slots), sampled rows including the last
+    w = WORKLOADS["mxfp4_8k"]
+    T = (2**31 - 1) // (BEAM.top_k * max(BEAM.hidden, BEAM.intermediate))
+    assert gl.validate(desc_for(w, BEAM), T) == gl.OK
+    inp = make_inputs(w, device=device(), tokens=T)
+    rows = np.sort(np.random.default_rng(7).choice(T, 12, replace=False))
+    rows[-1] = T - 1
+    _check(inp, BEAM, rows, f"mxfp4 Beam T={T} sampled")

@@ -2,7 +2,7 @@
 // sum_k w[t,k] y[slot(t,k)], accumulated in fp32 in rank order and rounded
 // once to the output dtype.  There is no shared expert to add ("Reflection
 // Releases Beam ...", section "Where Beam Saves and Where the Memory Bill
-// Comes In").  One workgroup per token, 8 consecutive columns per thread.
+// Comes In").  8 consecutive columns per thread.
 //
 // combine_residual also applies the step after the block: the post-sublayer
 // RMSNorm of SandwichNorm and the depth-scaled FP32 residual stream
@@ -40,6 +40,73 @@ __device__ __forceinline__ void load8<float>(const float* p, float* v) {
   }
 }
 
+template <typename YT>
+__device__ __forceinline__ void store_out(void* out, int64_t at, const float* acc, bool bf16) {
+  if (bf16) {
+    u32x4 q;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      q[i] = static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * i + 1])) << 16);
+    st16(static_cast<uint16_t*>(out) + at, q);
+  } else {
+    float* o = static_cast<float*>(out) + at;
+    st16(o, u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]),
+                  __float_as_uint(acc[2]), __float_as_uint(acc[3])});
+    st16(o + 4, u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]),
+                      __float_as_uint(acc[6]), __float_as_uint(acc[7])});
+  }
+}
+
+// Columns c .. c + 7 of token t.
+template <typename YT, bool OUT_BF16>
+__device__ __forceinline__ void combine_cols(const YT* __restrict__ y,
+                                             const int32_t* __restrict__ slot_of,
+                                             const float* __restrict__ w, void* __restrict__ out,
+                                             int K, int H, int64_t t, int c) {
+  constexpr int kMaxK = 16;
+  float v[kMaxK][8];
+#pragma unroll
+  for (int k = 0; k < kMaxK; ++k)
+    if (k < K) load8<YT>(y + static_cast<int64_t>(slot_of[t * K + k]) * H + c, v[k]);
+  float acc[8] = {};
+#pragma unroll
+  for (int k = 0; k < kMaxK; ++k) {
+    if (k < K) {
+      const float wk = w[t * K + k];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wk, v[k][i], acc[i]);
+    }
+  }
+  if (OUT_BF16) {
+    u32x4 q;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      q[i] = static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * i + 1])) << 16);
+    st16(static_cast<uint16_t*>(out) + t * H + c, q);
+  } else {
+    float* o = static_cast<float*>(out) + t * H + c;
+    st16(o, u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]),
+                  __float_as_uint(acc[2]), __float_as_uint(acc[3])});
+    st16(o + 4, u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]),
+                      __float_as_uint(acc[6]), __float_as_uint(acc[7])});
+  }
+}
+
+// Small batches: workgroup (t, j) sums token t's columns 1024 j .. 1024 j +
+// 1023, so that a decode batch still fills the chip, with the K rows' loads
+// all issued before the sums (which run in rank order).
+template <typename YT, bool OUT_BF16>
+__global__ __launch_bounds__(128) void combine_split(
+    const YT* __restrict__ y, const int32_t* __restrict__ slot_of,
+    const float* __restrict__ w, void* __restrict__ out, int K, int H) {
+  const int c = (blockIdx.y * 128 + threadIdx.x) * 8;
+  if (c < H) combine_cols<YT, OUT_BF16>(y, slot_of, w, out, K, H, blockIdx.x, c);
+}
+
+// Large batches: one workgroup per token, the same sums column group by
+// column group (fewer registers per thread than combine_split).
 template <typename YT, bool OUT_BF16>
 __global__ __launch_bounds__(128) void combine(
     const YT* __restrict__ y, const int32_t* __restrict__ slot_of,
@@ -59,40 +126,10 @@ __global__ __launch_bounds__(128) void combine(
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wk[k], v[i], acc[i]);
     }
-    if (OUT_BF16) {
-      u32x4 q;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        q[i] = static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * i])) |
-               (static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * i + 1])) << 16);
-      st16(static_cast<uint16_t*>(out) + t * H + c, q);
-    } else {
-      float* o = static_cast<float*>(out) + t * H + c;
-      st16(o, u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]),
-                    __float_as_uint(acc[2]), __float_as_uint(acc[3])});
-      st16(o + 4, u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]),
-                        __float_as_uint(acc[6]), __float_as_uint(acc[7])});
-    }
+    store_out<YT>(out, t * H + c, acc, OUT_BF16);
   }
 }
 
-template <typename YT>
-__device__ __forceinline__ void store_out(void* out, int64_t at, const float* acc, bool bf16) {
-  if (bf16) {
-    u32x4 q;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      q[i] = static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * i])) |
-             (static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * i + 1])) << 16);
-    st16(static_cast<uint16_t*>(out) + at, q);
-  } else {
-    float* o = static_cast<float*>(out) + at;
-    st16(o, u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]),
-                  __float_as_uint(acc[2]), __float_as_uint(acc[3])});
-    st16(o + 4, u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]),
-                      __float_as_uint(acc[6]), __float_as_uint(acc[7])});
-  }
-}
 
 constexpr int kCombineThreads = 128;
 
@@ -160,6 +197,11 @@ hipError_t launch_combine(const Plan& p, const int32_t* slot_of,
                           const float* w, void* out, void* ws, hipStream_t s,
                           Timer* tm, const Epilogue* ep) {
   const dim3 grid(static_cast<unsigned>(p.T)), block(128);
+  // below 2K tokens several workgroups per token (combine_split; measured
+  // at 64 tokens: 23 -> under 20 us); at 16K combine_split takes 0.36 ms
+  // against 0.30 for combine
+  const bool split = p.T < 2048;
+  const dim3 grid_cols(static_cast<unsigned>(p.T), static_cast<unsigned>(ceil_div(p.H, 1024)));
   const bool y_f32 = p.wdt == BEAM_F32 || p.wdt == BEAM_MXFP4 || p.stream_path;
   const bool out_bf16 = p.act == BEAM_BF16;
   if (ep) {
@@ -178,19 +220,23 @@ hipError_t launch_combine(const Plan& p, const int32_t* slot_of,
 #undef BEAM_COMBINE_RES
     return hipGetLastError();
   }
+#define BEAM_COMBINE(YT, OB, YP)                                                             \
+  do {                                                                                       \
+    if (split)                                                                               \
+      BEAM_LAUNCH(tm, "combine", (combine_split<YT, OB>), grid_cols, block, 0, s, YP, slot_of, \
+                  w, out, p.K, p.H);                                                         \
+    else                                                                                     \
+      BEAM_LAUNCH(tm, "combine", (combine<YT, OB>), grid, block, 0, s, YP, slot_of, w, out,   \
+                  p.K, p.H);                                                                 \
+  } while (0)
   if (y_f32) {
     const float* y = ws_at<float>(ws, p.off_y);
-    if (out_bf16)
-      BEAM_LAUNCH(tm, "combine", (combine<float, true>), grid, block, 0, s, y, slot_of, w, out, p.K, p.H);
-    else
-      BEAM_LAUNCH(tm, "combine", (combine<float, false>), grid, block, 0, s, y, slot_of, w, out, p.K, p.H);
+    if (out_bf16) BEAM_COMBINE(float, true, y); else BEAM_COMBINE(float, false, y);
   } else {
     const uint16_t* y = ws_at<uint16_t>(ws, p.off_y);
-    if (out_bf16)
-      BEAM_LAUNCH(tm, "combine", (combine<uint16_t, true>), grid, block, 0, s, y, slot_of, w, out, p.K, p.H);
-    else
-      BEAM_LAUNCH(tm, "combine", (combine<uint16_t, false>), grid, block, 0, s, y, slot_of, w, out, p.K, p.H);
+    if (out_bf16) BEAM_COMBINE(uint16_t, true, y); else BEAM_COMBINE(uint16_t, false, y);
   }
+#undef BEAM_COMBINE
   return hipGetLastError();
 }
 

@@ -75,7 +75,8 @@ typedef enum {
  * expert's last tile holding up to 288).  Every tile
  * height gives bit-identical outputs; the two paths agree within the layer
  * tolerance (they sum in different orders, and bf16 streaming keeps y in
- * fp32).  The flags exist for measurement and tests. */
+ * fp32).  The flags exist for measurement and tests; at most one of the
+ * BEAM_TILE_* flags, and not both path flags (else BEAM_ERR_INVALID_ARG). */
 #define BEAM_PATH_STREAM (1u << 1)     /* force the weight-streaming expert path (bf16, MXFP4) */
 #define BEAM_PATH_GROUPED (1u << 2)    /* force the tiled grouped-GEMM expert path */
 #define BEAM_TILE_128 (1u << 3)        /* grouped path: force 128-row M tiles */

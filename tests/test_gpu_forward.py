@@ -183,3 +183,18 @@ def test_zero_tokens_and_small_workspace():
                                 gl._p(ws.buf), 256, gl._stream())
         gl._check(st, "forward")
     assert ei.value.status == gl.ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("top_k,topk_groups", [(1, 1), (16, 4)])
+@pytest.mark.parametrize("T", [300, 2100])
+@pytest.mark.parametrize("path", [gl.PATH_STREAM, gl.PATH_GROUPED])
+def test_top_k_bounds(top_k, topk_groups, T, path):
+    # the smallest and the largest K the boundary accepts, on both expert
+    # paths and both combine forms (several workgroups per token below 2K
+    # tokens, one above), sampled rows against the oracle
+    sh = small_shape(top_k=top_k, topk_groups=topk_groups)
+    w = WORKLOADS["prefill4k"]
+    inp = make_inputs(w, device=device(), tokens=T, shape=sh, seed=120 + T + top_k)
+    rows = np.arange(0, T, 7)
+    _check(inp, sh, desc_for(w, sh, path), rows, BF16_TOL,
+           f"top_k={top_k} T={T} path={path}")

@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time K replays of the step captured in a HIP graph")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain 4 GiB device copy instead (the known-size "
                          "kernel that scales HBM byte counters)")
@@ -210,6 +212,34 @@ def cpu_baseline(inp, shape, seconds):
                       f"threads (host copies of the touched experts excluded)"}
 
 
+def graph_timing(step, stream, steps, T):
+    """Capture one step in a HIP graph (torch.cuda.CUDAGraph) and time `steps`
+    replays on `stream` with events, as the eager steps are timed."""
+    import numpy as np
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        g.replay()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[-1]) / steps
+    med = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+    return {"ms_per_step": ms, "value": T / (ms * 1e-3), "step_ms_median": med}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -260,6 +290,7 @@ def main():
     torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[-1]) / a.steps
     step_ms = np.sort([ev[i].elapsed_time(ev[i + 1]) for i in range(a.steps)])
+    graph = graph_timing(step, stream, a.steps, T) if a.graph else None
     sclk = read_sclk()
     per = {}
     for name, kms in timer.records():
@@ -322,6 +353,8 @@ def main():
                     "max_over_mean_load": float(counts.max() / counts.mean())},
         "kernels_ms": kern_ms,
     }
+    if graph is not None:
+        res["graph"] = graph
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, sh, a.cpu_seconds)
     print(json.dumps(res), flush=True)

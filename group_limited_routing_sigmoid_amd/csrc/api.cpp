@@ -72,8 +72,9 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
     while (p->ks < 16 && tiles * p->ks < 256 && (3 * p->H / 64) % (2 * p->ks) == 0)
       p->ks *= 2;
   } else if (p->act == BEAM_BF16 && p->E % 32 == 0) {
-    const int64_t waves = ceil_div(T, 32) * ceil_div(p->E, 64);
-    while (p->ks < 16 && waves * p->ks < 1024 && (p->H / 16) % (2 * p->ks) == 0)
+    // four waves per workgroup, each taking a quarter of the split's columns
+    const int64_t waves = ceil_div(T, 32) * ceil_div(p->E, 64) * 4;
+    while (p->ks < 16 && waves * p->ks < 2048 && (p->H / 16) % (8 * p->ks) == 0)
       p->ks *= 2;
   }
   // Very few tokens per expert: stream each touched expert's weights once.

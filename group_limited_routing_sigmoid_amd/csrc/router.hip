@@ -48,43 +48,66 @@ __device__ __forceinline__ void split3(const float* w, bf16x8& hi, bf16x8& mid,
   }
 }
 
-// grid (ceil(T/32), ceil(E/64), ks), one wave: 32 tokens x 64 experts (32
+// grid (ceil(T/32), ceil(E/64), ks), four waves: 32 tokens x 64 experts (32
 // in the last block when E % 64 == 32) over columns [z*kchunk, (z+1)*kchunk)
-// of H.
-__global__ __launch_bounds__(64) void router_logits_mfma(
+// of H.  Wave w takes the w-th quarter of those columns; the four partial
+// tiles meet in LDS and are added in wave order.  With few tokens the
+// kernel is bound by how much of W_r is in flight, so each wave issues the
+// loads of four 16-column steps before their products.
+constexpr int kLgWaves = 4;
+
+__global__ __launch_bounds__(kLgWaves * kWave) void router_logits_mfma(
     const uint16_t* __restrict__ x, const float* __restrict__ wr,
     float* __restrict__ part, int64_t T, int H, int E, int kchunk) {
-  const int lane = threadIdx.x;
+  __shared__ float red[kLgWaves - 1][2][16][kWave];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 32;
   const int e0 = blockIdx.y * 64;
   const int z = blockIdx.z;
-  const int kb = z * kchunk + 8 * (lane / 32);
+  const int kq = kchunk / kLgWaves;
+  const int kb = z * kchunk + wave * kq + 8 * (lane / 32);
   int64_t tr = t0 + (lane % 32);
   if (tr > T - 1) tr = T - 1;
   const uint16_t* xp = x + tr * H + kb;
-  const bool has1 = e0 + 32 < E;  // second 32 experts of the block (wave-uniform)
+  // without a second 32-expert half the wave reads the first half twice and
+  // stores one (keeps the loop free of branches)
+  const bool has1 = e0 + 32 < E;  // wave-uniform
   const float* wp0 = wr + static_cast<int64_t>(e0 + lane % 32) * H + kb;
   const float* wp1 = wr + static_cast<int64_t>(has1 ? e0 + 32 + lane % 32 : e0 + lane % 32) * H + kb;
   f32x16 acc0 = {}, acc1 = {};
-#pragma unroll 2
-  for (int k = 0; k < kchunk; k += 16) {
+#pragma unroll 4
+  for (int k = 0; k < kq; k += 16) {
     const bf16x8 a = as_bf16x8(ld16(xp + k));
     float w0[8], w1[8];
     *reinterpret_cast<u32x4*>(w0) = ld16(wp0 + k);
     *reinterpret_cast<u32x4*>(w0 + 4) = ld16(wp0 + k + 4);
-    bf16x8 h0, m0, l0;
+    *reinterpret_cast<u32x4*>(w1) = ld16(wp1 + k);
+    *reinterpret_cast<u32x4*>(w1 + 4) = ld16(wp1 + k + 4);
+    bf16x8 h0, m0, l0, h1, m1, l1;
     split3(w0, h0, m0, l0);
+    split3(w1, h1, m1, l1);
     acc0 = mfma32x32x16(a, l0, acc0);
+    acc1 = mfma32x32x16(a, l1, acc1);
     acc0 = mfma32x32x16(a, m0, acc0);
+    acc1 = mfma32x32x16(a, m1, acc1);
     acc0 = mfma32x32x16(a, h0, acc0);
-    if (has1) {
-      *reinterpret_cast<u32x4*>(w1) = ld16(wp1 + k);
-      *reinterpret_cast<u32x4*>(w1 + 4) = ld16(wp1 + k + 4);
-      bf16x8 h1, m1, l1;
-      split3(w1, h1, m1, l1);
-      acc1 = mfma32x32x16(a, l1, acc1);
-      acc1 = mfma32x32x16(a, m1, acc1);
-      acc1 = mfma32x32x16(a, h1, acc1);
+    acc1 = mfma32x32x16(a, h1, acc1);
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      red[wave - 1][0][r][lane] = acc0[r];
+      red[wave - 1][1][r][lane] = acc1[r];
+    }
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < kLgWaves - 1; ++w) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      acc0[r] = acc0[r] + red[w][0][r][lane];
+      acc1[r] = acc1[r] + red[w][1][r][lane];
     }
   }
   float* out = part + static_cast<int64_t>(z) * T * E;
@@ -188,91 +211,166 @@ __device__ __forceinline__ uint64_t rank_key(float u, int e) {
 
 constexpr int kSelWaves = 4;
 constexpr int kMaxE = 1024;
+constexpr int kMaxKs = 16;   // the plan splits the router's reduction at most 16 ways
 constexpr int kMaxG = 64;
 
-// grid ceil(T/4), block 256: wave w routes token 4*blockIdx.x + w.
-template <int EPL>
+// ---- wave-wide helpers for the selection --------------------------------
+
+// 64-bit DPP move (both halves with the same lane pattern)
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(v >> 32), CTRL, 0xF, 0xF, false);
+  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(v), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(v >> 32), l);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Maximum over the wave, returned uniform.  Within each row of 16 lanes:
+// swap neighbours, swap pairs (quad permutations), mirror the half rows,
+// mirror the row; every lane then holds its row's maximum, and the four
+// rows' maxima are read out lane by lane.  Needs every lane active.
+__device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
+  v = max64(v, dpp64<0xB1>(v));   // quad_perm(1, 0, 3, 2)
+  v = max64(v, dpp64<0x4E>(v));   // quad_perm(2, 3, 0, 1)
+  v = max64(v, dpp64<0x141>(v));  // row_half_mirror
+  v = max64(v, dpp64<0x140>(v));  // row_mirror
+  return max64(max64(readlane64(v, 0), readlane64(v, 16)),
+               max64(readlane64(v, 32), readlane64(v, 48)));
+}
+
+// grid ceil(T/4), block 256: wave w routes token 4*blockIdx.x + w, holding
+// EPL experts per lane in registers (lane l: experts l*EPL .. l*EPL+EPL-1).
+// KS is 1 (one partial per logit) or kMaxKs (ks <= kMaxKs partials).  SEG:
+// a group's experts are the L = gs/EPL lanes of one aligned power-of-two
+// segment, so group maxima are butterflies within the segment; otherwise
+// lane g scans group g's biased scores from LDS (one pad word per 32 keeps
+// the scan's lanes on distinct banks).
+__device__ __forceinline__ int upad(int e) { return e + (e >> 5); }
+
+template <int EPL, int KS, bool SEG>
 __global__ __launch_bounds__(256) void router_select(
     const float* __restrict__ part, int ks, int64_t T, int E, int G, int TG,
     int K, int topn, float scale, const float* __restrict__ bias,
     float* __restrict__ logits_out, int32_t* __restrict__ idx_out,
     float* __restrict__ w_out) {
-  __shared__ float s_sh[kSelWaves][kMaxE];
-  __shared__ float u_sh[kSelWaves][kMaxE];
-  __shared__ float g_sh[kSelWaves][kMaxG];
-  __shared__ int keep_sh[kSelWaves][kMaxG];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kSelWaves + wave;
-  const bool valid = t < T;
+  const bool valid = t < T;   // wave-uniform
+  const int64_t tc = valid ? t : T - 1;
   const int gs = E / G;
+  const float ninf = -__builtin_huge_valf();
 
-  // 1. logits (fixed-order sum of partials), scores, biased scores
+  // 1. logits (fixed-order sum of the partials), scores, biased scores.
+  // Every load is issued before the first add: indices are clamped into
+  // range instead of branched on, and the clamped values are not used.
+  float pz[EPL][KS], bz[EPL], sv[EPL], u[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = min(lane * EPL + j, E - 1);
+#pragma unroll
+    for (int z = 0; z < KS; ++z)
+      pz[j][z] = part[(static_cast<int64_t>(min(z, ks - 1)) * T + tc) * E + e];
+    bz[j] = bias ? bias[e] : 0.0f;
+  }
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane * EPL + j;
-    if (valid && e < E) {
-      float l = part[t * E + e];
-      for (int z = 1; z < ks; ++z) l = l + part[(static_cast<int64_t>(z) * T + t) * E + e];
-      if (logits_out) logits_out[t * E + e] = l;
-      const float s = sigmoid32(l);
-      s_sh[wave][e] = s;
-      u_sh[wave][e] = s + (bias ? bias[e] : 0.0f);
-    }
+    float l = pz[j][0];
+#pragma unroll
+    for (int z = 1; z < KS; ++z)
+      if (z < ks) l = l + pz[j][z];
+    sv[j] = sigmoid32(l);
+    u[j] = e < E ? sv[j] + bz[j] : ninf;
+    if (valid && e < E && logits_out) logits_out[t * E + e] = l;
   }
-  __syncthreads();
-  // 2. group scores: sum of the topn (1 or 2) largest biased scores
-  if (valid && lane < G) {
-    float t1 = -__builtin_huge_valf(), t2 = -__builtin_huge_valf();
-    for (int j = 0; j < gs; ++j) {
-      const float v = u_sh[wave][lane * gs + j];
-      if (v > t1) {
+
+  // 2. group scores: sum of the topn (1 or 2) largest biased scores (a
+  // repeated value counts twice).  gsc ends in lane g for group g.
+  float gsc = ninf;
+  if constexpr (SEG) {
+    float t1 = ninf, t2 = ninf;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      if (u[j] > t1) {
         t2 = t1;
-        t1 = v;
-      } else if (v > t2) {
-        t2 = v;
+        t1 = u[j];
+      } else if (u[j] > t2) {
+        t2 = u[j];
       }
     }
-    g_sh[wave][lane] = (topn == 1) ? t1 : t1 + t2;
-  }
-  __syncthreads();
-  // 3. keep the TG best groups (ties: lower group id)
-  if (valid && lane < G) {
-    const float mine = g_sh[wave][lane];
-    int rank = 0;
-    for (int g = 0; g < G; ++g) {
-      const float o = g_sh[wave][g];
-      rank += (o > mine) || (o == mine && g < lane);
+    const int L = gs / EPL;
+    for (int off = 1; off < L; off <<= 1) {
+      const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
+      const float n2 = fmaxf(fminf(t1, o1), fmaxf(t2, o2));
+      t1 = fmaxf(t1, o1);
+      t2 = n2;
     }
-    keep_sh[wave][lane] = rank < TG;
+    const float mine = (topn == 1) ? t1 : t1 + t2;
+    gsc = __shfl(mine, min(lane, G - 1) * L);
+  } else {
+    __shared__ float u_sh[kSelWaves][kMaxE + kMaxE / 32];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane * EPL + j;
+      if (e < E) u_sh[wave][upad(e)] = u[j];
+    }
+    __syncthreads();
+    if (lane < G) {
+      float t1 = ninf, t2 = ninf;
+      for (int j = 0; j < gs; ++j) {
+        const float v = u_sh[wave][upad(lane * gs + j)];
+        if (v > t1) {
+          t2 = t1;
+          t1 = v;
+        } else if (v > t2) {
+          t2 = v;
+        }
+      }
+      gsc = (topn == 1) ? t1 : t1 + t2;
+    }
   }
-  __syncthreads();
   if (!valid) return;
+
+  // 3. keep the TG best groups (ties: lower group id): bit g of `keep`
+  int rank = 0;
+  for (int g = 0; g < G; ++g) {
+    const float o = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gsc), g));
+    rank += (o > gsc) || (o == gsc && g < lane);
+  }
+  const uint64_t keep = __ballot(lane < G && rank < TG);
+
   // 4. top-K of the eligible experts by biased score, rank order
   uint64_t key[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane * EPL + j;
-    key[j] = (e < E && keep_sh[wave][e / gs]) ? rank_key(u_sh[wave][e], e) : 0;
+    key[j] = (e < E && ((keep >> (e / gs)) & 1)) ? rank_key(u[j], e) : 0;
   }
   float D = 0.0f, my_s = 0.0f;
   int my_e = 0;
   for (int k = 0; k < K; ++k) {
     uint64_t best = 0;
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) best = key[j] > best ? key[j] : best;
-#pragma unroll
-    for (int off = kWave / 2; off >= 1; off >>= 1) {
-      const uint64_t o = __shfl_xor(best, off);
-      best = o > best ? o : best;
-    }
+    for (int j = 0; j < EPL; ++j) best = max64(best, key[j]);
+    best = wave_max64(best);
     // K <= TG*E/G eligible experts always remain, so best != 0; the clamp
-    // only keeps the LDS read below in bounds.
+    // only keeps the lane index below in range.
     int e = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best));
     e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+    float se = sv[0];
 #pragma unroll
-    for (int j = 0; j < EPL; ++j)
+    for (int j = 0; j < EPL; ++j) {
       if (lane * EPL + j == e) key[j] = 0;
-    const float sk = s_sh[wave][e];
+      if (j == e % EPL) se = sv[j];
+    }
+    const float sk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, se), e / EPL));
     D = (k == 0) ? sk : D + sk;
     if (lane == k) {
       my_e = e;
@@ -308,7 +406,7 @@ hipError_t launch_router(const Plan& p, const void* x, const float* w_router,
       if (e != hipSuccess) return e;
     } else if (p.act == BEAM_BF16 && p.E % 32 == 0) {
       dim3 grid(static_cast<unsigned>(ceil_div(p.T, 32)), static_cast<unsigned>(ceil_div(p.E, 64)), ks);
-      BEAM_LAUNCH(tm, "router_logits_mfma", router_logits_mfma, grid, dim3(64), 0, s,
+      BEAM_LAUNCH(tm, "router_logits_mfma", router_logits_mfma, grid, dim3(kLgWaves * kWave), 0, s,
                          static_cast<const uint16_t*>(x), w_router, buf, p.T,
                          p.H, p.E, kchunk);
     } else {
@@ -321,16 +419,29 @@ hipError_t launch_router(const Plan& p, const void* x, const float* w_router,
   }
   const float* lo = logits_in ? nullptr : logits_out;
   dim3 grid(static_cast<unsigned>(ceil_div(p.T, kSelWaves)));
-#define BEAM_SEL(EPL)                                                          \
-  BEAM_LAUNCH(tm, "router_select", router_select<EPL>, grid, dim3(256), 0, s, part, ks, p.T, \
-                     p.E, p.G, p.TG, p.K, p.topn, p.scale, bias,              \
-                     const_cast<float*>(lo), idx, w)
   const int epl = static_cast<int>(ceil_div(p.E, kWave));
-  if (epl <= 1) BEAM_SEL(1);
-  else if (epl <= 2) BEAM_SEL(2);
-  else if (epl <= 4) BEAM_SEL(4);
-  else if (epl <= 8) BEAM_SEL(8);
+  const int eplp = epl <= 1 ? 1 : epl <= 2 ? 2 : epl <= 4 ? 4 : epl <= 8 ? 8 : 16;
+  const int gs = p.E / p.G, seg_l = gs / eplp;
+  const bool seg = gs % eplp == 0 && (seg_l & (seg_l - 1)) == 0;
+#define BEAM_SEL3(EPL, KS, SEG)                                                \
+  BEAM_LAUNCH(tm, "router_select", (router_select<EPL, KS, SEG>), grid, dim3(256), 0, s, part, \
+              ks, p.T, p.E, p.G, p.TG, p.K, p.topn, p.scale, bias,            \
+              const_cast<float*>(lo), idx, w)
+#define BEAM_SEL(EPL)                                                          \
+  do {                                                                         \
+    if (ks == 1) {                                                             \
+      if (seg) BEAM_SEL3(EPL, 1, true); else BEAM_SEL3(EPL, 1, false);         \
+    } else {                                                                   \
+      if (seg) BEAM_SEL3(EPL, kMaxKs, true); else BEAM_SEL3(EPL, kMaxKs, false); \
+    }                                                                          \
+  } while (0)
+  if (ks > kMaxKs) return hipErrorInvalidValue;
+  if (eplp == 1) BEAM_SEL(1);
+  else if (eplp == 2) BEAM_SEL(2);
+  else if (eplp == 4) BEAM_SEL(4);
+  else if (eplp == 8) BEAM_SEL(8);
   else BEAM_SEL(16);
+#undef BEAM_SEL3
 #undef BEAM_SEL
   return hipGetLastError();
 }

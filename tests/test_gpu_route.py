@@ -93,3 +93,33 @@ def test_route_deterministic_and_permutation_invariant():
     c = gl.route(d, inp.x[perm].contiguous(), inp.w_router, inp.bias)
     for u, v in zip(a, c):
         assert torch.equal(u[perm], v)
+
+
+@pytest.mark.parametrize("E,G,TG,K,topn", [
+    (16, 4, 2, 4, 2),      # a group is 4 lanes of one expert each
+    (24, 3, 2, 4, 2),      # 8-lane groups, lanes 24..63 hold no expert
+    (48, 4, 2, 6, 2),      # 12 experts per group: not a power-of-two lane segment
+    (100, 10, 3, 7, 1),    # two experts per lane, 5-lane groups (not a power of two)
+    (160, 5, 2, 8, 2),     # four experts per lane (rounded up from three)
+    (192, 64, 8, 8, 2),    # 3 experts per group, four per lane: groups straddle lanes
+    (512, 16, 4, 8, 2),    # eight experts per lane, 4-lane groups
+    (1024, 64, 16, 16, 2), # sixteen experts per lane, one lane per group
+    (1024, 64, 1, 16, 1),  # a single kept group of 16
+])
+def test_route_logits_in_group_layouts(E, G, TG, K, topn):
+    # every expert-to-lane layout of the selection kernel, from given logits
+    # on a coarse grid (many ties) and a coarse bias
+    dev = device()
+    sh = dataclasses.replace(BEAM, n_experts=E, n_groups=G, topk_groups=TG, top_k=K,
+                             group_score_topn=topn)
+    rng = np.random.default_rng(E * 131 + G)
+    T = 300
+    lg = (np.round(rng.standard_normal((T, E)) * 2) / 2).astype(np.float32)
+    lg[:5] = 0.0
+    bias = (np.round(rng.standard_normal(E) * 8) / 256).astype(np.float32)
+    d = gl.make_desc(sh, gl.BF16, gl.BF16, gl.ROUTE_LOGITS_IN)
+    idx, w, _ = gl.route(d, None, None, torch.as_tensor(bias, device=dev),
+                         logits=torch.as_tensor(lg, device=dev))
+    oi, ow, _ = oracle.route(sh, lg, bias)
+    np.testing.assert_array_equal(idx.cpu().numpy(), oi)
+    np.testing.assert_array_equal(w.cpu().numpy().view(np.uint32), ow.view(np.uint32))

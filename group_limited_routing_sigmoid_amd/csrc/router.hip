@@ -256,8 +256,8 @@ __device__ __forceinline__ int upad(int e) { return e + (e >> 5); }
 
 template <int EPL, int KS, bool SEG>
 __global__ __launch_bounds__(256) void router_select(
-    const float* __restrict__ part, int ks, int64_t T, int E, int G, int TG,
-    int K, int topn, float scale, const float* __restrict__ bias,
+    const float* __restrict__ part, int ks, int vec4, int64_t T, int E, int G,
+    int TG, int K, int topn, float scale, const float* __restrict__ bias,
     float* __restrict__ logits_out, int32_t* __restrict__ idx_out,
     float* __restrict__ w_out) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -270,15 +270,31 @@ __global__ __launch_bounds__(256) void router_select(
   // 1. logits (fixed-order sum of the partials), scores, biased scores.
   // Every load is issued before the first add: indices are clamped into
   // range instead of branched on, and the clamped values are not used.
+  // With vec4 (E % 4 == 0: 16-byte aligned rows) a lane's experts come four
+  // to a 16-byte load.
   float pz[EPL][KS], bz[EPL], sv[EPL], u[EPL];
+  if (EPL % 4 == 0 && vec4) {
 #pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    const int e = min(lane * EPL + j, E - 1);
+    for (int j = 0; j < EPL; j += 4) {
+      const int e = min(lane * EPL + j, E - 4);
 #pragma unroll
-    for (int z = 0; z < KS; ++z)
-      pz[j][z] = part[(static_cast<int64_t>(min(z, ks - 1)) * T + tc) * E + e];
-    bz[j] = bias ? bias[e] : 0.0f;
+      for (int z = 0; z < KS; ++z) {
+        const u32x4 v = ld16(part + (static_cast<int64_t>(min(z, ks - 1)) * T + tc) * E + e);
+#pragma unroll
+        for (int q = 0; q < 4 && j + q < EPL; ++q) pz[j + q][z] = __uint_as_float(v[q]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = min(lane * EPL + j, E - 1);
+#pragma unroll
+      for (int z = 0; z < KS; ++z)
+        pz[j][z] = part[(static_cast<int64_t>(min(z, ks - 1)) * T + tc) * E + e];
+    }
   }
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) bz[j] = bias ? bias[min(lane * EPL + j, E - 1)] : 0.0f;
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane * EPL + j;
@@ -423,9 +439,12 @@ hipError_t launch_router(const Plan& p, const void* x, const float* w_router,
   const int eplp = epl <= 1 ? 1 : epl <= 2 ? 2 : epl <= 4 ? 4 : epl <= 8 ? 8 : 16;
   const int gs = p.E / p.G, seg_l = gs / eplp;
   const bool seg = gs % eplp == 0 && (seg_l & (seg_l - 1)) == 0;
+  // partials live in the workspace and given logits are 16-byte aligned
+  // (checked at the boundary), so rows of E % 4 == 0 floats are too
+  const int vec4 = p.E % 4 == 0;
 #define BEAM_SEL3(EPL, KS, SEG)                                                \
   BEAM_LAUNCH(tm, "router_select", (router_select<EPL, KS, SEG>), grid, dim3(256), 0, s, part, \
-              ks, p.T, p.E, p.G, p.TG, p.K, p.topn, p.scale, bias,            \
+              ks, vec4, p.T, p.E, p.G, p.TG, p.K, p.topn, p.scale, bias,      \
               const_cast<float*>(lo), idx, w)
 #define BEAM_SEL(EPL)                                                          \
   do {                                                                         \

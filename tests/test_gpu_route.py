@@ -118,8 +118,8 @@ def test_route_logits_in_group_layouts(E, G, TG, K, topn):
     lg[:5] = 0.0
     bias = (np.round(rng.standard_normal(E) * 8) / 256).astype(np.float32)
     d = gl.make_desc(sh, gl.BF16, gl.BF16, gl.ROUTE_LOGITS_IN)
+    oi, ow, _ = oracle.route(sh, lg, bias)
     idx, w, _ = gl.route(d, None, None, torch.as_tensor(bias, device=dev),
                          logits=torch.as_tensor(lg, device=dev))
-    oi, ow, _ = oracle.route(sh, lg, bias)
     np.testing.assert_array_equal(idx.cpu().numpy(), oi)
     np.testing.assert_array_equal(w.cpu().numpy().view(np.uint32), ow.view(np.uint32))

@@ -14,6 +14,9 @@
 //                 grouped-GEMM M-tile list (with each expert's first tile)
 //                 and the list of active experts.
 //   perm_scatter  slot = offsets[e] + block base + rank.
+//   perm_small    T <= 256 (one block of tokens): the three steps above in
+//                 one workgroup, the bit matrix kept in LDS throughout (the
+//                 same slots; two launches fewer for decode batches).
 //   bias_update   the expert-bias balancing step on the same histogram idea
 //                 ("Reflection AI Introduces Beam ...", load-balancing
 //                 paragraph; DeepSeek-V3's bias-update rule).
@@ -123,6 +126,62 @@ __global__ __launch_bounds__(kPermBlock) void perm_scatter(
   }
 }
 
+// one block of 1024 threads: thread t < T marks and places token t, thread
+// e < E counts and scans expert e
+__global__ __launch_bounds__(kMaxE) void perm_small(
+    const int32_t* __restrict__ idx, int T, int K, int E, int bm, int xt,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ meta, int32_t* __restrict__ active,
+    int32_t* __restrict__ tile_off, int32_t* __restrict__ slot_token,
+    int32_t* __restrict__ slot_of) {
+  __shared__ uint32_t bits[kMaxE * kWords];
+  __shared__ int sh[kMaxE];
+  __shared__ int off_sh[kMaxE];
+  const int i = threadIdx.x;
+  for (int j = i; j < E * kWords; j += kMaxE) bits[j] = 0;
+  __syncthreads();
+  if (i < T)
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[i * K + k];
+      atomicOr(&bits[e * kWords + i / 32], 1u << (i % 32));
+    }
+  __syncthreads();
+  int c = 0;
+  if (i < E)
+#pragma unroll
+    for (int w = 0; w < kWords; ++w) c += __popc(bits[i * kWords + w]);
+  const int incl = block_scan_incl(c, sh);
+  const int off = incl - c;
+  const int nt = (c <= 0) ? 0 : max(1, (c - xt + bm - 1) / bm);
+  const int tincl = block_scan_incl(nt, sh);
+  const int toff = tincl - nt;
+  const int act = c > 0;
+  const int aincl = block_scan_incl(act, sh);
+  if (i < E) {
+    counts[i] = c;
+    offsets[i] = off;
+    off_sh[i] = off;
+    if (act) active[aincl - 1] = i;
+    tile_off[i] = toff;
+  }
+  if (i == E - 1) {
+    offsets[E] = incl;
+    tile_off[E] = tincl;
+    meta[kMetaTiles] = tincl;
+    meta[kMetaActive] = aincl;
+  }
+  __syncthreads();
+  if (i < T)
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[i * K + k];
+      int r = __popc(bits[e * kWords + i / 32] & ((1u << (i % 32)) - 1u));
+      for (int w = 0; w < i / 32; ++w) r += __popc(bits[e * kWords + w]);
+      const int slot = off_sh[e] + r;
+      slot_token[slot] = i;
+      slot_of[i * K + k] = slot;
+    }
+}
+
 // Expert-bias balancing step: one workgroup; integer histogram in LDS, then
 // bias[e] += gamma * sign(T*K - load_e*E) with the sign taken in integers.
 __global__ __launch_bounds__(kMaxE) void bias_update(
@@ -159,6 +218,13 @@ hipError_t launch_permute(const Plan& p, const int32_t* idx, int32_t* counts,
   int32_t* base = ws_at<int32_t>(ws, p.off_base);
   int32_t* rank = ws_at<int32_t>(ws, p.off_rank);
   const unsigned nb = static_cast<unsigned>(p.nb);
+  if (p.T <= kPermBlock) {
+    BEAM_LAUNCH(tm, "perm_small", perm_small, dim3(1), dim3(kMaxE), 0, s, idx,
+                static_cast<int>(p.T), p.K, p.E, p.bm, p.xt, counts, offsets,
+                ws_at<int32_t>(ws, p.off_meta), ws_at<int32_t>(ws, p.off_active),
+                ws_at<int32_t>(ws, p.off_tile_off), slot_token, slot_of);
+    return hipGetLastError();
+  }
   BEAM_LAUNCH(tm, "perm_rank", perm_rank, dim3(nb), dim3(kPermBlock), 0, s, idx, p.T,
                      p.K, p.E, hist, rank);
   BEAM_LAUNCH(tm, "perm_scan", perm_scan, dim3(1), dim3(kMaxE), 0, s, hist, p.nb, p.E,

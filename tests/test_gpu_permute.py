@@ -55,3 +55,19 @@ def test_permute_tiny_shape():
     got = gl.permute(d, torch.as_tensor(idx, device=dev))
     for name, w in zip(("counts", "offsets", "slot_token", "slot_of"), _expected(idx, 16)):
         np.testing.assert_array_equal(got[name].cpu().numpy(), w, err_msg=name)
+
+
+@pytest.mark.parametrize("T,E,G,K", [(256, 1024, 64, 16), (200, 1024, 64, 16), (100, 64, 8, 1),
+                                     (3, 96, 3, 16), (700, 1024, 64, 16)])
+def test_permute_expert_and_k_bounds(T, E, G, K):
+    # the most experts and picks per token the boundary accepts, and one pick:
+    # the one-workgroup form (T <= 256) and the three-kernel form (T = 700)
+    import dataclasses
+    dev = device()
+    rng = np.random.default_rng(T + E + K)
+    idx = _random_routing(T, E, K, rng)
+    sh = dataclasses.replace(BEAM, n_experts=E, n_groups=G, topk_groups=G, top_k=K)
+    d = gl.make_desc(sh, gl.BF16, gl.BF16)
+    got = gl.permute(d, torch.as_tensor(idx, device=dev))
+    for name, w in zip(("counts", "offsets", "slot_token", "slot_of"), _expected(idx, E)):
+        np.testing.assert_array_equal(got[name].cpu().numpy(), w, err_msg=name)

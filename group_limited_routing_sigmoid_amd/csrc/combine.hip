@@ -59,12 +59,12 @@ __device__ __forceinline__ void store_out(void* out, int64_t at, const float* ac
 }
 
 // Columns c .. c + 7 of token t.
-template <typename YT, bool OUT_BF16>
+template <typename YT, bool OUT_BF16, int KM>
 __device__ __forceinline__ void combine_cols(const YT* __restrict__ y,
                                              const int32_t* __restrict__ slot_of,
                                              const float* __restrict__ w, void* __restrict__ out,
                                              int K, int H, int64_t t, int c) {
-  constexpr int kMaxK = 16;
+  constexpr int kMaxK = KM;
   float v[kMaxK][8];
 #pragma unroll
   for (int k = 0; k < kMaxK; ++k)
@@ -94,19 +94,20 @@ __device__ __forceinline__ void combine_cols(const YT* __restrict__ y,
   }
 }
 
-// Small batches: workgroup (t, j) sums token t's columns 1024 j .. 1024 j +
-// 1023, so that a decode batch still fills the chip, with the K rows' loads
-// all issued before the sums (which run in rank order).
-template <typename YT, bool OUT_BF16>
+// Workgroup (t, j) sums token t's columns 1024 j .. 1024 j + 1023 (a decode
+// batch still fills the chip), with the K rows' loads all issued before the
+// sums (which run in rank order).  KM bounds K: 8 holds the loads in 64
+// registers per thread, 16 in 128.
+template <typename YT, bool OUT_BF16, int KM>
 __global__ __launch_bounds__(128) void combine_split(
     const YT* __restrict__ y, const int32_t* __restrict__ slot_of,
     const float* __restrict__ w, void* __restrict__ out, int K, int H) {
   const int c = (blockIdx.y * 128 + threadIdx.x) * 8;
-  if (c < H) combine_cols<YT, OUT_BF16>(y, slot_of, w, out, K, H, blockIdx.x, c);
+  if (c < H) combine_cols<YT, OUT_BF16, KM>(y, slot_of, w, out, K, H, blockIdx.x, c);
 }
 
-// Large batches: one workgroup per token, the same sums column group by
-// column group (fewer registers per thread than combine_split).
+// K > 8 on large batches: one workgroup per token, the same sums column
+// group by column group (fewer registers per thread than combine_split<16>).
 template <typename YT, bool OUT_BF16>
 __global__ __launch_bounds__(128) void combine(
     const YT* __restrict__ y, const int32_t* __restrict__ slot_of,
@@ -197,9 +198,10 @@ hipError_t launch_combine(const Plan& p, const int32_t* slot_of,
                           const float* w, void* out, void* ws, hipStream_t s,
                           Timer* tm, const Epilogue* ep) {
   const dim3 grid(static_cast<unsigned>(p.T)), block(128);
-  // below 2K tokens several workgroups per token (combine_split; measured
-  // at 64 tokens: 23 -> under 20 us); at 16K combine_split takes 0.36 ms
-  // against 0.30 for combine
+  // combine_split for K <= 8 at every T (16K tokens: 0.30 ms against 0.32
+  // for one workgroup per token; 8K fp8: 0.154 against 0.166); for larger K
+  // only below 2K tokens (64 tokens: 23 -> under 20 us), as with 16 rows'
+  // loads in flight it took 0.36 ms at 16K against 0.30 for combine
   const bool split = p.T < 2048;
   const dim3 grid_cols(static_cast<unsigned>(p.T), static_cast<unsigned>(ceil_div(p.H, 1024)));
   const bool y_f32 = p.wdt == BEAM_F32 || p.wdt == BEAM_MXFP4 || p.stream_path;
@@ -222,8 +224,11 @@ hipError_t launch_combine(const Plan& p, const int32_t* slot_of,
   }
 #define BEAM_COMBINE(YT, OB, YP)                                                             \
   do {                                                                                       \
-    if (split)                                                                               \
-      BEAM_LAUNCH(tm, "combine", (combine_split<YT, OB>), grid_cols, block, 0, s, YP, slot_of, \
+    if (p.K <= 8)                                                                            \
+      BEAM_LAUNCH(tm, "combine", (combine_split<YT, OB, 8>), grid_cols, block, 0, s, YP, slot_of, \
+                  w, out, p.K, p.H);                                                         \
+    else if (split)                                                                          \
+      BEAM_LAUNCH(tm, "combine", (combine_split<YT, OB, 16>), grid_cols, block, 0, s, YP, slot_of, \
                   w, out, p.K, p.H);                                                         \
     else                                                                                     \
       BEAM_LAUNCH(tm, "combine", (combine<YT, OB>), grid, block, 0, s, YP, slot_of, w, out,   \

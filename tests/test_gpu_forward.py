@@ -190,8 +190,9 @@ def test_zero_tokens_and_small_workspace():
 @pytest.mark.parametrize("path", [gl.PATH_STREAM, gl.PATH_GROUPED])
 def test_top_k_bounds(top_k, topk_groups, T, path):
     # the smallest and the largest K the boundary accepts, on both expert
-    # paths and both combine forms (several workgroups per token below 2K
-    # tokens, one above), sampled rows against the oracle
+    # paths and every combine form (several workgroups per token with 8 or
+    # 16 rows' loads in flight; for K = 16 one workgroup per token from 2K
+    # tokens on), sampled rows against the oracle
     sh = small_shape(top_k=top_k, topk_groups=topk_groups)
     w = WORKLOADS["prefill4k"]
     inp = make_inputs(w, device=device(), tokens=T, shape=sh, seed=120 + T + top_k)

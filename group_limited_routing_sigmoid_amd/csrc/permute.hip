@@ -58,20 +58,34 @@ __global__ __launch_bounds__(kPermBlock) void perm_rank(
     }
 }
 
-// Inclusive scan of v over the 1024 threads of the block (Hillis-Steele).
-__device__ int block_scan_incl(int v, int* sh) {
-  const int i = threadIdx.x;
-  sh[i] = v;
-  __syncthreads();
-  for (int off = 1; off < kMaxE; off <<= 1) {
-    const int a = (i >= off) ? sh[i - off] : 0;
-    __syncthreads();
-    sh[i] += a;
-    __syncthreads();
+// Inclusive scans of three values at once over the 1024 threads of the
+// block: within each wave by shifts of 1, 2, .., 32 lanes, then each wave
+// adds the totals of the waves before it (read from LDS).  Integer sums, so
+// any order gives the same result.
+__device__ void block_scan3_incl(int& a, int& b, int& c) {
+  __shared__ int tot[3][kMaxE / kWave];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int ua = __shfl_up(a, off), ub = __shfl_up(b, off), uc = __shfl_up(c, off);
+    if (lane >= off) {
+      a += ua;
+      b += ub;
+      c += uc;
+    }
   }
-  const int r = sh[i];
+  if (lane == kWave - 1) {
+    tot[0][wave] = a;
+    tot[1][wave] = b;
+    tot[2][wave] = c;
+  }
   __syncthreads();
-  return r;
+  for (int w = 0; w < wave; ++w) {
+    a += tot[0][w];
+    b += tot[1][w];
+    c += tot[2][w];
+  }
+  __syncthreads();
 }
 
 // one block of 1024 threads; thread e handles expert e
@@ -80,22 +94,33 @@ __global__ __launch_bounds__(kMaxE) void perm_scan(
     int32_t* __restrict__ base, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ meta,
     int32_t* __restrict__ active, int32_t* __restrict__ tile_off) {
-  __shared__ int sh[kMaxE];
   const int e = threadIdx.x;
   int c = 0;
-  if (e < E)
-    for (int64_t b = 0; b < nb; ++b) {
+  if (e < E) {
+    // eight blocks' counts loaded before they are added
+    int64_t b = 0;
+    for (; b + 8 <= nb; b += 8) {
+      int hv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) hv[j] = hist[(b + j) * E + e];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        base[(b + j) * E + e] = c;
+        c += hv[j];
+      }
+    }
+    for (; b < nb; ++b) {
       base[b * E + e] = c;
       c += hist[b * E + e];
     }
-  const int incl = block_scan_incl(c, sh);
-  const int off = incl - c;
+  }
   // M tiles of bm rows; the last may hold up to xt more (bm + xt in all)
   const int nt = (c <= 0) ? 0 : max(1, (c - xt + bm - 1) / bm);
-  const int tincl = block_scan_incl(nt, sh);
-  const int toff = tincl - nt;
   const int act = c > 0;
-  const int aincl = block_scan_incl(act, sh);
+  int incl = c, tincl = nt, aincl = act;
+  block_scan3_incl(incl, tincl, aincl);
+  const int off = incl - c;
+  const int toff = tincl - nt;
   if (e < E) {
     counts[e] = c;
     offsets[e] = off;
@@ -135,7 +160,6 @@ __global__ __launch_bounds__(kMaxE) void perm_small(
     int32_t* __restrict__ tile_off, int32_t* __restrict__ slot_token,
     int32_t* __restrict__ slot_of) {
   __shared__ uint32_t bits[kMaxE * kWords];
-  __shared__ int sh[kMaxE];
   __shared__ int off_sh[kMaxE];
   const int i = threadIdx.x;
   for (int j = i; j < E * kWords; j += kMaxE) bits[j] = 0;
@@ -150,13 +174,12 @@ __global__ __launch_bounds__(kMaxE) void perm_small(
   if (i < E)
 #pragma unroll
     for (int w = 0; w < kWords; ++w) c += __popc(bits[i * kWords + w]);
-  const int incl = block_scan_incl(c, sh);
-  const int off = incl - c;
   const int nt = (c <= 0) ? 0 : max(1, (c - xt + bm - 1) / bm);
-  const int tincl = block_scan_incl(nt, sh);
-  const int toff = tincl - nt;
   const int act = c > 0;
-  const int aincl = block_scan_incl(act, sh);
+  int incl = c, tincl = nt, aincl = act;
+  block_scan3_incl(incl, tincl, aincl);
+  const int off = incl - c;
+  const int toff = tincl - nt;
   if (i < E) {
     counts[i] = c;
     offsets[i] = off;

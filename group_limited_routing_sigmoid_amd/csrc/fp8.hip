@@ -12,11 +12,16 @@ namespace {
 // 16 lanes per (row, 128-column block), 8 consecutive columns per lane (one
 // 16-byte load of bf16, two of fp32); a wave covers 4 blocks.  The block's
 // amax is reduced over its 16 lanes; scale = amax / 448 (1 for a zero block),
-// code = e4m3(v / scale) with binary32 division, as in the recipe.
+// code = e4m3(v / scale) with binary32 division, as in the recipe.  With
+// slot_of (x in the forward) each scale also goes to the K slots of its row,
+// block-major: xss[kb * S + slot], so that a tile stage of the grouped
+// products reads the scale words of consecutive slots (one 1 KiB run per
+// 256 rows rather than a cache line per row).
 template <bool BF16>
 __global__ __launch_bounds__(256) void quant_e4m3_rows(
     const void* __restrict__ v, int64_t rows, int64_t cols,
-    uint8_t* __restrict__ q, float* __restrict__ scales) {
+    uint8_t* __restrict__ q, float* __restrict__ scales,
+    const int32_t* __restrict__ slot_of, int K, float* __restrict__ xss, int S) {
   const int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // 8-column group
   const int64_t nbc = cols / 128;
   const int64_t blk = g / 16;
@@ -50,7 +55,13 @@ __global__ __launch_bounds__(256) void quant_e4m3_rows(
   const uint32_t hi = e4m3x4(a[4] / sc, a[5] / sc, a[6] / sc, a[7] / sc);
   if (!live) return;
   *reinterpret_cast<uint2*>(q + at) = make_uint2(lo, hi);
-  if (g % 16 == 0) scales[blk] = sc;
+  if (g % 16 == 0) {
+    scales[blk] = sc;
+    if (xss) {
+      const int64_t row = blk / nbc, kb = blk % nbc;
+      for (int k = 0; k < K; ++k) xss[kb * S + slot_of[row * K + k]] = sc;
+    }
+  }
 }
 
 }  // namespace
@@ -61,30 +72,15 @@ hipError_t launch_quant_e4m3(int64_t rows, int64_t cols, int32_t dtype,
   const int64_t groups = rows * (cols / 128) * 16;
   const dim3 grid(static_cast<unsigned>(ceil_div(groups, 256)));
   if (dtype == BEAM_BF16)
-    BEAM_LAUNCH(tm, "quant_e4m3", quant_e4m3_rows<true>, grid, dim3(256), 0, s, v, rows, cols, q, scales);
+    BEAM_LAUNCH(tm, "quant_e4m3", quant_e4m3_rows<true>, grid, dim3(256), 0, s, v, rows, cols, q,
+                scales, nullptr, 0, nullptr, 0);
   else
-    BEAM_LAUNCH(tm, "quant_e4m3", quant_e4m3_rows<false>, grid, dim3(256), 0, s, v, rows, cols, q, scales);
+    BEAM_LAUNCH(tm, "quant_e4m3", quant_e4m3_rows<false>, grid, dim3(256), 0, s, v, rows, cols, q,
+                scales, nullptr, 0, nullptr, 0);
   return hipGetLastError();
 }
 
 bool fp8_experts_built() { return true; }
-
-namespace {
-
-// x's activation scales by slot, block-major: xss[kb * S + slot] =
-// xs[slot_token[slot] * nkb + kb], so that a tile stage of the grouped
-// products reads the scale words of consecutive slots (one 1 KiB run per
-// 256 rows rather than a cache line per row).
-__global__ __launch_bounds__(256) void slot_scales_fp8(const float* __restrict__ xs,
-                                                       const int32_t* __restrict__ slot_token,
-                                                       float* __restrict__ xss, int S, int nkb) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= static_cast<int64_t>(S) * nkb) return;
-  const int64_t kb = i / S, slot = i % S;
-  xss[i] = xs[static_cast<int64_t>(slot_token[slot]) * nkb + kb];
-}
-
-}  // namespace
 
 namespace {
 
@@ -780,12 +776,11 @@ hipError_t launch_experts_fp8(const Plan& p, const void* x,
   const int32_t* toff = ws_at<int32_t>(ws, p.off_tile_off);
   const int32_t* meta = ws_at<int32_t>(ws, p.off_meta);
   float* xss = ws_at<float>(ws, p.off_xss);
-  hipError_t e = launch_quant_e4m3(p.T, p.H, BEAM_BF16, x, xq, xs, s, tm);
-  if (e != hipSuccess) return e;
+  const int32_t* slot_of = ws_at<int32_t>(ws, p.off_slot_of);
   const int S = static_cast<int>(p.S);
-  BEAM_LAUNCH(tm, "slot_scales_fp8", slot_scales_fp8,
-              dim3(static_cast<unsigned>(ceil_div(p.S * (p.H / 128), 256))), dim3(256), 0, s, xs,
-              slot_token, xss, S, p.H / 128);
+  BEAM_LAUNCH(tm, "quant_e4m3", quant_e4m3_rows<true>,
+              dim3(static_cast<unsigned>(ceil_div(p.T * (p.H / 128) * 16, 256))), dim3(256), 0, s,
+              x, p.T, p.H, xq, xs, slot_of, p.K, xss, S);
   const int nt_gu = p.I / 128;
   const int nt_dn = static_cast<int>(ceil_div(p.H, BN));
   if (p.bm == small8::BMS) {

@@ -37,13 +37,18 @@ __device__ __forceinline__ int mx8_exponent(float amax) {
 
 // One thread per 32-value block of a row: E4M3 codes of v * 2^-x (exact
 // scaling, round to nearest even; |v * 2^-x| <= 448 by the choice of x) and
-// the E8M0 code x + 127.
+// the E8M0 code x + 127.  With slot_of (x in the grouped forward) the four
+// codes of each 128-column block kb also go, as one word, to the K slots of
+// the row: word kb * S + slot, so that a tile stage of the grouped products
+// reads its rows' words as one run rather than one cache line per row.
 template <bool BF16>
 __global__ __launch_bounds__(256) void quant_mxfp8_rows(
     const void* __restrict__ v, int64_t rows, int64_t cols, uint8_t* __restrict__ q,
-    uint8_t* __restrict__ scales) {
+    uint8_t* __restrict__ scales, const int32_t* __restrict__ slot_of, int K,
+    uint8_t* __restrict__ xss, int S) {
   const int64_t blk = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t nbc = cols / 32;
+  // cols % 128 == 0: the lanes that return are whole groups of four
   if (blk >= rows * nbc) return;
   const int64_t at = (blk / nbc) * cols + (blk % nbc) * 32;
   float a[32];
@@ -77,7 +82,20 @@ __global__ __launch_bounds__(256) void quant_mxfp8_rows(
   }
   st16(q + at, out[0]);
   st16(q + at + 16, out[1]);
-  scales[blk] = static_cast<uint8_t>(x + 127);
+  const uint32_t b = static_cast<uint32_t>(x + 127);
+  scales[blk] = static_cast<uint8_t>(b);
+  if (xss) {
+    // the four scale bytes of a 128-column block come from four consecutive
+    // lanes; the word goes to every slot of the row, block-major
+    const int l0 = (threadIdx.x % kWave) & ~3;
+    const uint32_t word = __shfl(b, l0) | (__shfl(b, l0 + 1) << 8) |
+                          (__shfl(b, l0 + 2) << 16) | (__shfl(b, l0 + 3) << 24);
+    if (threadIdx.x % 4 == 0) {
+      const int64_t row = blk / nbc, kb = (blk % nbc) / 4;
+      for (int k = 0; k < K; ++k)
+        reinterpret_cast<uint32_t*>(xss)[kb * S + slot_of[row * K + k]] = word;
+    }
+  }
 }
 
 // D = A(32x64, E2M1) * B(64x32, E4M3) + C with per-lane E8M0 scales.  Lane
@@ -212,19 +230,6 @@ __global__ __launch_bounds__(kThreads) void stream_down_mx(
   }
 }
 
-// x's E8M0 bytes per slot for the grouped products, one word (4 bytes, 128 k)
-// per stage, block-major: word kb * S + slot = bytes 4 kb .. 4 kb + 3 of
-// the slot's token row, so that a tile stage reads its rows' words as one
-// run rather than one cache line per row.
-__global__ __launch_bounds__(256) void slot_scales_mx(const uint8_t* __restrict__ xs,
-                                                      const int32_t* __restrict__ slot_token,
-                                                      uint8_t* __restrict__ xss, int S, int nkb) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= static_cast<int64_t>(S) * nkb) return;
-  const int64_t kb = i / S, slot = i % S;
-  reinterpret_cast<uint32_t*>(xss)[i] = *reinterpret_cast<const uint32_t*>(
-      xs + static_cast<int64_t>(slot_token[slot]) * (nkb * 4) + 4 * kb);
-}
 
 // ---- grouped E2M1 x E4M3 GEMM -----------------------------------------------
 // Same work list and XCD order as the bf16 grouped GEMM (M tiles of BMS = 256
@@ -781,9 +786,11 @@ hipError_t launch_quant_mxfp8(int64_t rows, int64_t cols, int32_t dtype, const v
                               uint8_t* q, uint8_t* scales, hipStream_t s, Timer* tm) {
   const dim3 grid(static_cast<unsigned>(ceil_div(rows * (cols / 32), 256)));
   if (dtype == BEAM_BF16)
-    BEAM_LAUNCH(tm, "quant_mxfp8", quant_mxfp8_rows<true>, grid, dim3(256), 0, s, v, rows, cols, q, scales);
+    BEAM_LAUNCH(tm, "quant_mxfp8", quant_mxfp8_rows<true>, grid, dim3(256), 0, s, v, rows, cols, q,
+                scales, nullptr, 0, nullptr, 0);
   else
-    BEAM_LAUNCH(tm, "quant_mxfp8", quant_mxfp8_rows<false>, grid, dim3(256), 0, s, v, rows, cols, q, scales);
+    BEAM_LAUNCH(tm, "quant_mxfp8", quant_mxfp8_rows<false>, grid, dim3(256), 0, s, v, rows, cols, q,
+                scales, nullptr, 0, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -805,17 +812,16 @@ hipError_t launch_experts_mxfp4(const Plan& p, const void* x, const uint8_t* w_g
   const int32_t* active = ws_at<int32_t>(ws, p.off_active);
   const int32_t* meta = ws_at<int32_t>(ws, p.off_meta);
   const int64_t max_active = p.S < p.E ? p.S : p.E;
-  hipError_t e = launch_quant_mxfp8(p.T, p.H, BEAM_BF16, x, xq, xs, s, tm);
-  if (e != hipSuccess) return e;
   if (!p.stream_path) {
     const int32_t* toff = ws_at<int32_t>(ws, p.off_tile_off);
     const int nt_gu = p.I / 128;
     const int nt_dn = static_cast<int>(ceil_div(p.H, tile::BN));
     uint8_t* xss = ws_at<uint8_t>(ws, p.off_xss);
     const int n_slots = static_cast<int>(p.S);
-    BEAM_LAUNCH(tm, "slot_scales_mx", slot_scales_mx,
-                dim3(static_cast<unsigned>(ceil_div(p.S * (p.H / 128), 256))), dim3(256), 0, s,
-                xs, slot_token, xss, n_slots, p.H / 128);
+    // x's E8M0 words also go to its slots, block-major (xss[kb * S + slot])
+    BEAM_LAUNCH(tm, "quant_mxfp8", quant_mxfp8_rows<true>,
+                dim3(static_cast<unsigned>(ceil_div(p.T * (p.H / 32), 256))), dim3(256), 0, s, x,
+                p.T, p.H, xq, xs, ws_at<int32_t>(ws, p.off_slot_of), p.K, xss, n_slots);
 #define BEAM_MX_GATE_UP(BMS, STAGES, PER)                                                     \
   BEAM_LAUNCH(tm, "grouped_gate_up_mx", (mxg::grouped_gemm_mx<BMS, STAGES, mxg::kGateUp, PER>), \
               tile::grid_for(p, nt_gu), dim3(tile::kThreads), 0, s, xq, xss, w_gate_up,        \
@@ -864,6 +870,8 @@ hipError_t launch_experts_mxfp4(const Plan& p, const void* x, const uint8_t* w_g
 #undef BEAM_MX_DOWN
     return hipGetLastError();
   }
+  hipError_t e = launch_quant_mxfp8(p.T, p.H, BEAM_BF16, x, xq, xs, s, tm);
+  if (e != hipSuccess) return e;
   BEAM_LAUNCH(tm, "stream_gate_up_mx", stream_gate_up_mx,
               dim3(static_cast<unsigned>(ceil_div(max_active * (p.I / 16), kWaves))),
               dim3(kThreads), 0, s, xq, xs, w_gate_up, s_gate_up, h, slot_token, counts,

@@ -59,6 +59,7 @@ What each oracle function follows, and what pins it (tests/test_oracle_*.py):
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -92,45 +93,63 @@ def lib():
         if not os.path.exists(_build.LIB) or (
                 os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC)):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
-        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-        L.bo_sigmoid32.argtypes = [ctypes.c_float]
-        L.bo_sigmoid32.restype = ctypes.c_float
-        L.bo_sigmoid_f64.argtypes = [ctypes.c_float]
-        L.bo_sigmoid_f64.restype = ctypes.c_double
-        L.bo_e4m3_decode.argtypes = [ctypes.c_uint8]
-        L.bo_e4m3_decode.restype = ctypes.c_double
-        L.bo_e4m3_encode.argtypes = [ctypes.c_float]
-        L.bo_e4m3_encode.restype = ctypes.c_uint8
-        L.bo_route.argtypes = [ctypes.POINTER(Shape), i64, vp, vp, vp, vp, vp]
-        L.bo_route.restype = i32
-        L.bo_logits.argtypes = [ctypes.POINTER(Shape), i64, vp, i32, vp, vp, i32]
-        L.bo_logits.restype = None
-        L.bo_e2m1_decode.argtypes = [ctypes.c_uint8]
-        L.bo_e2m1_decode.restype = ctypes.c_double
-        L.bo_e2m1_encode.argtypes = [ctypes.c_double]
-        L.bo_e2m1_encode.restype = ctypes.c_uint8
-        L.bo_mx_scale.argtypes = [ctypes.c_double, i32]
-        L.bo_mx_scale.restype = ctypes.c_uint8
-        L.bo_quant_mx.argtypes = [vp, i64, i32, vp, vp]
-        L.bo_mx8_act_scale.argtypes = [ctypes.c_double]
-        L.bo_mx8_act_scale.restype = ctypes.c_uint8
-        L.bo_quant_mx.restype = None
-        L.bo_quant_e4m3.argtypes = [vp, i64, i32, vp, vp]
-        L.bo_quant_e4m3.restype = None
-        L.bo_forward_tokens.argtypes = [ctypes.POINTER(Shape), i64, vp, vp, i32,
-                                        vp, vp, vp, vp, vp, vp, i32, i32, vp, i32]
-        L.bo_forward_tokens.restype = i32
-        L.bo_bias_update.argtypes = [i32, i64, i32, vp, ctypes.c_float, vp]
-        L.bo_bias_update.restype = None
-        L.bo_residual_epilogue.argtypes = [i64, i32, vp, vp, ctypes.c_double, i32, vp]
-        L.bo_residual_epilogue.restype = None
-        L.bo_bias_gamma.argtypes = [i64, i64, ctypes.c_float, ctypes.c_float]
-        L.bo_bias_gamma.restype = ctypes.c_float
-        L.bo_max_threads.argtypes = []
-        L.bo_max_threads.restype = i32
-        _lib = L
+        _lib = _bind(ctypes.CDLL(_build.LIB))
     return _lib
+
+
+@contextlib.contextmanager
+def library(path: str):
+    """Run the wrapper's functions on another build of the oracle's source
+    (the tests compile copies with planted mistakes to show that a pin
+    catches them), restoring the regular build afterwards."""
+    global _lib
+    saved = lib()
+    _lib = _bind(ctypes.CDLL(path))
+    try:
+        yield
+    finally:
+        _lib = saved
+
+
+def _bind(L):
+    """Declare the argument and result types of the oracle's exports."""
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.bo_sigmoid32.argtypes = [ctypes.c_float]
+    L.bo_sigmoid32.restype = ctypes.c_float
+    L.bo_sigmoid_f64.argtypes = [ctypes.c_float]
+    L.bo_sigmoid_f64.restype = ctypes.c_double
+    L.bo_e4m3_decode.argtypes = [ctypes.c_uint8]
+    L.bo_e4m3_decode.restype = ctypes.c_double
+    L.bo_e4m3_encode.argtypes = [ctypes.c_float]
+    L.bo_e4m3_encode.restype = ctypes.c_uint8
+    L.bo_route.argtypes = [ctypes.POINTER(Shape), i64, vp, vp, vp, vp, vp]
+    L.bo_route.restype = i32
+    L.bo_logits.argtypes = [ctypes.POINTER(Shape), i64, vp, i32, vp, vp, i32]
+    L.bo_logits.restype = None
+    L.bo_e2m1_decode.argtypes = [ctypes.c_uint8]
+    L.bo_e2m1_decode.restype = ctypes.c_double
+    L.bo_e2m1_encode.argtypes = [ctypes.c_double]
+    L.bo_e2m1_encode.restype = ctypes.c_uint8
+    L.bo_mx_scale.argtypes = [ctypes.c_double, i32]
+    L.bo_mx_scale.restype = ctypes.c_uint8
+    L.bo_quant_mx.argtypes = [vp, i64, i32, vp, vp]
+    L.bo_mx8_act_scale.argtypes = [ctypes.c_double]
+    L.bo_mx8_act_scale.restype = ctypes.c_uint8
+    L.bo_quant_mx.restype = None
+    L.bo_quant_e4m3.argtypes = [vp, i64, i32, vp, vp]
+    L.bo_quant_e4m3.restype = None
+    L.bo_forward_tokens.argtypes = [ctypes.POINTER(Shape), i64, vp, vp, i32,
+                                    vp, vp, vp, vp, vp, vp, i32, i32, vp, i32]
+    L.bo_forward_tokens.restype = i32
+    L.bo_bias_update.argtypes = [i32, i64, i32, vp, ctypes.c_float, vp]
+    L.bo_bias_update.restype = None
+    L.bo_residual_epilogue.argtypes = [i64, i32, vp, vp, ctypes.c_double, i32, vp]
+    L.bo_residual_epilogue.restype = None
+    L.bo_bias_gamma.argtypes = [i64, i64, ctypes.c_float, ctypes.c_float]
+    L.bo_bias_gamma.restype = ctypes.c_float
+    L.bo_max_threads.argtypes = []
+    L.bo_max_threads.restype = i32
+    return L
 
 
 def _ptr(a: np.ndarray):

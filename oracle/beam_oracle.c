@@ -352,10 +352,24 @@ static void fake_quant_row_mx(const double* in, int64_t n, double* out, float* t
     out[i] = ldexp(bo_e4m3_decode(tmpq[i]), (int)tmps[i / 32] - 127);
 }
 
-/* Round-trip a row through bo_quant_e4m3 and return the dequantised values. */
+/* Binary32 -> bfloat16 (round to nearest, ties to even) -> binary32. */
+static float round_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7F800000u) != 0x7F800000u) {       /* finite: add half an ulp, tie to even */
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    u &= 0xFFFF0000u;
+  }
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* Round-trip a row through bo_quant_e4m3 and return the dequantised values.
+ * bf16_first: the row is taken as binary32 values rounded to bfloat16 (the
+ * precision intermediate activations are stored in) before quantising. */
 static void fake_quant_row(const double* in, int64_t n, int block, double* out,
-                           float* tmpf, uint8_t* tmpq, float* tmps) {
-  for (int64_t i = 0; i < n; ++i) tmpf[i] = (float)in[i];
+                           float* tmpf, uint8_t* tmpq, float* tmps, int bf16_first) {
+  for (int64_t i = 0; i < n; ++i) tmpf[i] = bf16_first ? round_bf16((float)in[i]) : (float)in[i];
   bo_quant_e4m3(tmpf, n, block, tmpq, tmps);
   for (int64_t i = 0; i < n; ++i)
     out[i] = bo_e4m3_decode(tmpq[i]) * (double)tmps[i / block];
@@ -406,8 +420,9 @@ static double weight(const void* w, int dtype, const void* sc, int64_t e,
  *   out[t] = sum_k w_k y_{e_k}, in rank order; no shared expert ([P2]).
  * Everything in binary64.  act_quant = 1 first round-trips x (per token) and
  * h (per assignment) through the variant's activation recipe: bo_quant_e4m3
- * per 128 channels for FP8 weights, MXFP8 (bo_quant_mx, 32 channels) for
- * MXFP4 weights.
+ * per 128 channels for FP8 weights, h first rounded to binary32 and then to
+ * bfloat16 (the precision the bf16 path stores h in); MXFP8 (bo_quant_mx, 32
+ * channels, h rounded to binary32) for MXFP4 weights.
  * tokens[n] lists which rows of x to evaluate; out is [n, H]. */
 int bo_forward_tokens(const bo_shape* sh, int64_t n, const int64_t* tokens,
                       const void* x, int x_dtype, const int32_t* idx,
@@ -436,7 +451,7 @@ int bo_forward_tokens(const bo_shape* sh, int64_t n, const int64_t* tokens,
     const int mx = w_dtype == BO_MXFP4;
     for (int64_t h = 0; h < H; ++h) xr[h] = load_val(x, x_dtype, t * H + h);
     if (act_quant && mx) fake_quant_row_mx(xr, H, xr, tf, tq, tm);
-    else if (act_quant) fake_quant_row(xr, H, 128, xr, tf, tq, ts);
+    else if (act_quant) fake_quant_row(xr, H, 128, xr, tf, tq, ts, 0);
     for (int k = 0; k < K; ++k) {
       const int64_t e = idx[t * K + k];
       for (int64_t j = 0; j < I; ++j) {
@@ -448,7 +463,7 @@ int bo_forward_tokens(const bo_shape* sh, int64_t n, const int64_t* tokens,
         hv[j] = g / (1.0 + exp(-g)) * v;
       }
       if (act_quant && mx) fake_quant_row_mx(hv, I, hv, tf, tq, tm);
-      else if (act_quant) fake_quant_row(hv, I, 128, hv, tf, tq, ts);
+      else if (act_quant) fake_quant_row(hv, I, 128, hv, tf, tq, ts, 1);
       const double wk = (double)w[t * K + k];
       for (int64_t o = 0; o < H; ++o) {
         double y = 0.0;

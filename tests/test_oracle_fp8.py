@@ -1,8 +1,11 @@
 """Pin the oracle's OCP e4m3fn codec (the FP8 checkpoint form named in "Hugging
 Face releases Beam ..." and "Reflection Beam", section "Where to run it")
 against torch.float8_e4m3fn: every code decodes to torch's value, and binary32
-values encode to torch's round-to-nearest-even code."""
+values encode to torch's round-to-nearest-even code; and the FP8 activation
+recipe inside the forward, against numpy matmuls on the round-tripped x and h,
+with copies of the oracle carrying planted mistakes that the pin must catch."""
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -40,3 +43,108 @@ def test_encode_saturates():
     assert np.all(oracle.e4m3_encode(v) == 0x7E)
     assert np.all(oracle.e4m3_encode(-v) == 0xFE)
     assert oracle.e4m3_encode(np.array([np.nan], np.float32))[0] & 0x7F == 0x7F
+
+
+# ---- the FP8 activation recipe inside the forward (act_quant=True) --------
+# One expert at routing weight 1 turns the forward into a dense SwiGLU whose
+# x and h go through the e4m3 recipe; weights are e4m3 codes with power-of-
+# two block scales, so their dequantised values are exact.  The reference is
+# numpy float64 matmuls on values decoded by torch's e4m3fn, h rounded to
+# binary32 and then to bfloat16 by torch before its quantisation.
+
+def _fp8_layer(seed):
+    from synth import small_shape
+    sh = small_shape(hidden=256, intermediate=256, n_experts=1, n_groups=1,
+                     topk_groups=1, top_k=1)
+    rng = np.random.default_rng(seed)
+    T = 5
+    x = rng.standard_normal((T, sh.hidden)).astype(np.float32)
+    x[1, :128] *= 1e-3                  # blocks of one row on different scales
+    x[3, 128:] *= 40.0
+    H, I = sh.hidden, sh.intermediate
+    codes_gu = rng.integers(0, 0x7F, (1, 2 * I, H)).astype(np.uint8)
+    codes_gu[codes_gu & 0x78 == 0x78] &= 0x70      # keep codes finite (no 0x7F)
+    codes_gu |= (rng.integers(0, 2, codes_gu.shape) << 7).astype(np.uint8)
+    codes_d = rng.integers(0, 0x7F, (1, H, I)).astype(np.uint8)
+    codes_d[codes_d & 0x78 == 0x78] &= 0x70
+    codes_d |= (rng.integers(0, 2, codes_d.shape) << 7).astype(np.uint8)
+    s_gu = (2.0 ** rng.integers(-14, -10, (1, 2 * I // 128, H // 128))).astype(np.float32)
+    s_d = (2.0 ** rng.integers(-14, -10, (1, H // 128, I // 128))).astype(np.float32)
+    return sh, x, codes_gu, s_gu, codes_d, s_d
+
+
+def _e4m3_values(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn) \
+        .to(torch.float64).numpy()
+
+
+def _fp8_reference(x, codes_gu, s_gu, codes_d, s_d, I):
+    def dq_w(codes, s):
+        return _e4m3_values(codes[0]) * np.repeat(np.repeat(s[0].astype(np.float64), 128, 0), 128, 1)
+
+    def round_trip(v):
+        q, s = oracle.quant_e4m3(v.astype(np.float32), 128)
+        return _e4m3_values(q) * np.repeat(s.astype(np.float64), 128, axis=-1)
+
+    Wgu, Wd = dq_w(codes_gu, s_gu), dq_w(codes_d, s_d)
+    xq = round_trip(x)
+    g, u = xq @ Wgu[:I].T, xq @ Wgu[I:].T
+    h = g / (1.0 + np.exp(-g)) * u
+    h_bf = torch.from_numpy(h.astype(np.float32)).bfloat16().float().numpy()
+    return round_trip(h_bf) @ Wd.T
+
+
+def _fp8_forward(sh, x, codes_gu, s_gu, codes_d, s_d):
+    T = x.shape[0]
+    return oracle.forward_tokens(sh, np.arange(T), x, np.zeros((T, 1), np.int32),
+                                 np.ones((T, 1), np.float32), codes_gu, codes_d,
+                                 s_gu, s_d, act_quant=True)
+
+
+def test_forward_fp8_activation_recipe_single_expert():
+    sh, x, cgu, sgu, cd, sd = _fp8_layer(11)
+    got = _fp8_forward(sh, x, cgu, sgu, cd, sd)
+    ref = _fp8_reference(x, cgu, sgu, cd, sd, sh.intermediate)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max())
+    # without the activation recipe the output differs well beyond that
+    plain = oracle.forward_tokens(sh, np.arange(x.shape[0]), x,
+                                  np.zeros((x.shape[0], 1), np.int32),
+                                  np.ones((x.shape[0], 1), np.float32), cgu, cd, sgu, sd)
+    assert np.abs(plain - ref).max() > 1e-3 * np.abs(ref).max()
+
+
+# Copies of the oracle's source with one planted mistake each in the FP8
+# activation branch; every one must fail the pin above.
+FP8_MUTANTS = {
+    "h not round-tripped": (
+        "      else if (act_quant) fake_quant_row(hv, I, 128, hv, tf, tq, ts, 1);",
+        "      else if (0) fake_quant_row(hv, I, 128, hv, tf, tq, ts, 1);"),
+    "x not round-tripped": (
+        "    else if (act_quant) fake_quant_row(xr, H, 128, xr, tf, tq, ts, 0);",
+        "    else if (0) fake_quant_row(xr, H, 128, xr, tf, tq, ts, 0);"),
+    "h not rounded to bf16": (
+        "      else if (act_quant) fake_quant_row(hv, I, 128, hv, tf, tq, ts, 1);",
+        "      else if (act_quant) fake_quant_row(hv, I, 128, hv, tf, tq, ts, 0);"),
+    "scale of the wrong block": (
+        "    out[i] = bo_e4m3_decode(tmpq[i]) * (double)tmps[i / block];",
+        "    out[i] = bo_e4m3_decode(tmpq[i]) * (double)tmps[(i / block) ^ 1];"),
+    "codes left unscaled": (
+        "    out[i] = bo_e4m3_decode(tmpq[i]) * (double)tmps[i / block];",
+        "    out[i] = bo_e4m3_decode(tmpq[i]);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
+def test_fp8_recipe_pin_catches_planted_mistakes(name, tmp_path):
+    from oracle import build as ob
+    old, new = FP8_MUTANTS[name]
+    src = open(ob.SRC).read()
+    assert src.count(old) == 1, "the mutation site moved"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new))
+    so = ob.compile_to(str(path), str(tmp_path / "libmutant.so"))
+    sh, x, cgu, sgu, cd, sd = _fp8_layer(11)
+    ref = _fp8_reference(x, cgu, sgu, cd, sd, sh.intermediate)
+    with oracle.library(so):
+        got = _fp8_forward(sh, x, cgu, sgu, cd, sd)
+    assert not np.allclose(got, ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max())

@@ -9,6 +9,7 @@ every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -141,36 +142,61 @@ def _p(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream=None):
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+def _torch_stream(stream, device):
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
+def _stream(stream=None, device=None):
+    return ctypes.c_void_p(_torch_stream(stream, device).cuda_stream)
 
 
 class Workspace:
-    """A growable device byte buffer reused across calls."""
+    """A growable device byte buffer reused across calls.
+
+    Calls that may overlap (calls on different streams) need distinct
+    workspaces.  The buffer is allocated on the stream of the call that
+    grows it, and marked as used by any other stream a later call runs on,
+    so torch's allocator never hands its memory out again while queued
+    kernels may still use it."""
 
     def __init__(self, device="cuda"):
         self.device = torch.device(device)
         self.buf = None
+        self.streams = set()
 
-    def get(self, nbytes: int) -> Optional[torch.Tensor]:
+    def get(self, nbytes: int, stream=None) -> Optional[torch.Tensor]:
         if nbytes == 0:
             return None
+        s = _torch_stream(stream, self.device)
         if self.buf is None or self.buf.numel() < nbytes:
             self.buf = None
-            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            with torch.cuda.stream(s):
+                self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            self.streams = {s.cuda_stream}
+        elif s.cuda_stream not in self.streams:
+            self.buf.record_stream(s)
+            self.streams.add(s.cuda_stream)
         return self.buf
 
 
+# one default workspace per (device, stream): calls on one stream are
+# ordered, calls on different streams never share scratch memory
 _default_ws = {}
 
 
-def _ws(desc: Desc, T: int, workspace: Optional[Workspace], device):
+def _ws(desc: Desc, T: int, workspace: Optional[Workspace], device, stream=None):
     n = workspace_bytes(desc, T)
+    s = _torch_stream(stream, device)
     if workspace is None:
-        key = str(device)
+        key = (str(device), s.cuda_stream)
         workspace = _default_ws.setdefault(key, Workspace(device))
-    return workspace.get(n), n
+    return workspace.get(n, s), n
+
+
+def _alloc_on(stream):
+    """Context in which the binding allocates a call's outputs: the call's
+    stream, so that torch's allocator orders their reuse after its kernels."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
 
 
 def route(desc: Desc, x: Optional[torch.Tensor], w_router: Optional[torch.Tensor],
@@ -182,14 +208,15 @@ def route(desc: Desc, x: Optional[torch.Tensor], w_router: Optional[torch.Tensor
     lin = bool(desc.flags & ROUTE_LOGITS_IN)
     ref = logits if lin else x
     T, dev = ref.shape[0], ref.device
-    idx = torch.empty(T, desc.top_k, dtype=torch.int32, device=dev)
-    w = torch.empty(T, desc.top_k, dtype=torch.float32, device=dev)
-    if logits is None:
-        logits = torch.empty(T, desc.n_experts, dtype=torch.float32, device=dev)
-    buf, n = _ws(desc, T, workspace, dev)
+    with _alloc_on(stream):
+        idx = torch.empty(T, desc.top_k, dtype=torch.int32, device=dev)
+        w = torch.empty(T, desc.top_k, dtype=torch.float32, device=dev)
+        if logits is None:
+            logits = torch.empty(T, desc.n_experts, dtype=torch.float32, device=dev)
+    buf, n = _ws(desc, T, workspace, dev, stream)
     _check(lib().beam_moe_route(ctypes.byref(desc), T, _p(x), _p(w_router),
                                 _p(bias), _p(logits), _p(idx), _p(w), _p(buf),
-                                n, _stream(stream)), "beam_moe_route")
+                                n, _stream(stream, dev)), "beam_moe_route")
     return idx, w, logits
 
 
@@ -198,15 +225,16 @@ def permute(desc: Desc, topk_idx: torch.Tensor,
     """beam_moe_permute.  Returns dict(counts, offsets, slot_token, slot_of)."""
     T, dev = topk_idx.shape[0], topk_idx.device
     E, S = desc.n_experts, T * desc.top_k
-    out = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
-               offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
-               slot_token=torch.empty(max(S, 1), dtype=torch.int32, device=dev),
-               slot_of=torch.empty(max(S, 1), dtype=torch.int32, device=dev))
-    buf, n = _ws(desc, T, workspace, dev)
+    with _alloc_on(stream):
+        out = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
+                   offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                   slot_token=torch.empty(max(S, 1), dtype=torch.int32, device=dev),
+                   slot_of=torch.empty(max(S, 1), dtype=torch.int32, device=dev))
+    buf, n = _ws(desc, T, workspace, dev, stream)
     _check(lib().beam_moe_permute(ctypes.byref(desc), T, _p(topk_idx),
                                   _p(out["counts"]), _p(out["offsets"]),
                                   _p(out["slot_token"]), _p(out["slot_of"]),
-                                  _p(buf), n, _stream(stream)), "beam_moe_permute")
+                                  _p(buf), n, _stream(stream, dev)), "beam_moe_permute")
     out["slot_token"] = out["slot_token"][:S]
     out["slot_of"] = out["slot_of"][:S].view(T, desc.top_k)
     return out
@@ -224,11 +252,11 @@ def forward_residual(desc: Desc, x: torch.Tensor, w_router: Optional[torch.Tenso
     place) = sqrt((k-1)/k) residual + RMSNorm(block output) * norm_weight /
     sqrt(k).  Returns residual (and writes out when given)."""
     T, dev = x.shape[0], x.device
-    buf, n = _ws(desc, T, workspace, dev)
+    buf, n = _ws(desc, T, workspace, dev, stream)
     _check(lib().beam_moe_forward_residual(
         ctypes.byref(desc), T, _p(x), _p(w_router), _p(bias), _p(w_gate_up),
         _p(s_gate_up), _p(w_down), _p(s_down), _p(norm_weight), float(eps),
-        int(step), _p(residual), _p(out), _p(buf), n, _stream(stream)),
+        int(step), _p(residual), _p(out), _p(buf), n, _stream(stream, dev)),
         "beam_moe_forward_residual")
     return residual
 
@@ -238,7 +266,7 @@ def bias_update(desc: Desc, topk_idx: torch.Tensor, gamma: float,
     """beam_moe_bias_update: one balancing step on `bias` (in place)."""
     _check(lib().beam_moe_bias_update(ctypes.byref(desc), topk_idx.shape[0],
                                       _p(topk_idx), float(gamma), _p(bias),
-                                      _stream(stream)), "beam_moe_bias_update")
+                                      _stream(stream, bias.device)), "beam_moe_bias_update")
     return bias
 
 
@@ -253,10 +281,11 @@ def quant_e4m3(v: torch.Tensor, stream=None):
     dt = BF16 if v.dtype == torch.bfloat16 else F32
     if v.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError(v.dtype)
-    q = torch.empty(rows, cols, dtype=torch.uint8, device=v.device)
-    s = torch.empty(rows, max(cols // 128, 1), dtype=torch.float32, device=v.device)
+    with _alloc_on(stream):
+        q = torch.empty(rows, cols, dtype=torch.uint8, device=v.device)
+        s = torch.empty(rows, max(cols // 128, 1), dtype=torch.float32, device=v.device)
     _check(lib().beam_moe_quant_e4m3(rows, cols, dt, _p(v), _p(q), _p(s),
-                                     _stream(stream)), "beam_moe_quant_e4m3")
+                                     _stream(stream, v.device)), "beam_moe_quant_e4m3")
     return q, s[:, :cols // 128]
 
 
@@ -267,10 +296,11 @@ def quant_mxfp8(v: torch.Tensor, stream=None):
     if v.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError(v.dtype)
     dt = BF16 if v.dtype == torch.bfloat16 else F32
-    q = torch.empty(rows, cols, dtype=torch.uint8, device=v.device)
-    s = torch.empty(rows, max(cols // 32, 16), dtype=torch.uint8, device=v.device)
+    with _alloc_on(stream):
+        q = torch.empty(rows, cols, dtype=torch.uint8, device=v.device)
+        s = torch.empty(rows, max(cols // 32, 16), dtype=torch.uint8, device=v.device)
     _check(lib().beam_moe_quant_mxfp8(rows, cols, dt, _p(v), _p(q), _p(s),
-                                      _stream(stream)), "beam_moe_quant_mxfp8")
+                                      _stream(stream, v.device)), "beam_moe_quant_mxfp8")
     return q, s[:, :cols // 32]
 
 
@@ -314,18 +344,19 @@ def forward(desc: Desc, x: torch.Tensor, w_router: Optional[torch.Tensor],
     [T,H] (act dtype), or (out, topk_idx, topk_w, logits) with
     return_routing."""
     T, dev = x.shape[0], x.device
-    if out is None:
-        out = torch.empty(T, desc.hidden, dtype=x.dtype, device=dev)
     idx = w = None
-    if return_routing:
-        idx = torch.empty(T, desc.top_k, dtype=torch.int32, device=dev)
-        w = torch.empty(T, desc.top_k, dtype=torch.float32, device=dev)
-        if logits is None:
-            logits = torch.empty(T, desc.n_experts, dtype=torch.float32, device=dev)
-    buf, n = _ws(desc, T, workspace, dev)
+    with _alloc_on(stream):
+        if out is None:
+            out = torch.empty(T, desc.hidden, dtype=x.dtype, device=dev)
+        if return_routing:
+            idx = torch.empty(T, desc.top_k, dtype=torch.int32, device=dev)
+            w = torch.empty(T, desc.top_k, dtype=torch.float32, device=dev)
+            if logits is None:
+                logits = torch.empty(T, desc.n_experts, dtype=torch.float32, device=dev)
+    buf, n = _ws(desc, T, workspace, dev, stream)
     args = [ctypes.byref(desc), T, _p(x), _p(w_router), _p(bias), _p(w_gate_up),
             _p(s_gate_up), _p(w_down), _p(s_down), _p(out), _p(idx), _p(w),
-            _p(logits), _p(buf), n, _stream(stream)]
+            _p(logits), _p(buf), n, _stream(stream, dev)]
     if timer is None:
         _check(lib().beam_moe_forward(*args), "beam_moe_forward")
     else:

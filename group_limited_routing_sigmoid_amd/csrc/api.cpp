@@ -230,6 +230,10 @@ int beam_moe_validate(const beam_moe_desc* d, int64_t T) {
   const int64_t S = T * static_cast<int64_t>(d->top_k);
   const int64_t wide = d->hidden > d->intermediate ? d->hidden : d->intermediate;
   if (S * wide > 0x7FFFFFFF) return BEAM_ERR_UNSUPPORTED;
+  // element (bf16, fp32) and byte (e4m3, 4-bit) offsets inside one expert's
+  // weights are 32-bit: its gate/up matrix holds 2*I*H values
+  if (2 * static_cast<int64_t>(d->intermediate) * d->hidden > 0x7FFFFFFF)
+    return BEAM_ERR_UNSUPPORTED;
   return BEAM_OK;
 }
 

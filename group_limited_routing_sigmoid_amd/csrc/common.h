@@ -71,11 +71,14 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 // and subnormal codes as the format defines them.  It agrees with exact RNE
 // for every |v| < 464 (checked on gfx950 over all code values, all midpoints
 // and their neighbouring floats); from 464 up it gives the NaN code instead
-// of saturating, so callers pass values already scaled into [-448, 448] up to
-// a rounding of the scale.
+// of saturating, so the values are first clamped to [-448, 448]: a block
+// scale amax/448 rounded coarsely (a subnormal amax) can put v/scale past
+// 448, and the recipe saturates such values.
+__device__ __forceinline__ float sat448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), lo, true));
 }
 
 __device__ __forceinline__ float silu(float g) {

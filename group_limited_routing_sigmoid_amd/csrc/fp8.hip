@@ -9,10 +9,17 @@
 namespace beam {
 namespace {
 
+// The recipe's block scale: amax / 448 in binary32, or 1 where that is zero
+// (an all-zero block, or a subnormal amax whose quotient underflows).
+__device__ __forceinline__ float e4m3_scale(float amax) {
+  const float sc = amax / 448.0f;
+  return sc > 0.0f ? sc : 1.0f;
+}
+
 // 16 lanes per (row, 128-column block), 8 consecutive columns per lane (one
 // 16-byte load of bf16, two of fp32); a wave covers 4 blocks.  The block's
-// amax is reduced over its 16 lanes; scale = amax / 448 (1 for a zero block),
-// code = e4m3(v / scale) with binary32 division, as in the recipe.  With
+// amax is reduced over its 16 lanes; scale = e4m3_scale(amax), code =
+// e4m3(v / scale) with binary32 division, saturating, as in the recipe.  With
 // slot_of (x in the forward) each scale also goes to the K slots of its row,
 // block-major: xss[kb * S + slot], so that a tile stage of the grouped
 // products reads the scale words of consecutive slots (one 1 KiB run per
@@ -50,7 +57,7 @@ __global__ __launch_bounds__(256) void quant_e4m3_rows(
   for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(a[j]));
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));  // within 16 lanes
-  const float sc = (m > 0.0f) ? m / 448.0f : 1.0f;
+  const float sc = e4m3_scale(m);
   const uint32_t lo = e4m3x4(a[0] / sc, a[1] / sc, a[2] / sc, a[3] / sc);
   const uint32_t hi = e4m3x4(a[4] / sc, a[5] / sc, a[6] / sc, a[7] / sc);
   if (!live) return;
@@ -447,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
       for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(v0[j]), fabsf(v1[j])));
 #pragma unroll
       for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-      const float sc = (m > 0.0f) ? m / 448.0f : 1.0f;
+      const float sc = e4m3_scale(m);
       const uint32_t lo = e4m3x4(v0[0] / sc, v0[1] / sc, v0[2] / sc, v0[3] / sc);
       const uint32_t hi = e4m3x4(v1[0] / sc, v1[1] / sc, v1[2] / sc, v1[3] / sc);
       if (row0 + rl < row_end) {
@@ -486,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(
       for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(v0[j]), fabsf(v1[j])));
 #pragma unroll
       for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-      const float sc = (m > 0.0f) ? m / 448.0f : 1.0f;
+      const float sc = e4m3_scale(m);
       const uint32_t lo = e4m3x4(v0[0] / sc, v0[1] / sc, v0[2] / sc, v0[3] / sc);
       const uint32_t hi = e4m3x4(v1[0] / sc, v1[1] / sc, v1[2] / sc, v1[3] / sc);
       if (rl < x_rows) {
@@ -725,7 +732,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8_small(
       for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(v0[j]), fabsf(v1[j])));
 #pragma unroll
       for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-      const float sc = (m > 0.0f) ? m / 448.0f : 1.0f;
+      const float sc = e4m3_scale(m);
       const uint32_t lo = e4m3x4(v0[0] / sc, v0[1] / sc, v0[2] / sc, v0[3] / sc);
       const uint32_t hi = e4m3x4(v1[0] / sc, v1[1] / sc, v1[2] / sc, v1[3] / sc);
       if (row0 + rl < row_end) {

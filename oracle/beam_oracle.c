@@ -326,9 +326,11 @@ static double load_val(const void* base, int dtype, int64_t i) {
 }
 
 /* Per-token, per-block dynamic quantisation to e4m3 (the FP8 variant's
- * activation recipe): scale = amax / 448 in binary32 (1 if the block is all
- * zero), code = e4m3(v / scale) with a binary32 division.  Writes the codes
- * and one scale per block.  n must be a multiple of block. */
+ * activation recipe): scale = amax / 448 in binary32, or 1 where that is
+ * zero (an all-zero block, or a subnormal amax whose quotient underflows),
+ * code = e4m3(v / scale) with a binary32 division, saturating (a subnormal
+ * scale is coarse, so v / scale may pass 448).  Writes the codes and one
+ * scale per block.  n must be a multiple of block. */
 void bo_quant_e4m3(const float* v, int64_t n, int block, uint8_t* q,
                    float* scales) {
   for (int64_t b0 = 0; b0 < n; b0 += block) {
@@ -337,7 +339,8 @@ void bo_quant_e4m3(const float* v, int64_t n, int block, uint8_t* q,
       float a = fabsf(v[b0 + j]);
       if (a > amax) amax = a;
     }
-    float sc = (amax > 0.0f) ? amax / 448.0f : 1.0f;
+    float sc = amax / 448.0f;
+    if (!(sc > 0.0f)) sc = 1.0f;
     scales[b0 / block] = sc;
     for (int j = 0; j < block; ++j) q[b0 + j] = bo_e4m3_encode(v[b0 + j] / sc);
   }

@@ -78,6 +78,17 @@ def test_validate_small_top_k_bound():
     assert gl.validate(gl.make_desc(TINY, gl.F32, gl.F32), -1) == gl.ERR_INVALID_ARG
 
 
+def test_validate_bounds_expert_weight_offsets():
+    # one expert's gate/up matrix (2 I H values) is addressed with 32-bit
+    # element and byte offsets
+    assert gl.validate(_desc(hidden=32768, intermediate=16384), 1) == gl.OK
+    assert gl.validate(_desc(hidden=32768, intermediate=32768), 1) == gl.ERR_UNSUPPORTED
+    assert gl.validate(_desc(hidden=65536, intermediate=16384), 1) == gl.ERR_UNSUPPORTED
+    for wdt in (gl.FP8_E4M3, gl.MXFP4):
+        assert gl.validate(_desc(hidden=65536, intermediate=16384, weight_dtype=wdt),
+                           1) == gl.ERR_UNSUPPORTED
+
+
 def test_workspace_bytes():
     assert gl.workspace_bytes(_desc(), 0) == 0
     a, b = gl.workspace_bytes(_desc(), 64), gl.workspace_bytes(_desc(), 16384)

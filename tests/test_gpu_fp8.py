@@ -28,6 +28,14 @@ def test_quant_bit_exact(dtype):
     v[3, :128] = 0.0                                  # all-zero block
     v[5, 130] = 1e-30                                 # tiny amax block
     v[7, 256:384] = torch.linspace(-448.0, 448.0, 128)
+    # subnormal block maxima: a coarse scale puts v/scale past 448 (the
+    # recipe saturates), or amax/448 underflows to zero (scale 1)
+    v[9, 512:640] = torch.linspace(-1.0, 1.0, 128) * 1e-39
+    v[11, :128] = 0.0
+    v[11, 7] = -8.8e-43
+    v[13, 128:256] = 0.0
+    v[13, 130] = 3e-43
+    v[15, 384:512] = torch.arange(1, 129) * 1e-40
     v = v.to(dtype)
     q, s = gl.quant_e4m3(v.to(dev))
     oq, os_ = oracle.quant_e4m3(v.float().numpy(), 128)

@@ -148,3 +148,25 @@ def test_fp8_recipe_pin_catches_planted_mistakes(name, tmp_path):
     with oracle.library(so):
         got = _fp8_forward(sh, x, cgu, sgu, cd, sd)
     assert not np.allclose(got, ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max())
+
+
+def test_quant_scale_rule_on_tiny_blocks():
+    # scale = amax/448 in binary32, 1 where that quotient is zero; codes
+    # saturate (a subnormal scale is coarse, so v/scale can pass 448)
+    v = np.zeros((4, 128), np.float32)
+    v[0, :] = np.linspace(-1, 1, 128, dtype=np.float32) * np.float32(1e-39)
+    v[1, 5] = np.float32(3e-43)            # 3e-43/448 underflows to zero
+    v[2, 7] = np.float32(-8.8e-43)         # quotient rounds to the smallest subnormal
+    v[3, :] = np.float32(1e-40) * np.arange(1, 129, dtype=np.float32)
+    q, s = oracle.quant_e4m3(v, 128)
+    for r in range(4):
+        amax = np.float32(np.abs(v[r]).max())
+        sc = np.float32(amax / np.float32(448.0))
+        sc = sc if sc > 0 else np.float32(1.0)
+        assert s[r, 0].view(np.uint32) == sc.view(np.uint32)
+        want = oracle.e4m3_encode(np.minimum(np.maximum(v[r] / sc, -448), 448))
+        np.testing.assert_array_equal(q[r], want)
+        assert not np.any((q[r] & 0x7F) == 0x7F)           # never a NaN code
+    assert s[1, 0] == 1.0 and np.all(q[1] == 0)
+    # the coarse scale of row 2 puts its maximum past 448: saturated, not NaN
+    assert abs(v[2, 7] / s[2, 0]) > 448 and q[2, 7] == 0xFE

@@ -3,7 +3,10 @@
 A step is one forward of the whole block (router, permutation, experts,
 combine) over one batch of synthetic tokens already resident in HBM.  The
 default workload is the Beam-shape decode layer (64 bf16 tokens, hidden 5120,
-256 experts in 8 groups of 32, top-4 groups, top-8 experts, SwiGLU 2560).
+256 experts in 8 groups of 32, top-4 groups, top-8 experts, SwiGLU 2560),
+the HBM-bound half of the metric; the default run also times the MFMA-bound
+half, the 16,384-token prefill with skewed routing, in the same process and
+reports it under "prefill" in the same line.
 
 Prints one JSON line: throughput (tokens/s), the dominant kernel's roofline
 (its average duration from HIP events recorded around it on its own stream
@@ -34,6 +37,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode64")
+    ap.add_argument("--prefill-workload", default="prefill16k_skew",
+                    help="second workload timed in the default run (the MFMA-bound "
+                         "prefill); 'none' skips it.  Runs only with the default "
+                         "--workload and no --tokens")
     ap.add_argument("--tokens", type=int, default=None,
                     help="override the workload's token count (decode/verify sweep)")
     ap.add_argument("--path", choices=["auto", "stream", "grouped"], default="auto")
@@ -103,6 +110,17 @@ def traffic_for(kernel, workload):
     except (OSError, KeyError):
         return None
     return rec["bytes_per_launch"] if h == rec["sources_sha256"] else None
+
+
+def traffic_source(kernel, workload, value):
+    """Where the roofline's traffic figure comes from (it is not counted in
+    this run: HBM counters need profiler passes of their own)."""
+    if value is None:
+        return ("none: no counter run on the current kernel sources "
+                f"(profiles/traffic_{kernel}_{workload}.json absent or stale)")
+    return (f"replayed from profiles/traffic_{kernel}_{workload}.json: rocprofv3 "
+            "FETCH_SIZE and WRITE_SIZE runs on the same kernel sources (SHA-256 "
+            "checked), scaled by the copy calibration")
 
 
 def calibrate_copy(steps):
@@ -250,16 +268,30 @@ def main():
     if a.calibrate_copy:
         calibrate_copy(max(a.steps, 1))
         return
+    res = run_workload(a, a.workload, a.tokens)
+    if (a.prefill_workload != "none" and a.workload == "decode64" and a.tokens is None):
+        import torch
+        torch.cuda.empty_cache()
+        pre = run_workload(a, a.prefill_workload, None)
+        res["prefill"] = {k: pre[k] for k in (
+            "value", "unit", "ms_per_step", "step_ms", "dtype", "config", "roofline",
+            "layer", "sclk_mhz", "routing", "kernels_ms", "cpu_baseline", "graph")
+            if k in pre}
+    print(json.dumps(res), flush=True)
+
+
+def run_workload(a, workload, tokens):
+    """Times a.steps forwards of one workload; returns its result dict."""
     import numpy as np
     import torch
 
     import group_limited_routing_sigmoid_amd as gl
     from synth import WORKLOADS, make_inputs, FP8, MXFP4
 
-    w = WORKLOADS[a.workload]
+    w = WORKLOADS[workload]
     sh = w.shape
     dev = torch.device("cuda:0")
-    inp = make_inputs(w, device=dev, tokens=a.tokens)
+    inp = make_inputs(w, device=dev, tokens=tokens)
     T, H, I, E, K = inp.x.shape[0], sh.hidden, sh.intermediate, sh.n_experts, sh.top_k
     S = T * K
     flags = {"auto": 0, "stream": gl.PATH_STREAM, "grouped": gl.PATH_GROUPED}[a.path]
@@ -309,13 +341,14 @@ def main():
         ach = kb / (kern_ms[dom] * 1e-3) / 1e9 if kb else None
         roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": ach / HBM_PEAK_GBS if ach else None,
-                "traffic": traffic_for(dom, a.workload), "kernel": dom,
+                "traffic": traffic_for(dom, workload), "kernel": dom,
                 "kernel_ms": kern_ms[dom], "algorithmic_bytes": kb}
     else:
         ach = kf / (kern_ms[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
-                "frac": ach / peak, "traffic": traffic_for(dom, a.workload),
+                "frac": ach / peak, "traffic": traffic_for(dom, workload),
                 "kernel": dom, "kernel_ms": kern_ms[dom], "algorithmic_flops": kf}
+    roof["traffic_source"] = traffic_source(dom, workload, roof["traffic"])
     layer_bytes = touched * 3 * H * I * wbytes + E * H * 4 + 2 * T * H * inp.x.element_size()
     layer_flops = 2.0 * S * 3 * H * I
     roof_ms = max(layer_bytes / (HBM_PEAK_GBS * 1e9), layer_flops / (peak * 1e12)) * 1e3
@@ -334,7 +367,7 @@ def main():
         "vs_baseline": None,
         "dtype": {"fp8": "fp8", "f32": "f32", "mxfp4": "mxfp4"}.get(w.weight_dtype, "bf16"),
         "data": "synthetic",
-        "config": {"workload": a.workload, "tokens": T, "hidden": H,
+        "config": {"workload": workload, "tokens": T, "hidden": H,
                    "intermediate": I, "experts": E, "groups": sh.n_groups,
                    "topk_groups": sh.topk_groups, "top_k": K,
                    "routed_scale": sh.routed_scale, "path": a.path,
@@ -357,7 +390,8 @@ def main():
         res["graph"] = graph
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, sh, a.cpu_seconds)
-    print(json.dumps(res), flush=True)
+    del inp, ws, out
+    return res
 
 
 if __name__ == "__main__":

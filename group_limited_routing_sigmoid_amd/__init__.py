@@ -29,7 +29,9 @@ SYMBOLS = ("beam_status_string", "beam_moe_validate", "beam_moe_workspace_bytes"
            "beam_moe_forward", "beam_moe_timer_create", "beam_moe_timer_destroy",
            "beam_moe_timer_reset", "beam_moe_timer_count", "beam_moe_timer_read",
            "beam_moe_forward_timed", "beam_moe_bias_update", "beam_moe_bias_gamma",
-           "beam_moe_forward_residual", "beam_moe_quant_mxfp8")
+           "beam_moe_forward_residual", "beam_moe_quant_mxfp8",
+           "beam_moe_forward_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class Desc(ctypes.Structure):
@@ -72,6 +74,8 @@ def lib():
         L.beam_moe_forward.argtypes = [D, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                        vp, vp, vp, vp, sz, vp]
         L.beam_moe_forward_timed.argtypes = L.beam_moe_forward.argtypes + [vp]
+        L.beam_moe_forward_noalloc.argtypes = [D, i64, vp, vp, vp, vp, vp, vp, vp, vp,
+                                               vp, vp, vp, vp]
         L.beam_moe_forward_residual.argtypes = [D, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                                 ctypes.c_float, i32, vp, vp, vp, sz, vp]
         L.beam_moe_timer_create.argtypes = [i32, ctypes.POINTER(vp)]
@@ -364,4 +368,24 @@ def forward(desc: Desc, x: torch.Tensor, w_router: Optional[torch.Tensor],
                "beam_moe_forward_timed")
     if return_routing:
         return out, idx, w, logits
+    return out
+
+
+def forward_noalloc(desc: Desc, x: torch.Tensor, w_router: Optional[torch.Tensor],
+                    bias: Optional[torch.Tensor], w_gate_up: torch.Tensor,
+                    w_down: torch.Tensor, out: torch.Tensor,
+                    s_gate_up: Optional[torch.Tensor] = None,
+                    s_down: Optional[torch.Tensor] = None,
+                    topk_idx: Optional[torch.Tensor] = None,
+                    topk_w: Optional[torch.Tensor] = None,
+                    logits: Optional[torch.Tensor] = None, stream=None):
+    """beam_moe_forward_noalloc: the block with the library's own per-device
+    scratch array as workspace (at most NOALLOC_SCRATCH_BYTES).  Every output
+    is the caller's; nothing is allocated.  Calls that may overlap on one GPU
+    race on the shared array."""
+    T, dev = x.shape[0], x.device
+    _check(lib().beam_moe_forward_noalloc(
+        ctypes.byref(desc), T, _p(x), _p(w_router), _p(bias), _p(w_gate_up),
+        _p(s_gate_up), _p(w_down), _p(s_down), _p(out), _p(topk_idx), _p(topk_w),
+        _p(logits), _stream(stream, dev)), "beam_moe_forward_noalloc")
     return out

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "internal.h"
 
@@ -429,6 +431,60 @@ int beam_moe_forward_residual(const beam_moe_desc* d, int64_t T, const void* x,
   ep.residual = residual;
   return forward_impl(d, T, x, w_router, bias, w_gate_up, s_gate_up, w_down, s_down, out,
                       nullptr, nullptr, nullptr, workspace, ws_bytes, stream, nullptr, &ep);
+}
+
+}  // extern "C"
+
+// ---- forward for callers that cannot allocate ------------------------------
+// The workspace of beam_moe_forward_noalloc: a file-scope device array; every
+// GPU the library runs on holds its own copy until the process ends.  In
+// host code its name is a host-side stand-in, not a device address: host
+// code uses only the per-device address looked up below.
+static __device__ __align__(256) unsigned char scratch[BEAM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// Address of the current device's copy of `scratch`, looked up once per
+// device with that device current.
+int current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return BEAM_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return BEAM_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BEAM_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BEAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int beam_moe_forward_noalloc(const beam_moe_desc* d, int64_t T, const void* x,
+                             const float* w_router, const float* bias,
+                             const void* w_gate_up, const void* s_gate_up,
+                             const void* w_down, const void* s_down, void* out,
+                             int32_t* topk_idx, float* topk_w, float* logits,
+                             void* stream) {
+  Plan p;
+  int st = make_plan(d, T, &p);
+  if (st != BEAM_OK) return st;
+  if (T == 0) return BEAM_OK;
+  if (p.total > BEAM_NOALLOC_SCRATCH_BYTES) return BEAM_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = current_scratch(&ws);
+  if (st != BEAM_OK) return st;
+  return forward_impl(d, T, x, w_router, bias, w_gate_up, s_gate_up, w_down, s_down,
+                      out, topk_idx, topk_w, logits, ws, BEAM_NOALLOC_SCRATCH_BYTES,
+                      stream, nullptr);
 }
 
 int beam_moe_forward_timed(const beam_moe_desc* d, int64_t T, const void* x,

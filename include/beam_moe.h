@@ -197,6 +197,31 @@ int beam_moe_forward(const beam_moe_desc* desc, int64_t T, const void* x,
                      int32_t* topk_idx, float* topk_w, float* logits,
                      void* workspace, size_t ws_bytes, void* stream);
 
+/* beam_moe_forward for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The workspace is instead a device array inside the
+ * library, BEAM_NOALLOC_SCRATCH_BYTES bytes, of which every GPU the library
+ * runs on holds its own copy until the process ends (looked up once per
+ * device, on the first call with that device current).  The call allocates
+ * nothing and makes no hipMalloc/hipFree.
+ *   Arguments as beam_moe_forward without workspace and ws_bytes; `stream`
+ *   must belong to the current device.
+ *   BEAM_ERR_WORKSPACE when beam_moe_workspace_bytes(desc, T) exceeds
+ *   BEAM_NOALLOC_SCRATCH_BYTES (64 MiB: bf16 Beam-layer batches up to about
+ *   500 tokens, FP8 about 580, MXFP4 about 320); nothing is launched then.
+ * All calls on one GPU share its array: calls that may overlap on one GPU
+ * (on different streams, or from different host threads without ordering)
+ * race and give undefined results.  Nothing in the array needs to start
+ * cleared: every call writes what it reads.  Results are bitwise identical
+ * to beam_moe_forward's. */
+#define BEAM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int beam_moe_forward_noalloc(const beam_moe_desc* desc, int64_t T, const void* x,
+                             const float* w_router, const float* bias,
+                             const void* w_gate_up, const void* s_gate_up,
+                             const void* w_down, const void* s_down, void* out,
+                             int32_t* topk_idx, float* topk_w, float* logits,
+                             void* stream);
+
 /* beam_moe_forward followed, in the same combine kernel, by the step after
  * the block in a Beam layer stack: the post-sublayer RMSNorm of SandwichNorm
  * and the depth-scaled FP32 residual stream ("Reflection Beam", section

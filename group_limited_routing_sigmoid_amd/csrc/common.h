@@ -35,6 +35,20 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Buffer resource for raw 16-byte loads from base (bytes: the extent the
+// hardware checks; loads past it return zeros).  Third word as gfx9 raw
+// buffers take it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+// 16-byte load at byte offset voff + soff from a buffer resource (soff
+// wave-uniform: it goes in a scalar register).
+__device__ __forceinline__ u32x4 buf16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 __device__ __forceinline__ void st16(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }

@@ -8,15 +8,15 @@
 //   gate/up  h[slot, c] = silu(x[tok] . W_gu[e, c]) * (x[tok] . W_gu[e, I+c])
 //   down     y[slot, n] = h[slot] . W_d[e, n]
 //
-// Work is the list of (expert, 256-slot M tile) entries built by the
-// permutation kernels, crossed with 256-wide N tiles.  A gate/up N tile holds
-// 128 gate rows of W_gu and the 128 matching up rows, so every wave owns both
-// halves of its channels and applies silu(g)*u in registers; x rows are
-// gathered by slot inside the A loads (no permuted copy of x).  Tiles move
-// from global memory straight into LDS (global_load_lds_dwordx4), double
-// buffered, 16-byte chunks XOR-swizzled by row so the MFMA operand reads are
-// bank-conflict free; operand fragments are double buffered in registers.
-// 8 waves (2 per SIMD) each compute 128x64 with 32x32x16 bf16 MFMA.
+// Work is the list of (expert, M tile) entries built by the permutation
+// kernels, crossed with 256-wide N tiles.  A gate/up N tile holds 128 gate
+// rows of W_gu and the 128 matching up rows, so every wave owns both halves
+// of its channels and applies silu(g)*u in registers; x rows are gathered by
+// slot inside the A loads (no permuted copy of x).  Tiles move from global
+// memory straight into LDS, 16-byte chunks XOR-swizzled by row so the MFMA
+// operand reads are bank-conflict free.  256-row tiles: four waves of
+// 128x128 (below); 128- and 160-row tiles for experts holding few rows:
+// eight waves with a three-stage copy ring (further below).
 //
 // Tile layout, DMA pattern and the XCD-aware tile order: grouped_tile.h.
 //
@@ -123,89 +123,286 @@ __device__ __forceinline__ void tile_mainloop_rows(
   }
 }
 
+// ---- 256 x 256 tiles, four waves of 128 x 128 ---------------------------------
+// For batches whose experts reuse their weights over several M tiles.  One
+// wave per SIMD, each wave 128 rows x 128 columns: its 256 fp32 sums stay in
+// the accumulation registers, and a stage's fragment reads from LDS are
+// 128 KiB per workgroup (two thirds of the eight-wave layout's).  Wave (wm,
+// wn) takes the 32-row A fragments 2f + wm (f = 0..3), so a partial tile's
+// valid rows split evenly over the two SIMD halves; its B rows are gate rows
+// 64 wn .. +63 with the matching up rows 128 + 64 wn .. +63 (gate/up), or
+// rows 128 wn .. +127 (down).  Stages are 64 deep, double buffered in LDS
+// (same tile layout and swizzle as the other forms), and staged through two
+// register sets: stage s is loaded during stage s - 2 and written to LDS late
+// in stage s - 1, so a load has about 1.75 stages to arrive (a direct copy
+// into LDS can only be issued once the buffer it fills is free).
+// The wave's instruction stream is ordered by hand (scheduling fences after
+// every product): a wave issues in order, so a burst of memory instructions
+// between bursts of products leaves its SIMD's matrix core idle while it
+// issues them; one memory instruction after each product keeps it fed.  The
+// stage boundary sits inside the last k16 step: half of its products are
+// issued, the wave waits for its LDS traffic and meets the others, then
+// reads the next stage's first fragments between the other half.  Same
+// products in the same k order as the other tile forms: bit-identical.
+namespace w4 {
+
+constexpr int kThreads4 = 256;
+constexpr int kBuf = 2 * kTileBytes;   // bytes of one LDS stage
+
+// s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0) / lgkmcnt(0) alone (vmcnt 63 and
+// expcnt 7 mean "no wait") / lgkmcnt(0) then s_barrier, as builtins so the
+// compiler's wait-count tracking knows the counters afterwards (it cannot
+// see into inline assembly).
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// lgkmcnt(8): all but this wave's last 8 LDS operations have completed
+__device__ __forceinline__ void wait_lds_but8() { __builtin_amdgcn_s_waitcnt(0xC87F); }
+__device__ __forceinline__ void wait_lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+}
+
+// Per-lane byte offsets, computed once per tile.  With the swizzle
+// swz(row, chunk), a row's key (row ^ (row >> 3)) & 7 depends only on the
+// lane and on the parity of the 32-row block (the 8-row region) the row
+// lies in, so a few bases plus constants address every access.
+struct Addr4 {
+  uint32_t a_vo[8];     // global: this lane's A row and chunk, copy region i
+  uint32_t b_vo[2];     // global: this lane's row and chunk inside a B region of parity p
+  uint32_t b_so[8];     // global, wave-uniform: B region i's first row
+  uint32_t st;          // LDS: this lane's 16 bytes in the wave's first region
+  uint32_t a_rd[4];     // LDS: A fragment 0 of k16 step kk
+  uint32_t b_rd[4][2];  // LDS: B fragment n of k16 step kk, n % 2 = p, less bimm(n)
+};
+
+// LDS byte offset of B fragment n beyond b_rd[.][n % 2]
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(
+__device__ __forceinline__ constexpr int bimm(int n) {
+  return (MODE == kGateUp) ? (n / 2) * 16384 : (n / 2) * 8192;
+}
+
+struct Frags4 {
+  bf16x8 a[4], b[4];
+};
+
+// Fragment read j of a k16 step: A fragment j (j < 4, rows 32 (2 j + wm)),
+// or B fragment j - 4, from the stage at LDS byte offset buf.
+template <int NF, int MODE>
+__device__ __forceinline__ void read_frag(Frags4& f, int j, const unsigned char* L,
+                                          uint32_t buf, int kk, const Addr4& ad) {
+  if (j < 4) {
+    if (j < NF)
+      f.a[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(L + buf + ad.a_rd[kk] + j * 8192));
+  } else {
+    const int n = j - 4;
+    f.b[n] = as_bf16x8(
+        *reinterpret_cast<const u32x4*>(L + buf + ad.b_rd[kk][n & 1] + bimm<MODE>(n)));
+  }
+}
+
+// Product j of a k16 step: A fragment j / 4 with B fragment j % 4.
+template <int NF>
+__device__ __forceinline__ void mfma_j(const Frags4& f, int j, f32x16 (&acc)[4][4]) {
+  if (j / 4 < NF) acc[j / 4][j % 4] = mfma32x32x16(f.a[j / 4], f.b[j % 4], acc[j / 4][j % 4]);
+}
+
+// One 16-byte-per-lane copy of a stage (1 KiB): copy i < 8 is A region
+// wave + 4 i, copy i >= 8 is B region wave + 4 (i - 8), into the stage at
+// LDS byte offset buf.  Buffer loads straight into LDS: the lane's 16 bytes
+// land at M0 + 16 lane, so M0 is the region's (wave-uniform) start.
+__device__ __forceinline__ void copy_i(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                       unsigned char* L, uint32_t buf, int k, int i,
+                                       const Addr4& ad, int wave) {
+  if (i < 8) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        ra, (__attribute__((address_space(3))) void*)(L + buf + (wave + 4 * i) * 1024), 16,
+        ad.a_vo[i], 2 * k, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rb, (__attribute__((address_space(3))) void*)(L + buf + kTileBytes + (wave + 4 * (i - 8)) * 1024),
+        16, ad.b_vo[i & 1], ad.b_so[i - 8] + 2 * k, 0, 0);
+  }
+}
+
+// Stages are filled by copies straight into LDS, double buffered.  A buffer
+// is free once every wave has passed the barrier that ends the reads of the
+// stage it held (inside the stage's last k16 step): stage t + 2's weight (B)
+// copies go out right then, between the step's remaining products, and its
+// A copies in the next stage's first step; all must have landed by the next
+// barrier, about one stage later (the most two 64 KiB buffers allow).
+template <int NF, int MODE>
+__device__ __forceinline__ void mainloop4(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                          int nk, unsigned char* L, const Addr4& ad,
+                                          f32x16 (&acc)[4][4]) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  Frags4 f0, f1;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) copy_i(ra, rb, L, 0, 0, (i + 8) % 16, ad, wave);
+#pragma unroll
+  for (int i = 8; i < 16; ++i) copy_i(ra, rb, L, kBuf, min(1, nk - 1) * BK, i, ad, wave);
+  // stage 0 landed: all but stage 1's 8 B copies (vmcnt(8))
+  __builtin_amdgcn_s_waitcnt(0x0F78);
+  wait_lds_barrier();
+#pragma unroll
+  for (int j = 0; j < 8; ++j) read_frag<NF, MODE>(f0, j, L, 0, 0, ad);
+  for (int t = 0; t < nk; ++t) {
+    const uint32_t cur = (t & 1) * kBuf, nb = kBuf - cur;
+    // stage t + 1's A copies go to nb in step 0 (its B copies went out at the
+    // end of the previous stage), stage t + 2's B copies to cur once this
+    // stage's reads are done; beyond the last stage the copies repeat it (in
+    // bounds, never read)
+    const int k1 = min(t + 1, nk - 1) * BK, k2 = min(t + 2, nk - 1) * BK;
+    wait_lds();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      mfma_j<NF>(f0, j, acc);
+      if (j < 8) read_frag<NF, MODE>(f1, j, L, cur, 1, ad);
+      else copy_i(ra, rb, L, nb, k1, j - 8, ad, wave);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_lds();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      mfma_j<NF>(f1, j, acc);
+      if (j < 8) read_frag<NF, MODE>(f0, j, L, cur, 2, ad);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_lds();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      mfma_j<NF>(f0, j, acc);
+      if (j < 8) read_frag<NF, MODE>(f1, j, L, cur, 3, ad);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_lds();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      mfma_j<NF>(f1, j, acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // this wave's reads of cur are done and its copies of stage t + 1 have
+    // landed; then every wave's have
+    wait_all();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int j = 8; j < 16; ++j) {
+      mfma_j<NF>(f1, j, acc);
+      if (j < 12) {
+        read_frag<NF, MODE>(f0, 2 * (j - 8), L, nb, 0, ad);
+        read_frag<NF, MODE>(f0, 2 * (j - 8) + 1, L, nb, 0, ad);
+      } else {
+        copy_i(ra, rb, L, cur, k2, 8 + 2 * (j - 12), ad, wave);
+        copy_i(ra, rb, L, cur, k2, 9 + 2 * (j - 12), ad, wave);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_all();
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads4) void grouped_gemm_bf16_w4(
     const uint16_t* __restrict__ a_src,   // gate/up: x [T,H]; down: h [S,I]
     const uint16_t* __restrict__ w,       // W_gu [E,2I,H] or W_d [E,H,I]
     uint16_t* __restrict__ out,           // gate/up: h [S,I]; down: y [S,H]
     const int32_t* __restrict__ slot_token, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off,
-    const int32_t* __restrict__ meta, int E, int H, int I, int n_nt) {
+    const int32_t* __restrict__ meta, int T, int E, int H, int I, int n_nt) {
   __shared__ __attribute__((aligned(16))) TileLds lds;
-
   Coords tc;
   if (!tile_coords(counts, offsets, tile_off, meta, E, n_nt, tc)) return;
   const int e = tc.e, nt = tc.nt, row0 = tc.row0, row_end = tc.row_end;
   const int K = (MODE == kGateUp) ? H : I;
-
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int wm = wave / 4, wn = wave % 4;
-
-  // 32-bit element offsets from wave-uniform bases (the caller guarantees
-  // S * max(H, I) < 2^31; one expert's weights are far below that).
+  const int lane = threadIdx.x % kWave, l32 = lane % 32, hi = lane / 32;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wm = wave / 2, wn = wave % 2;
   const uint16_t* wbase = (MODE == kGateUp) ? w + static_cast<int64_t>(e) * 2 * I * H
                                             : w + static_cast<int64_t>(e) * H * I;
   const int m_valid = min(BM, row_end - row0);
-  uint32_t a_off[kLoads], b_off[kLoads];
-  bool a_ok[kLoads];
+  // buffer resources: x (or h) and this expert's weight matrix; loads past
+  // either return zeros (the down product's last N tile may pass H)
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(
+      a_src, (MODE == kGateUp) ? static_cast<uint32_t>(T) * H * 2
+                               : static_cast<uint32_t>(row_end) * I * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(
+      wbase, static_cast<uint32_t>((MODE == kGateUp) ? 2 * I * H : H * I) * 2);
+  Addr4 ad;
+  // copy regions of this wave: wave + 4 i (i < 8) of A and of B, 8 rows each;
+  // A rows past the tile's last valid row copy that row (their sums are
+  // never stored)
 #pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const int r = dma_row(wave, lane, i);
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * (wave + 4 * i) + lane / 8;
     const int c = dma_chunk(r, lane);
-    a_ok[i] = r < m_valid;
-    int slot = row0 + r;
-    if (slot > row_end - 1) slot = row_end - 1;  // padded rows: any valid row
-    if (MODE == kGateUp) {
-      a_off[i] = static_cast<uint32_t>(slot_token[slot]) * H + c * 8;
-      // rows 0..127: gate channels nt*128 + r; rows 128..255: up channels
-      const int wrow = (r < 128) ? (nt * 128 + r) : (I + nt * 128 + (r - 128));
-      b_off[i] = static_cast<uint32_t>(wrow) * H + c * 8;
-    } else {
-      a_off[i] = static_cast<uint32_t>(slot) * I + c * 8;
-      // the last N tile may run past H (H is a multiple of 128 only)
-      b_off[i] = static_cast<uint32_t>(min(nt * BN + r, H - 1)) * I + c * 8;
+    const int slot = min(row0 + r, row_end - 1);
+    ad.a_vo[i] = (((MODE == kGateUp) ? static_cast<uint32_t>(slot_token[slot]) * H
+                                     : static_cast<uint32_t>(slot) * I) + c * 8) * 2;
+    const int r0 = 8 * (wave + 4 * i);
+    const int wrow0 = (MODE == kGateUp) ? ((r0 < 128) ? nt * 128 + r0 : I + nt * 128 + (r0 - 128))
+                                        : nt * BN + r0;
+    ad.b_so[i] = static_cast<uint32_t>(wrow0) * K * 2;
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    // rows 8 (wave + 4 i) + lane / 8 with i % 2 = p: key (lane / 8) ^ (wave + 4 p)
+    const int c = (lane % 8) ^ (((lane / 8) ^ (wave + 4 * p)) & 7);
+    ad.b_vo[p] = (static_cast<uint32_t>(lane / 8) * K + c * 8) * 2;
+  }
+  ad.st = wave * 1024 + 16 * lane;
+  const int key_a = ((lane & 7) ^ ((4 * wm + l32 / 8) & 7)) & 7;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    ad.a_rd[kk] = (32 * wm + l32) * kRowBytes + ((((2 * kk + hi) ^ key_a) & 7) << 4);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int key_b = ((lane & 7) ^ ((4 * p + l32 / 8) & 7)) & 7;
+      const int rowb = ((MODE == kGateUp) ? wn * 64 : wn * 128) + p * 32 + l32;
+      ad.b_rd[kk][p] = kTileBytes + rowb * kRowBytes + ((((2 * kk + hi) ^ key_b) & 7) << 4);
     }
   }
-  // A rows of this wave: wm*128 + mi*32 + lane%32.
-  // B rows: gate/up -> gate wn*32 + lane%32 and up 128 + wn*32 + lane%32;
-  //         down    -> wn*64 + ni*32 + lane%32.
-  int arow[4], brow[2];
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) arow[i] = wm * 128 + i * 32 + lane % 32;
+  for (int f = 0; f < 4; ++f)
 #pragma unroll
-  for (int n = 0; n < 2; ++n)
-    brow[n] = (MODE == kGateUp) ? (n * 128 + wn * 32 + lane % 32)
-                                : (wn * 64 + n * 32 + lane % 32);
-
-  f32x16 acc[4][2];
+    for (int n = 0; n < 4; ++n) acc[f][n] = f32x16{};
+  // this wave's fragments holding a valid row: 2f + wm < ceil(m_valid / 32)
+  const int g = (m_valid + 31) / 32;
+  const int nf = min(4, max(0, (g - wm + 1) / 2));
+  const int nk = K / BK;
+  unsigned char* L = &lds[0][0];
+  switch (nf) {
+    case 4: mainloop4<4, MODE>(ra, rb, nk, L, ad, acc); break;
+    case 3: mainloop4<3, MODE>(ra, rb, nk, L, ad, acc); break;
+    case 2: mainloop4<2, MODE>(ra, rb, nk, L, ad, acc); break;
+    case 1: mainloop4<1, MODE>(ra, rb, nk, L, ad, acc); break;
+    default: mainloop4<0, MODE>(ra, rb, nk, L, ad, acc); break;
+  }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int n = 0; n < 2; ++n) acc[i][n] = f32x16{};
-  tile_mainloop_rows(wave_frags(m_valid, wm), a_src, a_off, a_ok, K, wbase, b_off, 0,
-                     K / BK, lds, acc, arow, brow);
-
-  // ---- epilogue -------------------------------------------------------------
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int f = 0; f < 4; ++f) {
+    if (f >= nf) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = row0 + wm * 128 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+      const int row = row0 + 32 * (2 * f + wm) + 8 * (r / 4) + 4 * hi + (r % 4);
       if (row >= row_end) continue;
       if (MODE == kGateUp) {
-        const int ch = nt * 128 + wn * 32 + lane % 32;
-        const float h = silu(acc[i][0][r]) * acc[i][1][r];
-        out[static_cast<int64_t>(row) * I + ch] = f32_to_bf16_bits(h);
-      } else {
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
-          const int col = nt * BN + wn * 64 + n * 32 + lane % 32;
-          if (col < H) out[static_cast<int64_t>(row) * H + col] = f32_to_bf16_bits(acc[i][n][r]);
+          const int ch = nt * 128 + wn * 64 + n * 32 + l32;
+          const float hv = silu(acc[f][n][r]) * acc[f][n + 2][r];
+          out[static_cast<int64_t>(row) * I + ch] = f32_to_bf16_bits(hv);
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const int col = nt * BN + wn * 128 + n * 32 + l32;
+          if (col < H) out[static_cast<int64_t>(row) * H + col] = f32_to_bf16_bits(acc[f][n][r]);
         }
       }
     }
   }
 }
+
+}  // namespace w4
 
 // ---- 128- and 160-row tiles with a ring of three copy stages ----------------
 // For batches whose experts hold few rows the products are bound by the
@@ -484,13 +681,14 @@ hipError_t launch_grouped_bf16(const Plan& p, const void* x,
   if (p.bm == 128) { BEAM_SMALL_TILES(128); }
   if (p.bm == 160) { BEAM_SMALL_TILES(160); }
 #undef BEAM_SMALL_TILES
-  BEAM_LAUNCH(tm, "grouped_gate_up_bf16", grouped_gemm_bf16<kGateUp>, grid_for(p, nt_gu),
-              dim3(kThreads), 0, s, static_cast<const uint16_t*>(x),
+  BEAM_LAUNCH(tm, "grouped_gate_up_bf16", w4::grouped_gemm_bf16_w4<kGateUp>, grid_for(p, nt_gu),
+              dim3(w4::kThreads4), 0, s, static_cast<const uint16_t*>(x),
               static_cast<const uint16_t*>(w_gate_up), h, slot_token, counts,
-              offsets, toff, meta, p.E, p.H, p.I, nt_gu);
-  BEAM_LAUNCH(tm, "grouped_down_bf16", grouped_gemm_bf16<kDown>, grid_for(p, nt_dn),
-              dim3(kThreads), 0, s, h, static_cast<const uint16_t*>(w_down), y,
-              slot_token, counts, offsets, toff, meta, p.E, p.H, p.I, nt_dn);
+              offsets, toff, meta, static_cast<int>(p.T), p.E, p.H, p.I, nt_gu);
+  BEAM_LAUNCH(tm, "grouped_down_bf16", w4::grouped_gemm_bf16_w4<kDown>, grid_for(p, nt_dn),
+              dim3(w4::kThreads4), 0, s, h, static_cast<const uint16_t*>(w_down), y,
+              slot_token, counts, offsets, toff, meta, static_cast<int>(p.T), p.E, p.H, p.I,
+              nt_dn);
   return hipGetLastError();
 }
 

@@ -377,28 +377,50 @@ __global__ __launch_bounds__(kThreads4) void grouped_gemm_bf16_w4(
     case 1: mainloop4<1, MODE>(ra, rb, nk, L, ad, acc); break;
     default: mainloop4<0, MODE>(ra, rb, nk, L, ad, acc); break;
   }
+  // Epilogue through LDS: each lane holds 16 rows of one column, so the wave
+  // writes its output tile (bf16) to its own LDS region first and stores it
+  // back as 16-byte row pieces.  Every wave has finished reading the last
+  // stage once all have passed the barrier.
+  __builtin_amdgcn_s_barrier();
+  constexpr int kCols = (MODE == kGateUp) ? 64 : 128;  // output columns per wave
+  // LDS row pitch (bytes): gate/up rows padded by 16 bytes; the down
+  // product's 4 x 128 rows of 256 bytes fill the stage buffers exactly
+  constexpr int kPitch = (MODE == kGateUp) ? 2 * kCols + 16 : 2 * kCols;
+  static_assert(4 * 128 * kPitch <= static_cast<int>(sizeof(TileLds)), "epilogue tile fits");
+  unsigned char* R = L + wave * (128 * kPitch);
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
     if (f >= nf) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = row0 + 32 * (2 * f + wm) + 8 * (r / 4) + 4 * hi + (r % 4);
-      if (row >= row_end) continue;
+      const int lr = 32 * f + 8 * (r / 4) + 4 * hi + (r % 4);  // row inside the wave's 128
       if (MODE == kGateUp) {
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
-          const int ch = nt * 128 + wn * 64 + n * 32 + l32;
           const float hv = silu(acc[f][n][r]) * acc[f][n + 2][r];
-          out[static_cast<int64_t>(row) * I + ch] = f32_to_bf16_bits(hv);
+          *reinterpret_cast<uint16_t*>(R + lr * kPitch + 2 * (n * 32 + l32)) = f32_to_bf16_bits(hv);
         }
       } else {
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const int col = nt * BN + wn * 128 + n * 32 + l32;
-          if (col < H) out[static_cast<int64_t>(row) * H + col] = f32_to_bf16_bits(acc[f][n][r]);
-        }
+        for (int n = 0; n < 4; ++n)
+          *reinterpret_cast<uint16_t*>(R + lr * kPitch + 2 * (n * 32 + l32)) =
+              f32_to_bf16_bits(acc[f][n][r]);
       }
     }
+  }
+  wait_lds();
+  // 16-byte pieces: kCols / 8 per row; a lane takes pieces lane, lane + 64, ...
+  constexpr int kPieces = 128 * kCols / 8;
+  const int col0 = (MODE == kGateUp) ? nt * 128 + wn * 64 : nt * BN + wn * 128;
+  const int ld = (MODE == kGateUp) ? I : H;
+#pragma unroll
+  for (int q = lane; q < kPieces; q += kWave) {
+    const int lr = q / (kCols / 8), pc = q % (kCols / 8);
+    const int row = row0 + 32 * (2 * (lr / 32) + wm) + lr % 32;
+    const int col = col0 + 8 * pc;
+    if ((lr / 32) >= nf || row >= row_end || col >= ld) continue;
+    st16(out + static_cast<int64_t>(row) * ld + col,
+         *reinterpret_cast<const u32x4*>(R + lr * kPitch + 16 * pc));
   }
 }
 

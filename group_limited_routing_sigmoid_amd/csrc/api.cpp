@@ -154,7 +154,7 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
   p->off_slot_of = take(S * 4);
   p->off_meta = take(kMetaWords * 4);
   p->off_active = take(E * 4);
-  p->off_tile_off = take((E + 1) * 4);
+  p->off_tile_off = take((tt_expert(static_cast<int>(E)) + p->max_tiles) * 4);
   // h is fp32 on the fp32 path and before the MXFP8 quantisation of the
   // streaming 4-bit path, bf16 otherwise; the grouped e4m3 and 4-bit gate/up
   // GEMMs write only its codes

@@ -43,16 +43,6 @@ __device__ __forceinline__ int dma_chunk(int row, int lane) {
   return (lane % 8) ^ ((row ^ (row >> 3)) & 7);
 }
 
-// Largest e with tile_off[e] * n_nt <= L (tile_off is non-decreasing).
-__device__ __forceinline__ int find_expert(const int32_t* tile_off, int E, int n_nt, int L) {
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tile_off[mid] * n_nt <= L) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 struct Coords {
   int e;        // expert
   int nt;       // N tile
@@ -61,27 +51,41 @@ struct Coords {
 };
 
 // Workgroups are dealt round-robin to the 8 XCDs, each with its own L2, and
-// start roughly in order.  Workgroup b takes logical tile
-//   256 (b / 256) + 32 (b % 8) + (b / 8) % 32,
-// so the chip works through the logical order in rounds of 256 tiles (one
-// tile per compute unit), every XCD taking 32 consecutive ones.  The logical
-// order is: expert, then bands of 8 M tiles, then quads of 4 N tiles, with
-// the M tile moving fastest inside a quad.  At any time the 8 XCDs then
-// share one window of one expert's weights and token rows in the last-level
-// cache, and each XCD's 32 tiles are about 8 M x 4 N tiles whose operand
-// slices its L2 shares (measured on the 16K-token layer: gate/up 8.20 ->
-// 7.53 ms against XCDs walking separate eighths of the order; the blocking
-// alone, without the shared window, gained nothing).
-// Returns false for workgroups past the last logical tile.
+// start roughly in order.  The logical tiles form two sequences: those of
+// hot experts (several M tiles, weights reused) and those of cold experts
+// (one tile, weights streamed once from HBM); inside a sequence the order is
+// expert, then bands of 8 M tiles, then quads of 4 N tiles, the M tile
+// moving fastest inside a quad.  The sequences are cut into chunks of 32
+// tiles, and chunk g = 8 (b / 256) + b % 8 goes to workgroups b of one
+// round of 256 (one tile per compute unit) on one XCD: chunk g is cold when
+// floor((g + 1) C / N) > floor(g C / N) (C cold chunks of N), so cold chunks
+// are spread evenly over the rounds.  Then
+// - the hot chunks of a round are consecutive: the XCDs on them share one
+//   window of one expert's weights and token rows in the last-level cache,
+//   and each XCD's 32 tiles (about 8 M x 4 N) share operand slices in its L2
+//   (measured on the 16K-token layer: gate/up 8.20 -> 7.53 ms against XCDs
+//   walking separate eighths of an expert-major order);
+// - the cold chunks stream weights from HBM while the hot ones keep the
+//   matrix cores busy, instead of the chip alternating between the two.
+// Returns false for workgroups past the last tile.
 __device__ __forceinline__ bool tile_coords(const int32_t* counts, const int32_t* offsets,
-                                            const int32_t* tile_off, const int32_t* meta,
+                                            const int32_t* tt, const int32_t* meta,
                                             int E, int n_nt, Coords& c, int bm = BM) {
-  const int n_log = meta[kMetaTiles] * n_nt;
+  const int nm = meta[kMetaTiles], nmh = meta[kMetaHot];
+  const int nh = nmh * n_nt, nc = (nm - nmh) * n_nt;  // logical tiles per sequence
+  const int chh = (nh + kXcdRun - 1) / kXcdRun, chc = (nc + kXcdRun - 1) / kXcdRun;
+  const int ch = chh + chc;
   const int b = blockIdx.x;
-  const int L = (b / kRound) * kRound + (b % kXcds) * kXcdRun + (b / kXcds) % kXcdRun;
-  if (L >= n_log) return false;
-  const int e = find_expert(tile_off, E, n_nt, L);
-  const int t0 = tile_off[e], nt_e = tile_off[e + 1] - t0;
+  const int g = (b / kRound) * kXcds + b % kXcds;
+  if (g >= ch) return false;
+  const int c0 = static_cast<int>(static_cast<int64_t>(g) * chc / ch);
+  const int c1 = static_cast<int>(static_cast<int64_t>(g + 1) * chc / ch);
+  const bool cold = c1 > c0;
+  const int L = (cold ? c0 : g - c0) * kXcdRun + (b / kXcds) % kXcdRun;
+  if (L >= (cold ? nc : nh)) return false;
+  const int mbase = cold ? nmh : 0;  // the sequence's first M tile
+  const int e = tt[tt_expert(E) + mbase + L / n_nt];
+  const int t0 = tt[e] - mbase, nt_e = tt[tt_count(E) + e];
   const int j = L - t0 * n_nt;
   const int band = j / (kBandM * n_nt);
   const int gm = min(kBandM, nt_e - band * kBandM);
@@ -130,11 +134,11 @@ __device__ __forceinline__ void ring_barrier(int n) {
 }
 #undef BEAM_RING_BARRIER
 
-// Grid of a grouped launch: an upper bound on the logical tiles, rounded to
-// whole rounds (the workgroup -> tile map is a bijection on each round).
+// Grid of a grouped launch: whole rounds covering an upper bound on the
+// chunks (each of the two sequences may end in a partial chunk).
 inline dim3 grid_for(const Plan& p, int n_nt) {
-  const int64_t rounds = ceil_div(p.max_tiles * n_nt, kRound);
-  return dim3(static_cast<unsigned>(rounds * kRound));
+  const int64_t chunks = ceil_div(p.max_tiles * n_nt, kXcdRun) + 1;
+  return dim3(static_cast<unsigned>(ceil_div(chunks, kXcds) * kRound));
 }
 
 }  // namespace tile

@@ -58,8 +58,22 @@ static inline P* ws_at(void* ws, size_t off) {
   return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
 }
 
-// meta words (int32) at off_meta: [0] = grouped M tiles, [1] = active experts
-constexpr int kMetaTiles = 0, kMetaActive = 1, kMetaWords = 4;
+// meta words (int32) at off_meta: [0] = grouped M tiles, [1] = active
+// experts, [2] = M tiles of hot experts
+constexpr int kMetaTiles = 0, kMetaActive = 1, kMetaHot = 2, kMetaWords = 4;
+
+// An expert whose tokens fill at least this many M tiles reuses its weights
+// over several tiles ("hot"); the others stream theirs once ("cold").
+constexpr int kHotTiles = 2;
+
+// Tile table (int32 words at off_tile_off), written by the permutation:
+//   [0, E]            first M tile of each expert in the combined order: the
+//                     hot experts' tiles first, then the cold experts', each
+//                     group in expert order
+//   [E + 1, 2E + 1)   M tiles of each expert
+//   [2E + 2, ...)     the expert of each M tile of the combined order
+__host__ __device__ constexpr int tt_count(int E) { return E + 1; }
+__host__ __device__ constexpr int tt_expert(int E) { return 2 * E + 2; }
 
 // router.hip
 hipError_t launch_router(const Plan& p, const void* x, const float* w_router,

@@ -58,34 +58,65 @@ __global__ __launch_bounds__(kPermBlock) void perm_rank(
     }
 }
 
-// Inclusive scans of three values at once over the 1024 threads of the
+// Inclusive scans of four values at once over the 1024 threads of the
 // block: within each wave by shifts of 1, 2, .., 32 lanes, then each wave
 // adds the totals of the waves before it (read from LDS).  Integer sums, so
 // any order gives the same result.
-__device__ void block_scan3_incl(int& a, int& b, int& c) {
-  __shared__ int tot[3][kMaxE / kWave];
+__device__ void block_scan4_incl(int (&v)[4]) {
+  __shared__ int tot[4][kMaxE / kWave];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
-    const int ua = __shfl_up(a, off), ub = __shfl_up(b, off), uc = __shfl_up(c, off);
-    if (lane >= off) {
-      a += ua;
-      b += ub;
-      c += uc;
-    }
+    int u[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) u[q] = __shfl_up(v[q], off);
+    if (lane >= off)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] += u[q];
   }
-  if (lane == kWave - 1) {
-    tot[0][wave] = a;
-    tot[1][wave] = b;
-    tot[2][wave] = c;
-  }
+  if (lane == kWave - 1)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tot[q][wave] = v[q];
   __syncthreads();
-  for (int w = 0; w < wave; ++w) {
-    a += tot[0][w];
-    b += tot[1][w];
-    c += tot[2][w];
-  }
+  for (int w = 0; w < wave; ++w)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] += tot[q][w];
   __syncthreads();
+}
+
+// Per expert (thread e of a 1024-thread block; experts past E count 0):
+// slots, offsets, the active list, the M tiles (of bm rows, the last holding
+// up to bm + xt) and the tile table, hot experts' tiles first.  Returns the
+// expert's exclusive slot offset.
+__device__ int expert_tables(int e, int c, int E, int bm, int xt, int32_t* __restrict__ counts,
+                             int32_t* __restrict__ offsets, int32_t* __restrict__ meta,
+                             int32_t* __restrict__ active, int32_t* __restrict__ tt) {
+  __shared__ int n_hot;
+  const int nt = (c <= 0) ? 0 : max(1, (c - xt + bm - 1) / bm);
+  const int hot = nt >= kHotTiles;
+  int v[4] = {c, nt, c > 0, hot ? nt : 0};
+  block_scan4_incl(v);
+  if (threadIdx.x == kMaxE - 1) n_hot = v[3];
+  __syncthreads();
+  const int off = v[0] - c;
+  const int t_before = v[1] - nt, hot_before = v[3] - (hot ? nt : 0);
+  const int pos = hot ? hot_before : n_hot + (t_before - hot_before);
+  if (e < E) {
+    counts[e] = c;
+    offsets[e] = off;
+    if (c > 0) active[v[2] - 1] = e;
+    tt[e] = pos;
+    tt[tt_count(E) + e] = nt;
+    for (int t = 0; t < nt; ++t) tt[tt_expert(E) + pos + t] = e;
+  }
+  if (e == E - 1) {
+    offsets[E] = v[0];
+    tt[E] = v[1];
+    meta[kMetaTiles] = v[1];
+    meta[kMetaActive] = v[2];
+    meta[kMetaHot] = n_hot;
+  }
+  return off;
 }
 
 // one block of 1024 threads; thread e handles expert e
@@ -114,25 +145,7 @@ __global__ __launch_bounds__(kMaxE) void perm_scan(
       c += hist[b * E + e];
     }
   }
-  // M tiles of bm rows; the last may hold up to xt more (bm + xt in all)
-  const int nt = (c <= 0) ? 0 : max(1, (c - xt + bm - 1) / bm);
-  const int act = c > 0;
-  int incl = c, tincl = nt, aincl = act;
-  block_scan3_incl(incl, tincl, aincl);
-  const int off = incl - c;
-  const int toff = tincl - nt;
-  if (e < E) {
-    counts[e] = c;
-    offsets[e] = off;
-    if (act) active[aincl - 1] = e;
-    tile_off[e] = toff;
-  }
-  if (e == E - 1) {
-    offsets[E] = incl;
-    tile_off[E] = tincl;
-    meta[kMetaTiles] = tincl;
-    meta[kMetaActive] = aincl;
-  }
+  expert_tables(e, c, E, bm, xt, counts, offsets, meta, active, tile_off);
 }
 
 __global__ __launch_bounds__(kPermBlock) void perm_scatter(
@@ -174,25 +187,8 @@ __global__ __launch_bounds__(kMaxE) void perm_small(
   if (i < E)
 #pragma unroll
     for (int w = 0; w < kWords; ++w) c += __popc(bits[i * kWords + w]);
-  const int nt = (c <= 0) ? 0 : max(1, (c - xt + bm - 1) / bm);
-  const int act = c > 0;
-  int incl = c, tincl = nt, aincl = act;
-  block_scan3_incl(incl, tincl, aincl);
-  const int off = incl - c;
-  const int toff = tincl - nt;
-  if (i < E) {
-    counts[i] = c;
-    offsets[i] = off;
-    off_sh[i] = off;
-    if (act) active[aincl - 1] = i;
-    tile_off[i] = toff;
-  }
-  if (i == E - 1) {
-    offsets[E] = incl;
-    tile_off[E] = tincl;
-    meta[kMetaTiles] = tincl;
-    meta[kMetaActive] = aincl;
-  }
+  const int off = expert_tables(i, c, E, bm, xt, counts, offsets, meta, active, tile_off);
+  if (i < E) off_sh[i] = off;
   __syncthreads();
   if (i < T)
     for (int k = 0; k < K; ++k) {

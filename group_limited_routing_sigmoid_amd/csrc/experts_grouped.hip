@@ -131,11 +131,10 @@ __device__ __forceinline__ void tile_mainloop_rows(
 // wn) takes the 32-row A fragments 2f + wm (f = 0..3), so a partial tile's
 // valid rows split evenly over the two SIMD halves; its B rows are gate rows
 // 64 wn .. +63 with the matching up rows 128 + 64 wn .. +63 (gate/up), or
-// rows 128 wn .. +127 (down).  Stages are 64 deep, double buffered in LDS
-// (same tile layout and swizzle as the other forms), and staged through two
-// register sets: stage s is loaded during stage s - 2 and written to LDS late
-// in stage s - 1, so a load has about 1.75 stages to arrive (a direct copy
-// into LDS can only be issued once the buffer it fills is free).
+// rows 128 wn .. +127 (down).  Stages are 64 deep (same tile layout and
+// swizzle as the other forms), copied straight into LDS: token (or h) rows
+// double buffered, weight rows triple buffered, so the weight copies go out
+// about 1.75 stages before they are read (mainloop4).
 // The wave's instruction stream is ordered by hand (scheduling fences after
 // every product): a wave issues in order, so a burst of memory instructions
 // between bursts of products leaves its SIMD's matrix core idle while it
@@ -147,7 +146,6 @@ __device__ __forceinline__ void tile_mainloop_rows(
 namespace w4 {
 
 constexpr int kThreads4 = 256;
-constexpr int kBuf = 2 * kTileBytes;   // bytes of one LDS stage
 
 // s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0) / lgkmcnt(0) alone (vmcnt 63 and
 // expcnt 7 mean "no wait") / lgkmcnt(0) then s_barrier, as builtins so the
@@ -170,9 +168,9 @@ struct Addr4 {
   uint32_t a_vo[8];     // global: this lane's A row and chunk, copy region i
   uint32_t b_vo[2];     // global: this lane's row and chunk inside a B region of parity p
   uint32_t b_so[8];     // global, wave-uniform: B region i's first row
-  uint32_t st;          // LDS: this lane's 16 bytes in the wave's first region
-  uint32_t a_rd[4];     // LDS: A fragment 0 of k16 step kk
-  uint32_t b_rd[4][2];  // LDS: B fragment n of k16 step kk, n % 2 = p, less bimm(n)
+  uint32_t a_rd[4];     // LDS, inside an A buffer: A fragment 0 of k16 step kk
+  uint32_t b_rd[4][2];  // LDS, inside a B buffer: B fragment n of k16 step kk,
+                        // n % 2 = p, less bimm(n)
 };
 
 // LDS byte offset of B fragment n beyond b_rd[.][n % 2]
@@ -185,18 +183,20 @@ struct Frags4 {
   bf16x8 a[4], b[4];
 };
 
-// Fragment read j of a k16 step: A fragment j (j < 4, rows 32 (2 j + wm)),
-// or B fragment j - 4, from the stage at LDS byte offset buf.
+// Fragment read j of a k16 step: A fragment j (j < 4, rows 32 (2 j + wm))
+// from the A buffer at LDS byte offset abuf, or B fragment j - 4 from the B
+// buffer at bbuf.
 template <int NF, int MODE>
 __device__ __forceinline__ void read_frag(Frags4& f, int j, const unsigned char* L,
-                                          uint32_t buf, int kk, const Addr4& ad) {
+                                          uint32_t abuf, uint32_t bbuf, int kk,
+                                          const Addr4& ad) {
   if (j < 4) {
     if (j < NF)
-      f.a[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(L + buf + ad.a_rd[kk] + j * 8192));
+      f.a[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(L + abuf + ad.a_rd[kk] + j * 8192));
   } else {
     const int n = j - 4;
     f.b[n] = as_bf16x8(
-        *reinterpret_cast<const u32x4*>(L + buf + ad.b_rd[kk][n & 1] + bimm<MODE>(n)));
+        *reinterpret_cast<const u32x4*>(L + bbuf + ad.b_rd[kk][n & 1] + bimm<MODE>(n)));
   }
 }
 
@@ -206,72 +206,88 @@ __device__ __forceinline__ void mfma_j(const Frags4& f, int j, f32x16 (&acc)[4][
   if (j / 4 < NF) acc[j / 4][j % 4] = mfma32x32x16(f.a[j / 4], f.b[j % 4], acc[j / 4][j % 4]);
 }
 
-// One 16-byte-per-lane copy of a stage (1 KiB): copy i < 8 is A region
-// wave + 4 i, copy i >= 8 is B region wave + 4 (i - 8), into the stage at
-// LDS byte offset buf.  Buffer loads straight into LDS: the lane's 16 bytes
-// land at M0 + 16 lane, so M0 is the region's (wave-uniform) start.
+// LDS of the four-wave tiles (160 KiB, all of it): two A buffers (token or
+// h rows, 32 KiB each) and three B buffers (weight rows), so that the weight
+// copies, which miss the caches most, can be issued two stages ahead.
+constexpr int kLds4 = 5 * kTileBytes;
+constexpr int kABuf0 = 0, kBBuf0 = 2 * kTileBytes;
+
+// One 16-byte-per-lane copy straight into LDS (1 KiB per wave): region
+// wave + 4 i of the A tile (A = true) or of the B tile, stage k, into the
+// buffer at LDS byte offset buf.  Buffer loads with the LDS flag: the lane's
+// 16 bytes land at M0 + 16 lane, M0 = the region's (wave-uniform) start.
+template <bool A>
 __device__ __forceinline__ void copy_i(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                        unsigned char* L, uint32_t buf, int k, int i,
                                        const Addr4& ad, int wave) {
-  if (i < 8) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        ra, (__attribute__((address_space(3))) void*)(L + buf + (wave + 4 * i) * 1024), 16,
-        ad.a_vo[i], 2 * k, 0, 0);
-  } else {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rb, (__attribute__((address_space(3))) void*)(L + buf + kTileBytes + (wave + 4 * (i - 8)) * 1024),
-        16, ad.b_vo[i & 1], ad.b_so[i - 8] + 2 * k, 0, 0);
-  }
+  __attribute__((address_space(3))) void* dst =
+      (__attribute__((address_space(3))) void*)(L + buf + (wave + 4 * i) * 1024);
+  if (A)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, ad.a_vo[i], 2 * k, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, ad.b_vo[i & 1], ad.b_so[i] + 2 * k, 0,
+                                             0);
 }
 
-// Stages are filled by copies straight into LDS, double buffered.  A buffer
-// is free once every wave has passed the barrier that ends the reads of the
-// stage it held (inside the stage's last k16 step): stage t + 2's weight (B)
-// copies go out right then, between the step's remaining products, and its
-// A copies in the next stage's first step; all must have landed by the next
-// barrier, about one stage later (the most two 64 KiB buffers allow).
+// Stage t reads A buffer t % 2 and B buffer t % 3.  The weight copies of
+// stage t + 2 go out in stage t's first k16 step (their buffer held stage
+// t - 1, done at stage t - 1's barrier), the token-row copies of stage t + 2
+// right after stage t's barrier (their buffer held stage t); both must have
+// landed by stage t + 1's barrier: weights about 1.75 stages after issue,
+// token rows (mostly cache hits) about one.  Every copy is a direct LDS
+// load, so the copies complete in issue order and "stage t + 1 has landed"
+// at stage t's barrier is vmcnt(8): only stage t + 2's 8 weight copies per
+// wave were issued after them.  (A load into registers may complete before
+// an earlier copy into LDS, so the two kinds are never mixed here.)
 template <int NF, int MODE>
 __device__ __forceinline__ void mainloop4(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                           int nk, unsigned char* L, const Addr4& ad,
                                           f32x16 (&acc)[4][4]) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   Frags4 f0, f1;
+  const int k1 = min(1, nk - 1) * BK;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) copy_i(ra, rb, L, 0, 0, (i + 8) % 16, ad, wave);
+  for (int i = 0; i < 8; ++i) copy_i<true>(ra, rb, L, kABuf0, 0, i, ad, wave);
 #pragma unroll
-  for (int i = 8; i < 16; ++i) copy_i(ra, rb, L, kBuf, min(1, nk - 1) * BK, i, ad, wave);
-  // stage 0 landed: all but stage 1's 8 B copies (vmcnt(8))
-  __builtin_amdgcn_s_waitcnt(0x0F78);
+  for (int i = 0; i < 8; ++i) copy_i<false>(ra, rb, L, kBBuf0, 0, i, ad, wave);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) copy_i<false>(ra, rb, L, kBBuf0 + kTileBytes, k1, i, ad, wave);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) copy_i<true>(ra, rb, L, kABuf0 + kTileBytes, k1, i, ad, wave);
+  // stage 0 landed: all but stage 1's 16 copies (vmcnt(16))
+  __builtin_amdgcn_s_waitcnt(0x4070);
   wait_lds_barrier();
 #pragma unroll
-  for (int j = 0; j < 8; ++j) read_frag<NF, MODE>(f0, j, L, 0, 0, ad);
+  for (int j = 0; j < 8; ++j) read_frag<NF, MODE>(f0, j, L, kABuf0, kBBuf0, 0, ad);
+  int b3 = 0;  // t % 3
   for (int t = 0; t < nk; ++t) {
-    const uint32_t cur = (t & 1) * kBuf, nb = kBuf - cur;
-    // stage t + 1's A copies go to nb in step 0 (its B copies went out at the
-    // end of the previous stage), stage t + 2's B copies to cur once this
-    // stage's reads are done; beyond the last stage the copies repeat it (in
-    // bounds, never read)
-    const int k1 = min(t + 1, nk - 1) * BK, k2 = min(t + 2, nk - 1) * BK;
+    const uint32_t ca = (t & 1) * kTileBytes, na = kTileBytes - ca;
+    const uint32_t cb = kBBuf0 + b3 * kTileBytes;
+    const int b3n = (b3 == 2) ? 0 : b3 + 1;
+    const uint32_t nbb = kBBuf0 + b3n * kTileBytes;            // stage t + 1
+    const uint32_t b2 = kBBuf0 + (b3n == 2 ? 0 : b3n + 1) * kTileBytes;  // stage t + 2
+    // beyond the last stage the copies repeat it (in bounds, never read)
+    const int k2 = min(t + 2, nk - 1) * BK;
     wait_lds();
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       mfma_j<NF>(f0, j, acc);
-      if (j < 8) read_frag<NF, MODE>(f1, j, L, cur, 1, ad);
-      else copy_i(ra, rb, L, nb, k1, j - 8, ad, wave);
+      if (j < 8) read_frag<NF, MODE>(f1, j, L, ca, cb, 1, ad);
+      else copy_i<false>(ra, rb, L, b2, k2, j - 8, ad, wave);
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_lds();
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       mfma_j<NF>(f1, j, acc);
-      if (j < 8) read_frag<NF, MODE>(f0, j, L, cur, 2, ad);
+      if (j < 8) read_frag<NF, MODE>(f0, j, L, ca, cb, 2, ad);
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_lds();
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       mfma_j<NF>(f0, j, acc);
-      if (j < 8) read_frag<NF, MODE>(f1, j, L, cur, 3, ad);
+      if (j < 8) read_frag<NF, MODE>(f1, j, L, ca, cb, 3, ad);
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_lds();
@@ -280,22 +296,23 @@ __device__ __forceinline__ void mainloop4(__amdgpu_buffer_rsrc_t ra, __amdgpu_bu
       mfma_j<NF>(f1, j, acc);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // this wave's reads of cur are done and its copies of stage t + 1 have
-    // landed; then every wave's have
-    wait_all();
+    // this wave's copies of stage t + 1 have landed and its reads of stage
+    // t are done (vmcnt(8) lgkmcnt(0)); then every wave's are
+    __builtin_amdgcn_s_waitcnt(0x0078);
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int j = 8; j < 16; ++j) {
       mfma_j<NF>(f1, j, acc);
       if (j < 12) {
-        read_frag<NF, MODE>(f0, 2 * (j - 8), L, nb, 0, ad);
-        read_frag<NF, MODE>(f0, 2 * (j - 8) + 1, L, nb, 0, ad);
+        read_frag<NF, MODE>(f0, 2 * (j - 8), L, na, nbb, 0, ad);
+        read_frag<NF, MODE>(f0, 2 * (j - 8) + 1, L, na, nbb, 0, ad);
       } else {
-        copy_i(ra, rb, L, cur, k2, 8 + 2 * (j - 12), ad, wave);
-        copy_i(ra, rb, L, cur, k2, 9 + 2 * (j - 12), ad, wave);
+        copy_i<true>(ra, rb, L, ca, k2, 2 * (j - 12), ad, wave);
+        copy_i<true>(ra, rb, L, ca, k2, 2 * (j - 12) + 1, ad, wave);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    b3 = b3n;
   }
   wait_all();
 }
@@ -308,7 +325,7 @@ __global__ __launch_bounds__(kThreads4) void grouped_gemm_bf16_w4(
     const int32_t* __restrict__ slot_token, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off,
     const int32_t* __restrict__ meta, int T, int E, int H, int I, int n_nt) {
-  __shared__ __attribute__((aligned(16))) TileLds lds;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLds4];
   Coords tc;
   if (!tile_coords(counts, offsets, tile_off, meta, E, n_nt, tc)) return;
   const int e = tc.e, nt = tc.nt, row0 = tc.row0, row_end = tc.row_end;
@@ -348,7 +365,6 @@ __global__ __launch_bounds__(kThreads4) void grouped_gemm_bf16_w4(
     const int c = (lane % 8) ^ (((lane / 8) ^ (wave + 4 * p)) & 7);
     ad.b_vo[p] = (static_cast<uint32_t>(lane / 8) * K + c * 8) * 2;
   }
-  ad.st = wave * 1024 + 16 * lane;
   const int key_a = ((lane & 7) ^ ((4 * wm + l32 / 8) & 7)) & 7;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -357,7 +373,7 @@ __global__ __launch_bounds__(kThreads4) void grouped_gemm_bf16_w4(
     for (int p = 0; p < 2; ++p) {
       const int key_b = ((lane & 7) ^ ((4 * p + l32 / 8) & 7)) & 7;
       const int rowb = ((MODE == kGateUp) ? wn * 64 : wn * 128) + p * 32 + l32;
-      ad.b_rd[kk][p] = kTileBytes + rowb * kRowBytes + ((((2 * kk + hi) ^ key_b) & 7) << 4);
+      ad.b_rd[kk][p] = rowb * kRowBytes + ((((2 * kk + hi) ^ key_b) & 7) << 4);
     }
   }
   f32x16 acc[4][4];
@@ -369,7 +385,7 @@ __global__ __launch_bounds__(kThreads4) void grouped_gemm_bf16_w4(
   const int g = (m_valid + 31) / 32;
   const int nf = min(4, max(0, (g - wm + 1) / 2));
   const int nk = K / BK;
-  unsigned char* L = &lds[0][0];
+  unsigned char* L = lds;
   switch (nf) {
     case 4: mainloop4<4, MODE>(ra, rb, nk, L, ad, acc); break;
     case 3: mainloop4<3, MODE>(ra, rb, nk, L, ad, acc); break;
@@ -386,7 +402,7 @@ __global__ __launch_bounds__(kThreads4) void grouped_gemm_bf16_w4(
   // LDS row pitch (bytes): gate/up rows padded by 16 bytes; the down
   // product's 4 x 128 rows of 256 bytes fill the stage buffers exactly
   constexpr int kPitch = (MODE == kGateUp) ? 2 * kCols + 16 : 2 * kCols;
-  static_assert(4 * 128 * kPitch <= static_cast<int>(sizeof(TileLds)), "epilogue tile fits");
+  static_assert(4 * 128 * kPitch <= kLds4, "epilogue tile fits");
   unsigned char* R = L + wave * (128 * kPitch);
 #pragma unroll
   for (int f = 0; f < 4; ++f) {

@@ -26,6 +26,8 @@
 // (its column index wraps modulo H), so every product is exact and the sums
 // are fp32.  The reduction is split into ks slices; the router's selection
 // kernel adds the ks partial logits in a fixed order.
+#include <utility>
+
 #include "grouped_tile.h"
 
 namespace beam {
@@ -229,16 +231,73 @@ __device__ __forceinline__ void copy_i(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffe
                                              0);
 }
 
-// Stage t reads A buffer t % 2 and B buffer t % 3.  The weight copies of
-// stage t + 2 go out in stage t's first k16 step (their buffer held stage
-// t - 1, done at stage t - 1's barrier), the token-row copies of stage t + 2
-// right after stage t's barrier (their buffer held stage t); both must have
-// landed by stage t + 1's barrier: weights about 1.75 stages after issue,
-// token rows (mostly cache hits) about one.  Every copy is a direct LDS
-// load, so the copies complete in issue order and "stage t + 1 has landed"
-// at stage t's barrier is vmcnt(8): only stage t + 2's 8 weight copies per
-// wave were issued after them.  (A load into registers may complete before
-// an earlier copy into LDS, so the two kinds are never mixed here.)
+// Stage t reads A buffer t % 2 and B buffer t % 3.  Its 64 products are
+// slots 0..63 (k16 step s / 16), the barrier between slots 55 and 56.  A
+// compute unit's texture path takes about 64 bytes a cycle, so the copies
+// (64 KiB per stage per workgroup) are spread over the stage rather than
+// issued in bursts (four waves issuing together in a window of a few
+// products stall at issue):
+// - token rows of stage t + 1, into A buffer (t + 1) % 2 (free since stage
+//   t - 1's barrier): regions 0, 1 at slots 58, 62 of stage t - 1, regions
+//   2..7 at slots 1, 4, .., 16 of stage t;
+// - weights of stage t + 2, into B buffer (t + 2) % 3 (free since stage
+//   t - 1's barrier): regions 0..7 at slots 20, 24, .., 48.
+// Both must have landed by stage t + 1's barrier.  Every copy is a direct
+// LDS load, so the copies complete in issue order and "stage t + 1 has
+// landed" at stage t's barrier is vmcnt(8): only stage t + 2's 8 weight
+// copies per wave were issued after the last of them.  (A load into
+// registers may complete before an earlier copy into LDS, so the two kinds
+// are never mixed here.)  Fragment reads: those of k16 step k + 1 in the
+// first 8 slots of step k, those of the next stage's step 0 two per slot
+// after the barrier.
+// LDS offsets and k columns of one stage's slots
+struct Stage4 {
+  uint32_t ca, na;       // A buffers of stages t and t + 1
+  uint32_t cb, nbb, b2;  // B buffers of stages t, t + 1 and t + 2
+  int kn1, kn2;          // k columns of stages t + 1 and t + 2
+};
+
+// Slot S (a compile-time constant) of a stage: its product and the memory
+// operations issued beside it.
+template <int NF, int MODE, int S>
+__device__ __forceinline__ void slot4(Frags4& f0, Frags4& f1, f32x16 (&acc)[4][4],
+                                      __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                      unsigned char* L, const Addr4& ad, int wave,
+                                      const Stage4& g) {
+  constexpr int step = S / 16, j = S % 16;
+  if constexpr (j == 0) wait_lds();
+  if constexpr (S == 56) {
+    // this wave's copies of stage t + 1 have landed and its reads of stage t
+    // are done (vmcnt(8) lgkmcnt(0)); then every wave's are
+    __builtin_amdgcn_s_waitcnt(0x0078);
+    __builtin_amdgcn_s_barrier();
+  }
+  if constexpr (step % 2 == 0) mfma_j<NF>(f0, j, acc);
+  else mfma_j<NF>(f1, j, acc);
+  if constexpr (step < 3 && j < 8) {
+    if constexpr (step % 2 == 0) read_frag<NF, MODE>(f1, j, L, g.ca, g.cb, step + 1, ad);
+    else read_frag<NF, MODE>(f0, j, L, g.ca, g.cb, step + 1, ad);
+  }
+  if constexpr (S >= 56 && S < 60) {
+    read_frag<NF, MODE>(f0, 2 * (S - 56), L, g.na, g.nbb, 0, ad);
+    read_frag<NF, MODE>(f0, 2 * (S - 56) + 1, L, g.na, g.nbb, 0, ad);
+  }
+  if constexpr (S >= 1 && S <= 16 && (S - 1) % 3 == 0)
+    copy_i<true>(ra, rb, L, g.na, g.kn1, 2 + (S - 1) / 3, ad, wave);
+  if constexpr (S >= 20 && S <= 48 && S % 4 == 0)
+    copy_i<false>(ra, rb, L, g.b2, g.kn2, (S - 20) / 4, ad, wave);
+  if constexpr (S == 58 || S == 62) copy_i<true>(ra, rb, L, g.ca, g.kn2, (S - 58) / 4, ad, wave);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int NF, int MODE, int... S>
+__device__ __forceinline__ void stage4(std::integer_sequence<int, S...>, Frags4& f0, Frags4& f1,
+                                       f32x16 (&acc)[4][4], __amdgpu_buffer_rsrc_t ra,
+                                       __amdgpu_buffer_rsrc_t rb, unsigned char* L,
+                                       const Addr4& ad, int wave, const Stage4& g) {
+  (slot4<NF, MODE, S>(f0, f1, acc, ra, rb, L, ad, wave, g), ...);
+}
+
 template <int NF, int MODE>
 __device__ __forceinline__ void mainloop4(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                           int nk, unsigned char* L, const Addr4& ad,
@@ -252,66 +311,26 @@ __device__ __forceinline__ void mainloop4(__amdgpu_buffer_rsrc_t ra, __amdgpu_bu
   for (int i = 0; i < 8; ++i) copy_i<false>(ra, rb, L, kBBuf0, 0, i, ad, wave);
 #pragma unroll
   for (int i = 0; i < 8; ++i) copy_i<false>(ra, rb, L, kBBuf0 + kTileBytes, k1, i, ad, wave);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) copy_i<true>(ra, rb, L, kABuf0 + kTileBytes, k1, i, ad, wave);
-  // stage 0 landed: all but stage 1's 16 copies (vmcnt(16))
-  __builtin_amdgcn_s_waitcnt(0x4070);
+  copy_i<true>(ra, rb, L, kABuf0 + kTileBytes, k1, 0, ad, wave);
+  copy_i<true>(ra, rb, L, kABuf0 + kTileBytes, k1, 1, ad, wave);
+  // stage 0 landed: all but stage 1's 10 copies so far (vmcnt(10))
+  __builtin_amdgcn_s_waitcnt(0x007A);
   wait_lds_barrier();
 #pragma unroll
   for (int j = 0; j < 8; ++j) read_frag<NF, MODE>(f0, j, L, kABuf0, kBBuf0, 0, ad);
   int b3 = 0;  // t % 3
   for (int t = 0; t < nk; ++t) {
-    const uint32_t ca = (t & 1) * kTileBytes, na = kTileBytes - ca;
-    const uint32_t cb = kBBuf0 + b3 * kTileBytes;
+    Stage4 g;
+    g.ca = (t & 1) * kTileBytes;
+    g.na = kTileBytes - g.ca;
+    g.cb = kBBuf0 + b3 * kTileBytes;
     const int b3n = (b3 == 2) ? 0 : b3 + 1;
-    const uint32_t nbb = kBBuf0 + b3n * kTileBytes;            // stage t + 1
-    const uint32_t b2 = kBBuf0 + (b3n == 2 ? 0 : b3n + 1) * kTileBytes;  // stage t + 2
+    g.nbb = kBBuf0 + b3n * kTileBytes;
+    g.b2 = kBBuf0 + (b3n == 2 ? 0 : b3n + 1) * kTileBytes;
     // beyond the last stage the copies repeat it (in bounds, never read)
-    const int k2 = min(t + 2, nk - 1) * BK;
-    wait_lds();
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      mfma_j<NF>(f0, j, acc);
-      if (j < 8) read_frag<NF, MODE>(f1, j, L, ca, cb, 1, ad);
-      else copy_i<false>(ra, rb, L, b2, k2, j - 8, ad, wave);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    wait_lds();
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      mfma_j<NF>(f1, j, acc);
-      if (j < 8) read_frag<NF, MODE>(f0, j, L, ca, cb, 2, ad);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    wait_lds();
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      mfma_j<NF>(f0, j, acc);
-      if (j < 8) read_frag<NF, MODE>(f1, j, L, ca, cb, 3, ad);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    wait_lds();
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      mfma_j<NF>(f1, j, acc);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // this wave's copies of stage t + 1 have landed and its reads of stage
-    // t are done (vmcnt(8) lgkmcnt(0)); then every wave's are
-    __builtin_amdgcn_s_waitcnt(0x0078);
-    __builtin_amdgcn_s_barrier();
-#pragma unroll
-    for (int j = 8; j < 16; ++j) {
-      mfma_j<NF>(f1, j, acc);
-      if (j < 12) {
-        read_frag<NF, MODE>(f0, 2 * (j - 8), L, na, nbb, 0, ad);
-        read_frag<NF, MODE>(f0, 2 * (j - 8) + 1, L, na, nbb, 0, ad);
-      } else {
-        copy_i<true>(ra, rb, L, ca, k2, 2 * (j - 12), ad, wave);
-        copy_i<true>(ra, rb, L, ca, k2, 2 * (j - 12) + 1, ad, wave);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    g.kn1 = min(t + 1, nk - 1) * BK;
+    g.kn2 = min(t + 2, nk - 1) * BK;
+    stage4<NF, MODE>(std::make_integer_sequence<int, 64>{}, f0, f1, acc, ra, rb, L, ad, wave, g);
     b3 = b3n;
   }
   wait_all();

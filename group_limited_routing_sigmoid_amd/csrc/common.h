@@ -95,8 +95,12 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
       __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), lo, true));
 }
 
+// silu(g) = g * sigmoid(g), the sigmoid from the hardware exponential and
+// reciprocal (each within about 1 ulp of binary32).  The bf16 paths round
+// silu(g) * u to 8 bits next, so an IEEE divide (about ten instructions more
+// per output, most of a 256-row tile's epilogue) buys nothing there.
 __device__ __forceinline__ float silu(float g) {
-  return g / (1.0f + __expf(-g));
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
 __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) {

@@ -258,8 +258,10 @@ struct Stage4 {
 };
 
 // Slot S (a compile-time constant) of a stage: its product and the memory
-// operations issued beside it.
-template <int NF, int MODE, int S>
+// operations issued beside it.  TAIL: 0 for stages t < nk - 2; 1 for stage
+// nk - 2 and 2 for stage nk - 1, which issue no copies past the last stage
+// (so their barriers wait for every copy).
+template <int NF, int MODE, int TAIL, int S>
 __device__ __forceinline__ void slot4(Frags4& f0, Frags4& f1, f32x16 (&acc)[4][4],
                                       __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                       unsigned char* L, const Addr4& ad, int wave,
@@ -268,8 +270,9 @@ __device__ __forceinline__ void slot4(Frags4& f0, Frags4& f1, f32x16 (&acc)[4][4
   if constexpr (j == 0) wait_lds();
   if constexpr (S == 56) {
     // this wave's copies of stage t + 1 have landed and its reads of stage t
-    // are done (vmcnt(8) lgkmcnt(0)); then every wave's are
-    __builtin_amdgcn_s_waitcnt(0x0078);
+    // are done (vmcnt(8) lgkmcnt(0), or vmcnt(0) in the last two stages);
+    // then every wave's are
+    __builtin_amdgcn_s_waitcnt(TAIL == 0 ? 0x0078 : 0x0070);
     __builtin_amdgcn_s_barrier();
   }
   if constexpr (step % 2 == 0) mfma_j<NF>(f0, j, acc);
@@ -278,24 +281,39 @@ __device__ __forceinline__ void slot4(Frags4& f0, Frags4& f1, f32x16 (&acc)[4][4
     if constexpr (step % 2 == 0) read_frag<NF, MODE>(f1, j, L, g.ca, g.cb, step + 1, ad);
     else read_frag<NF, MODE>(f0, j, L, g.ca, g.cb, step + 1, ad);
   }
-  if constexpr (S >= 56 && S < 60) {
+  if constexpr (S >= 56 && S < 60 && TAIL < 2) {
     read_frag<NF, MODE>(f0, 2 * (S - 56), L, g.na, g.nbb, 0, ad);
     read_frag<NF, MODE>(f0, 2 * (S - 56) + 1, L, g.na, g.nbb, 0, ad);
   }
-  if constexpr (S >= 1 && S <= 16 && (S - 1) % 3 == 0)
+  if constexpr (S >= 1 && S <= 16 && (S - 1) % 3 == 0 && TAIL < 2)
     copy_i<true>(ra, rb, L, g.na, g.kn1, 2 + (S - 1) / 3, ad, wave);
-  if constexpr (S >= 20 && S <= 48 && S % 4 == 0)
+  if constexpr (S >= 20 && S <= 48 && S % 4 == 0 && TAIL == 0)
     copy_i<false>(ra, rb, L, g.b2, g.kn2, (S - 20) / 4, ad, wave);
-  if constexpr (S == 58 || S == 62) copy_i<true>(ra, rb, L, g.ca, g.kn2, (S - 58) / 4, ad, wave);
+  if constexpr ((S == 58 || S == 62) && TAIL == 0)
+    copy_i<true>(ra, rb, L, g.ca, g.kn2, (S - 58) / 4, ad, wave);
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int NF, int MODE, int... S>
+template <int NF, int MODE, int TAIL, int... S>
 __device__ __forceinline__ void stage4(std::integer_sequence<int, S...>, Frags4& f0, Frags4& f1,
                                        f32x16 (&acc)[4][4], __amdgpu_buffer_rsrc_t ra,
                                        __amdgpu_buffer_rsrc_t rb, unsigned char* L,
                                        const Addr4& ad, int wave, const Stage4& g) {
-  (slot4<NF, MODE, S>(f0, f1, acc, ra, rb, L, ad, wave, g), ...);
+  (slot4<NF, MODE, TAIL, S>(f0, f1, acc, ra, rb, L, ad, wave, g), ...);
+}
+
+// LDS buffers and k columns of stage t (b3 = t % 3)
+__device__ __forceinline__ Stage4 stage_at(int t, int b3, int nk) {
+  Stage4 g;
+  g.ca = (t & 1) * kTileBytes;
+  g.na = kTileBytes - g.ca;
+  g.cb = kBBuf0 + b3 * kTileBytes;
+  const int b3n = (b3 == 2) ? 0 : b3 + 1;
+  g.nbb = kBBuf0 + b3n * kTileBytes;
+  g.b2 = kBBuf0 + (b3n == 2 ? 0 : b3n + 1) * kTileBytes;
+  g.kn1 = min(t + 1, nk - 1) * BK;
+  g.kn2 = min(t + 2, nk - 1) * BK;
+  return g;
 }
 
 template <int NF, int MODE>
@@ -318,21 +336,19 @@ __device__ __forceinline__ void mainloop4(__amdgpu_buffer_rsrc_t ra, __amdgpu_bu
   wait_lds_barrier();
 #pragma unroll
   for (int j = 0; j < 8; ++j) read_frag<NF, MODE>(f0, j, L, kABuf0, kBBuf0, 0, ad);
+  constexpr auto kSlots = std::make_integer_sequence<int, 64>{};
   int b3 = 0;  // t % 3
-  for (int t = 0; t < nk; ++t) {
-    Stage4 g;
-    g.ca = (t & 1) * kTileBytes;
-    g.na = kTileBytes - g.ca;
-    g.cb = kBBuf0 + b3 * kTileBytes;
-    const int b3n = (b3 == 2) ? 0 : b3 + 1;
-    g.nbb = kBBuf0 + b3n * kTileBytes;
-    g.b2 = kBBuf0 + (b3n == 2 ? 0 : b3n + 1) * kTileBytes;
-    // beyond the last stage the copies repeat it (in bounds, never read)
-    g.kn1 = min(t + 1, nk - 1) * BK;
-    g.kn2 = min(t + 2, nk - 1) * BK;
-    stage4<NF, MODE>(std::make_integer_sequence<int, 64>{}, f0, f1, acc, ra, rb, L, ad, wave, g);
-    b3 = b3n;
+  int t = 0;
+  for (; t < nk - 2; ++t) {
+    stage4<NF, MODE, 0>(kSlots, f0, f1, acc, ra, rb, L, ad, wave, stage_at(t, b3, nk));
+    b3 = (b3 == 2) ? 0 : b3 + 1;
   }
+  if (t == nk - 2) {
+    stage4<NF, MODE, 1>(kSlots, f0, f1, acc, ra, rb, L, ad, wave, stage_at(t, b3, nk));
+    b3 = (b3 == 2) ? 0 : b3 + 1;
+    ++t;
+  }
+  stage4<NF, MODE, 2>(kSlots, f0, f1, acc, ra, rb, L, ad, wave, stage_at(t, b3, nk));
   wait_all();
 }
 

@@ -17,7 +17,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbeam_moe.so")
+# another build of the same library (e.g. a host-sanitizer build) may be
+# named in BEAM_MOE_LIB; there is no fallback when the file is missing
+LIB_PATH = os.environ.get("BEAM_MOE_LIB") or os.path.join(_HERE, "libbeam_moe.so")
 
 F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
 ROUTE_LOGITS_IN, PATH_STREAM, PATH_GROUPED = 1 << 0, 1 << 1, 1 << 2

@@ -31,9 +31,15 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = ["hipcc", *COMMON]
+def _host(flags):
+    # host-only flags (e.g. sanitizers): each behind -Xarch_host so the GPU
+    # code is compiled exactly as in the regular build
+    return [f for fl in flags for f in ("-Xarch_host", fl)]
+
+
+def _compile(src: str, verbose: bool, build_dir: str, host_flags=()) -> str:
+    obj = os.path.join(build_dir, src + ".o")
+    cmd = ["hipcc", *COMMON, *_host(host_flags)]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     if src in NO_CONTRACT:
@@ -51,18 +57,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, lib: str = None, build_dir: str = None,
+          host_flags=()) -> str:
+    """Compile every source and link the library (default: in-tree).  `lib`,
+    `build_dir` and `host_flags` serve instrumented host builds, e.g. the
+    sanitizer runs of tests/sanitize.py."""
+    lib = lib or LIB
+    build_dir = build_dir or BUILD
+    os.makedirs(build_dir, exist_ok=True)
     jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o",
-           LIB + ".tmp", *objs]
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, host_flags), SOURCES))
+    cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC",
+           *_host(host_flags), "-o", lib + ".tmp", *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -108,7 +108,9 @@ const char* beam_status_string(int status);
  * Supported: 1 <= E <= 1024, E % G == 0, E/G <= 64, 1 <= TG <= G,
  * 1 <= K <= min(16, TG*E/G), group_score_topn in {1,2} and <= E/G,
  * H % 128 == 0 and I % 128 == 0, routed_scale finite and > 0, T >= 0,
- * T*K*max(H, I) < 2^31 (52,428 tokens for the Beam layer).   Returns BEAM_OK or the first error found. */
+ * T*K*max(H, I) < 2^31 (52,428 tokens for the Beam layer), 2*I*H < 2^31
+ * (one expert's gate/up matrix is addressed with 32-bit offsets).  Returns
+ * BEAM_OK or the first error found. */
 int beam_moe_validate(const beam_moe_desc* desc, int64_t T);
 
 /* Bytes of workspace beam_moe_forward / beam_moe_route need for T tokens.
@@ -116,7 +118,14 @@ int beam_moe_validate(const beam_moe_desc* desc, int64_t T);
 int beam_moe_workspace_bytes(const beam_moe_desc* desc, int64_t T,
                              size_t* bytes);
 
-/* Router only (the steps before the experts).
+/* Router only (the steps before the experts): logits x W_r^T, sigmoid
+ * scores, the selection bias, group scores, the kept groups, the top K and
+ * the normalised, scaled weights.  "Hugging Face releases Beam ..." (MoE
+ * paragraph: 8 groups of 32 experts, best 4 groups, top 8); "Reflection
+ * Releases Beam ...", section "Where Beam Saves and Where the Memory Bill
+ * Comes In" (DeepSeek-V3 group-limited sigmoid router, weights normalised
+ * and scaled by 2.5); "Reflection AI Introduces Beam ..." (load-balancing
+ * paragraph: the bias steers selection only).
  *   x         device [T, H] act_dtype; unused with BEAM_ROUTE_LOGITS_IN
  *   w_router  device [E, H] fp32; unused with BEAM_ROUTE_LOGITS_IN
  *   bias      device [E] fp32 selection bias, or NULL for zero
@@ -133,7 +142,12 @@ int beam_moe_route(const beam_moe_desc* desc, int64_t T, const void* x,
                    size_t ws_bytes, void* stream);
 
 /* Token permutation for a given routing (the dispatch between router and
- * experts): a stable counting sort of the T*K assignments by expert.
+ * experts): a stable counting sort of the T*K assignments by expert.  The
+ * pages route each token to 8 of 256 experts ("Hugging Face releases Beam
+ * ...", MoE paragraph) and leave the dispatch to the implementation ("Beam
+ * Turns Frontier-Scale Openness Into an Infrastructure Decision", section
+ * "Sparse compute still requires dense planning": each token's rows have to
+ * reach the experts it selected, which this grouping by expert provides).
  *   topk_idx    device [T, K] int32, each row K distinct ids in [0, E)
  *   counts      device [E] int32: assignments per expert
  *   offsets     device [E+1] int32: exclusive prefix sum of counts
@@ -170,7 +184,13 @@ int beam_moe_quant_e4m3(int64_t rows, int64_t cols, int32_t dtype,
 int beam_moe_quant_mxfp8(int64_t rows, int64_t cols, int32_t dtype,
                          const void* v, uint8_t* q, uint8_t* scales, void* stream);
 
-/* The whole block.
+/* The whole block: router, K SwiGLU experts per token and the weighted
+ * combine ("Hugging Face releases Beam ...", MoE paragraph: SwiGLU
+ * intermediate 2,560 on hidden 5,120; "Reflection Releases Beam ...",
+ * section "Where Beam Saves and Where the Memory Bill Comes In": no shared
+ * expert; "Reflection Beam", section "Where to run it", and the checkpoint
+ * paragraph of "Hugging Face releases Beam ...": the FP8 and 4-bit
+ * checkpoint forms).
  *   x          device [T, H] act_dtype
  *   w_router   device [E, H] fp32 (unused with BEAM_ROUTE_LOGITS_IN)
  *   bias       device [E] fp32 or NULL

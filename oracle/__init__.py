@@ -89,6 +89,9 @@ def shape_of(s) -> Shape:
 
 def lib():
     global _lib
+    if _lib is None and os.environ.get("BEAM_ORACLE_LIB"):
+        # another build of the oracle's source (the host-sanitizer runs)
+        _lib = _bind(ctypes.CDLL(os.environ["BEAM_ORACLE_LIB"]))
     if _lib is None:
         if not os.path.exists(_build.LIB) or (
                 os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC)):

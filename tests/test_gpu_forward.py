@@ -98,7 +98,8 @@ def test_odd_widths_skewed(path):
            f"H=I=384 skew path={path}")
 
 
-@pytest.mark.parametrize("path", [0, gl.PATH_GROUPED])
+# default choice (the grouped path at 64 tokens) and the streaming path forced
+@pytest.mark.parametrize("path", [0, gl.PATH_STREAM])
 def test_beam_decode64(path):
     w = WORKLOADS["decode64"]
     inp = inputs("decode64")

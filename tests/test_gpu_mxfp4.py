@@ -2,8 +2,13 @@
 
 The activation quantiser is bit-exact against the oracle's MX codec.  Layer
 outputs: against the binary64 oracle on the same (exactly dequantised) MXFP4
-weights with unquantised activations, max rel err <= 6e-2 (the 8-bit
-activations set the error, as on the FP8 path); against the oracle that also
+weights with unquantised activations the error is set by the 8-bit
+activations; tests/golden/mx_recipe_study.json measures that cost with the
+oracle alone (the MXFP8 emulation against the weight-only oracle over 48
+layers, 4 shapes x 4 batch sizes from one token x 3 seeds: mean 4.7e-2, max
+6.0e-2), so MX_TOL is the study's maximum plus EMU_TOL, the allowance for the
+GPU's distance from the emulation (max|gpu - ref| <= max|gpu - emu| +
+max|emu - ref|), rounded up to 7.5e-2.  Against the oracle that also
 round-trips x and h through MXFP8 (what the kernels compute, h quantised
 from fp32) the remaining difference is h evaluated in fp32 rather than
 binary64: an h value within ~1e-6 of an e4m3 rounding midpoint may land on
@@ -11,6 +16,10 @@ the other side, moving that element by one e4m3 step (<= 2^-3 of it), about
 2^-3 / sqrt(I/2) of the output per flip (0.8% at I = 256, 0.25% at I =
 2560).  The bar for this comparison is 1e-2: a few flips pass, while a wrong
 operand layout or block scale gives errors of order one."""
+import json
+import math
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -22,8 +31,10 @@ from gpu_util import desc_for, device, inputs, max_rel_err, oracle_forward
 
 pytestmark = pytest.mark.gpu
 
-MX_TOL = 6e-2
 EMU_TOL = 1e-2
+with open(os.path.join(os.path.dirname(__file__), "golden", "mx_recipe_study.json")) as _f:
+    _STUDY_MAX = json.load(_f)["max"]
+MX_TOL = math.ceil((_STUDY_MAX + EMU_TOL) * 40) / 40     # 7.5e-2 for max 6.0e-2
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])

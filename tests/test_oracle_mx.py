@@ -147,3 +147,23 @@ def test_forward_mxfp4_activation_recipe_single_expert():
     h = g / (1 + np.exp(-g)) * u
     ref = mx8(h) @ Wd.T
     np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_mx_recipe_study_reproduces():
+    # The stored study behind the 4-bit GPU bar (tests/golden/mx_recipe_study.py,
+    # oracle only): re-run two of its layers, a single token and a 33-token
+    # batch, and check the stored figures and summary.
+    import sys
+    sys.path.insert(0, os.path.join(os.path.dirname(__file__), "golden"))
+    import mx_recipe_study as st
+    with open(os.path.join(os.path.dirname(__file__), "golden",
+                           "mx_recipe_study.json")) as f:
+        data = json.load(f)
+    assert data["n"] == len(data["cases"]) >= 20
+    assert any(c["T"] == 1 for c in data["cases"])
+    errs = [c["layer_err"] for c in data["cases"]]
+    assert data["max"] == max(errs)
+    for c in (data["cases"][0], data["cases"][11]):
+        whole, rows = st.study_one(c["H"], c["I"], c["E"], c["T"], c["seed"])
+        assert whole == pytest.approx(c["layer_err"], rel=1e-12)
+        assert rows == pytest.approx(c["worst_row_err"], rel=1e-12)

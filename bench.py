@@ -52,6 +52,10 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain 4 GiB device copy instead (the known-size "
                          "kernel that scales HBM byte counters)")
+    ap.add_argument("--dense-ref", action="store_true",
+                    help="time the library GEMM (torch.matmul, hipBLASLt) on dense "
+                         "bf16 products of the expert shapes instead: the reference "
+                         "the grouped GEMMs are compared with")
     return ap.parse_args()
 
 
@@ -142,6 +146,38 @@ def calibrate_copy(steps):
     print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n,
                       "ms": ms, "GBps_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}),
           flush=True)
+
+
+def dense_reference(steps, warmup):
+    """torch.matmul (hipBLASLt on ROCm) on dense bf16 products with the Beam
+    expert shapes: 16,384 rows (the 16K-token prefill's rows if one expert
+    held them all) times the gate/up matrix [2I, H] and the down matrix
+    [H, I], and about the hot experts' rows in the skewed 16K layer (10,680 to 10,928: 10,880).
+    Reports TFLOP/s per shape."""
+    import torch
+    H, I = 5120, 2560
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    out = []
+    for name, M, N, K in (("gate_up", 16384, 2 * I, H), ("down", 16384, H, I),
+                          ("gate_up_hot_expert", 10880, 2 * I, H)):
+        a = torch.randn(M, K, generator=g, device="cuda:0").to(torch.bfloat16)
+        w = torch.randn(N, K, generator=g, device="cuda:0").to(torch.bfloat16)
+        wt = w.t()                      # nn.Linear layout: x @ W^T
+        for _ in range(warmup):
+            torch.matmul(a, wt)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            torch.matmul(a, wt)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        out.append({"shape": name, "M": M, "N": N, "K": K, "ms": ms, "TFLOPs": tf,
+                    "frac_bf16_peak": tf / BF16_PEAK_TFLOPS})
+        del a, w, wt
+    print(json.dumps({"dense_reference": "torch.matmul bf16", "results": out}), flush=True)
 
 
 def read_sclk():
@@ -267,6 +303,9 @@ def main():
         sys.exit(2)
     if a.calibrate_copy:
         calibrate_copy(max(a.steps, 1))
+        return
+    if a.dense_ref:
+        dense_reference(max(a.steps, 1), a.warmup)
         return
     res = run_workload(a, a.workload, a.tokens)
     if (a.prefill_workload != "none" and a.workload == "decode64" and a.tokens is None):

@@ -98,9 +98,10 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
   const int64_t S = p->S, E = p->E, H = p->H, I = p->I;
   // Grouped tiles of 128 (or, bf16, 160) rows with a deeper copy ring while
   // the experts hold few rows, 256 rows above; measured on the Beam layer.
-  // bf16, 128 / 160 / 256 rows: 3.93 / 3.94 / 4.46 ms at 2K tokens, 4.20 /
-  // 4.18 / 4.82 at 3K, 5.30 / 4.72 / 5.00 at 4K, 6.27 / 6.06 / 5.42 at 5K;
-  // so 128 below T*K = 96E, 160 below 144E.  MXFP4, 128 / 256 rows: 1.57 /
+  // bf16, 128 / 256 rows (the four-wave 256-row tiles with triple-buffered
+  // weights): 3.77 / 3.82 ms at 2K tokens, 3.88 / 3.93 at 2.5K, 4.16 / 4.02
+  // at 3K, and 256 rows 4.19 ms at 4K against 4.72 for the 160-row ring; so
+  // 128 below T*K = 96E, 256 above (160 rows on request).  MXFP4, 128 / 256 rows: 1.57 /
   // 1.61 ms at 1K tokens, 2.77 / 2.38 at 4K; so 128 below T*K = 32E.  FP8,
   // 128 / 256 (+32) rows: 1.63 / 1.99 ms at 64 tokens, 2.28 / 2.60 at 2K,
   // 2.76 / 2.93 at 3.5K, 3.31 / 3.02 at 4K; so 128 below T*K = 120E.
@@ -110,7 +111,6 @@ int make_plan(const beam_moe_desc* d, int64_t T, Plan* p) {
     else if (p->flags & BEAM_TILE_160) p->bm = 160;
     else if (p->flags & BEAM_TILE_256) p->bm = kGemmBM;
     else if (S < 96 * E) p->bm = 128;
-    else if (S < 144 * E) p->bm = 160;
   } else if (p->wdt == BEAM_MXFP4) {
     // 64-slot tiles with 256-deep stages (H, I multiples of 512) against the
     // rest at default: 1.02 / 1.11 ms at 64 tokens, 1.33 / 1.46 at 1K, 1.44

@@ -70,7 +70,7 @@ typedef enum {
 /* Expert path (default: bf16 streams its weights below T*K = E/2 and uses
  * grouped tiles above; MXFP4 and FP8 use grouped tiles; fp32 has one path).
  * Tile height of the grouped path (default: bf16 128 rows below T*K = 96E,
- * 160 below 144E, 256 above; MXFP4 64 below 56E when H and I are multiples
+ * 256 above, 160 only on request; MXFP4 64 below 56E when H and I are multiples
  * of 512, else 128 below 32E, 256 above; FP8 128 below 120E, 256 above, an
  * expert's last tile holding up to 288).  Every tile
  * height gives bit-identical outputs; the two paths agree within the layer

@@ -380,15 +380,17 @@ __global__ __launch_bounds__(kThreads4) void grouped_gemm_bf16_w4(
       wbase, static_cast<uint32_t>((MODE == kGateUp) ? 2 * I * H : H * I) * 2);
   Addr4 ad;
   // copy regions of this wave: wave + 4 i (i < 8) of A and of B, 8 rows each;
-  // A rows past the tile's last valid row copy that row (their sums are
-  // never stored)
+  // the copies of A rows past the tile's last valid row read past the end of
+  // the buffer (zeros, no memory traffic; their sums are never stored)
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = 8 * (wave + 4 * i) + lane / 8;
     const int c = dma_chunk(r, lane);
     const int slot = min(row0 + r, row_end - 1);
-    ad.a_vo[i] = (((MODE == kGateUp) ? static_cast<uint32_t>(slot_token[slot]) * H
-                                     : static_cast<uint32_t>(slot) * I) + c * 8) * 2;
+    ad.a_vo[i] = (r < m_valid) ? (((MODE == kGateUp) ? static_cast<uint32_t>(slot_token[slot]) * H
+                                                     : static_cast<uint32_t>(slot) * I) +
+                                  c * 8) * 2
+                               : 0x80000000u;
     const int r0 = 8 * (wave + 4 * i);
     const int wrow0 = (MODE == kGateUp) ? ((r0 < 128) ? nt * 128 + r0 : I + nt * 128 + (r0 - 128))
                                         : nt * BN + r0;

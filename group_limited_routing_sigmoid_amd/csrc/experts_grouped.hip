@@ -462,18 +462,25 @@ __global__ __launch_bounds__(kThreads4) void grouped_gemm_bf16_w4(
     }
   }
   wait_lds();
-  // 16-byte pieces: kCols / 8 per row; a lane takes pieces lane, lane + 64, ...
-  constexpr int kPieces = 128 * kCols / 8;
-  const int col0 = (MODE == kGateUp) ? nt * 128 + wn * 64 : nt * BN + wn * 128;
+  // 16-byte pieces, kPc per row: lane l takes piece l % kPc of rows
+  // l / kPc + kRowsPer i, so its column is fixed and every step's LDS read
+  // and store addresses are a constant apart (the loop unrolls fully and the
+  // reads go out ahead of the stores)
+  constexpr int kPc = kCols / 8;
+  constexpr int kRowsPer = kWave / kPc;
+  constexpr int kSteps = 128 / kRowsPer;
+  const int pc = lane % kPc, lr0 = lane / kPc;
+  const int col = ((MODE == kGateUp) ? nt * 128 + wn * 64 : nt * BN + wn * 128) + 8 * pc;
   const int ld = (MODE == kGateUp) ? I : H;
+  const bool col_ok = col < ld;
+  const unsigned char* rd = R + lr0 * kPitch + 16 * pc;
 #pragma unroll
-  for (int q = lane; q < kPieces; q += kWave) {
-    const int lr = q / (kCols / 8), pc = q % (kCols / 8);
-    const int row = row0 + 32 * (2 * (lr / 32) + wm) + lr % 32;
-    const int col = col0 + 8 * pc;
-    if ((lr / 32) >= nf || row >= row_end || col >= ld) continue;
-    st16(out + static_cast<int64_t>(row) * ld + col,
-         *reinterpret_cast<const u32x4*>(R + lr * kPitch + 16 * pc));
+  for (int i = 0; i < kSteps; ++i) {
+    const int f = (kRowsPer * i) / 32;  // the A fragment these rows belong to
+    const int row = row0 + 32 * (2 * f + wm) + lr0 + (kRowsPer * i) % 32;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(rd + kRowsPer * i * kPitch);
+    if (f < nf && row < row_end && col_ok) st16(out + static_cast<int64_t>(row) * ld + col, v);
+    if (i % 8 == 7) __builtin_amdgcn_sched_barrier(0);  // eight reads in flight at most
   }
 }
 

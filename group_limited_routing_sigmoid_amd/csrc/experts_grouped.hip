@@ -323,16 +323,26 @@ __device__ __forceinline__ void mainloop4(__amdgpu_buffer_rsrc_t ra, __amdgpu_bu
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   Frags4 f0, f1;
   const int k1 = min(1, nk - 1) * BK;
+  if constexpr (MODE == kGateUp) {
+    // (the weights of stages 0 and 1 went out before, in the kernel)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) copy_i<true>(ra, rb, L, kABuf0, 0, i, ad, wave);
+    for (int i = 0; i < 8; ++i) copy_i<true>(ra, rb, L, kABuf0, 0, i, ad, wave);
+    copy_i<true>(ra, rb, L, kABuf0 + kTileBytes, k1, 0, ad, wave);
+    copy_i<true>(ra, rb, L, kABuf0 + kTileBytes, k1, 1, ad, wave);
+    // stage 0 landed (stage 1's weights too): all but the last 2 copies
+    __builtin_amdgcn_s_waitcnt(0x0072);  // vmcnt(2) lgkmcnt(0)
+  } else {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) copy_i<false>(ra, rb, L, kBBuf0, 0, i, ad, wave);
+    for (int i = 0; i < 8; ++i) copy_i<true>(ra, rb, L, kABuf0, 0, i, ad, wave);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) copy_i<false>(ra, rb, L, kBBuf0 + kTileBytes, k1, i, ad, wave);
-  copy_i<true>(ra, rb, L, kABuf0 + kTileBytes, k1, 0, ad, wave);
-  copy_i<true>(ra, rb, L, kABuf0 + kTileBytes, k1, 1, ad, wave);
-  // stage 0 landed: all but stage 1's 10 copies so far (vmcnt(10))
-  __builtin_amdgcn_s_waitcnt(0x007A);
+    for (int i = 0; i < 8; ++i) copy_i<false>(ra, rb, L, kBBuf0, 0, i, ad, wave);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) copy_i<false>(ra, rb, L, kBBuf0 + kTileBytes, k1, i, ad, wave);
+    copy_i<true>(ra, rb, L, kABuf0 + kTileBytes, k1, 0, ad, wave);
+    copy_i<true>(ra, rb, L, kABuf0 + kTileBytes, k1, 1, ad, wave);
+    // stage 0 landed: all but stage 1's 10 copies so far
+    __builtin_amdgcn_s_waitcnt(0x007A);  // vmcnt(10) lgkmcnt(0)
+  }
   wait_lds_barrier();
 #pragma unroll
   for (int j = 0; j < 8; ++j) read_frag<NF, MODE>(f0, j, L, kABuf0, kBBuf0, 0, ad);
@@ -379,18 +389,9 @@ __global__ __launch_bounds__(kThreads4) void grouped_gemm_bf16_w4(
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(
       wbase, static_cast<uint32_t>((MODE == kGateUp) ? 2 * I * H : H * I) * 2);
   Addr4 ad;
-  // copy regions of this wave: wave + 4 i (i < 8) of A and of B, 8 rows each;
-  // the copies of A rows past the tile's last valid row read past the end of
-  // the buffer (zeros, no memory traffic; their sums are never stored)
+  // copy regions of this wave: wave + 4 i (i < 8) of A and of B, 8 rows each
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int r = 8 * (wave + 4 * i) + lane / 8;
-    const int c = dma_chunk(r, lane);
-    const int slot = min(row0 + r, row_end - 1);
-    ad.a_vo[i] = (r < m_valid) ? (((MODE == kGateUp) ? static_cast<uint32_t>(slot_token[slot]) * H
-                                                     : static_cast<uint32_t>(slot) * I) +
-                                  c * 8) * 2
-                               : 0x80000000u;
     const int r0 = 8 * (wave + 4 * i);
     const int wrow0 = (MODE == kGateUp) ? ((r0 < 128) ? nt * 128 + r0 : I + nt * 128 + (r0 - 128))
                                         : nt * BN + r0;
@@ -401,6 +402,36 @@ __global__ __launch_bounds__(kThreads4) void grouped_gemm_bf16_w4(
     // rows 8 (wave + 4 i) + lane / 8 with i % 2 = p: key (lane / 8) ^ (wave + 4 p)
     const int c = (lane % 8) ^ (((lane / 8) ^ (wave + 4 * p)) & 7);
     ad.b_vo[p] = (static_cast<uint32_t>(lane / 8) * K + c * 8) * 2;
+  }
+  // Gate/up: the token indices of the wave's A rows are loaded first, all
+  // eight, then the weights of stages 0 and 1 are copied while they are in
+  // flight, then the token rows' addresses are formed (the down product's
+  // rows are its slots; it copies stage 0's rows first, mainloop4).  Copies
+  // of A rows past the tile's last valid row read past the end of the buffer
+  // (zeros, no memory traffic; their sums are never stored).
+  uint32_t src_row[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int slot = min(row0 + 8 * (wave + 4 * i) + lane / 8, row_end - 1);
+    src_row[i] = (MODE == kGateUp) ? static_cast<uint32_t>(slot_token[slot])
+                                   : static_cast<uint32_t>(slot);
+  }
+  const int nk = K / BK;
+  if constexpr (MODE == kGateUp) {
+    const int k1 = min(1, nk - 1) * BK;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) copy_i<false>(ra, rb, lds, kBBuf0, 0, i, ad, wave);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) copy_i<false>(ra, rb, lds, kBBuf0 + kTileBytes, k1, i, ad, wave);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(src_row[i]));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * (wave + 4 * i) + lane / 8;
+    const int c = dma_chunk(r, lane);
+    ad.a_vo[i] = (r < m_valid) ? (src_row[i] * ((MODE == kGateUp) ? H : I) + c * 8) * 2
+                               : 0x80000000u;
   }
   const int key_a = ((lane & 7) ^ ((4 * wm + l32 / 8) & 7)) & 7;
 #pragma unroll
@@ -421,7 +452,6 @@ __global__ __launch_bounds__(kThreads4) void grouped_gemm_bf16_w4(
   // this wave's fragments holding a valid row: 2f + wm < ceil(m_valid / 32)
   const int g = (m_valid + 31) / 32;
   const int nf = min(4, max(0, (g - wm + 1) / 2));
-  const int nk = K / BK;
   unsigned char* L = lds;
   switch (nf) {
     case 4: mainloop4<4, MODE>(ra, rb, nk, L, ad, acc); break;

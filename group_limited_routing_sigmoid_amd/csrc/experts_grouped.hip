@@ -149,6 +149,21 @@ namespace w4 {
 
 constexpr int kThreads4 = 256;
 
+// Two floats to two bf16 (round to nearest even, as f32_to_bf16_bits), x in
+// the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float2 v) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{v.x, v.y}, bf16x2_t));
+}
+// The low (high) halves of a and b, a's in the low half of the result.
+__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) {
+  return (a & 0xFFFFu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xFFFF0000u);
+}
+
 // s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0) / lgkmcnt(0) alone (vmcnt 63 and
 // expcnt 7 mean "no wait") / lgkmcnt(0) then s_barrier, as builtins so the
 // compiler's wait-count tracking knows the counters afterwards (it cannot
@@ -466,51 +481,64 @@ __global__ __launch_bounds__(kThreads4) void grouped_gemm_bf16_w4(
   // stage once all have passed the barrier.
   __builtin_amdgcn_s_barrier();
   constexpr int kCols = (MODE == kGateUp) ? 64 : 128;  // output columns per wave
-  // LDS row pitch (bytes): gate/up rows padded by 16 bytes; the down
-  // product's 4 x 128 rows of 256 bytes fill the stage buffers exactly
-  constexpr int kPitch = (MODE == kGateUp) ? 2 * kCols + 16 : 2 * kCols;
-  static_assert(4 * 128 * kPitch <= kLds4, "epilogue tile fits");
-  unsigned char* R = L + wave * (128 * kPitch);
+  // LDS layout: pairs of rows interleaved, one 32-bit word per (row pair,
+  // column) holding the even row's value in its low half and the odd row's
+  // in its high half (a lane's rows 4q + 0..3 are two such pairs of one
+  // column, so it writes both with one conversion and one 4-byte store);
+  // pair pitch padded by 16 bytes on gate/up, the down product's 4 x 64
+  // pairs of 512 bytes fill the stage buffers exactly
+  constexpr int kPairPitch = (MODE == kGateUp) ? 4 * kCols + 16 : 4 * kCols;
+  static_assert(4 * 64 * kPairPitch <= kLds4, "epilogue tile fits");
+  unsigned char* R = L + wave * (64 * kPairPitch);
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
     if (f >= nf) continue;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int lr = 32 * f + 8 * (r / 4) + 4 * hi + (r % 4);  // row inside the wave's 128
-      if (MODE == kGateUp) {
+    for (int r = 0; r < 16; r += 2) {
+      const int pr = 16 * f + 4 * (r / 4) + 2 * hi + (r % 4) / 2;  // pair inside the wave's 64
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          const float hv = silu(acc[f][n][r]) * acc[f][n + 2][r];
-          *reinterpret_cast<uint16_t*>(R + lr * kPitch + 2 * (n * 32 + l32)) = f32_to_bf16_bits(hv);
+      for (int n = 0; n < ((MODE == kGateUp) ? 2 : 4); ++n) {
+        float2 v;
+        if (MODE == kGateUp) {
+          v.x = silu(acc[f][n][r]) * acc[f][n + 2][r];
+          v.y = silu(acc[f][n][r + 1]) * acc[f][n + 2][r + 1];
+        } else {
+          v.x = acc[f][n][r];
+          v.y = acc[f][n][r + 1];
         }
-      } else {
-#pragma unroll
-        for (int n = 0; n < 4; ++n)
-          *reinterpret_cast<uint16_t*>(R + lr * kPitch + 2 * (n * 32 + l32)) =
-              f32_to_bf16_bits(acc[f][n][r]);
+        *reinterpret_cast<uint32_t*>(R + pr * kPairPitch + 4 * (n * 32 + l32)) = pack_bf16x2(v);
       }
     }
   }
   wait_lds();
-  // 16-byte pieces, kPc per row: lane l takes piece l % kPc of rows
-  // l / kPc + kRowsPer i, so its column is fixed and every step's LDS read
-  // and store addresses are a constant apart (the loop unrolls fully and the
-  // reads go out ahead of the stores)
+  // 16-byte row pieces, kPc per row: lane l takes piece l % kPc of the row
+  // pairs l / kPc + kPairsPer i (two 16-byte reads give the piece of both
+  // rows), so its column is fixed and every step's addresses are a constant
+  // apart (the loop unrolls fully and the reads go out ahead of the stores)
   constexpr int kPc = kCols / 8;
-  constexpr int kRowsPer = kWave / kPc;
-  constexpr int kSteps = 128 / kRowsPer;
-  const int pc = lane % kPc, lr0 = lane / kPc;
+  constexpr int kPairsPer = kWave / kPc;
+  constexpr int kSteps = 64 / kPairsPer;
+  const int pc = lane % kPc, pr0 = lane / kPc;
   const int col = ((MODE == kGateUp) ? nt * 128 + wn * 64 : nt * BN + wn * 128) + 8 * pc;
   const int ld = (MODE == kGateUp) ? I : H;
   const bool col_ok = col < ld;
-  const unsigned char* rd = R + lr0 * kPitch + 16 * pc;
+  const unsigned char* rd = R + pr0 * kPairPitch + 32 * pc;
 #pragma unroll
   for (int i = 0; i < kSteps; ++i) {
-    const int f = (kRowsPer * i) / 32;  // the A fragment these rows belong to
-    const int row = row0 + 32 * (2 * f + wm) + lr0 + (kRowsPer * i) % 32;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(rd + kRowsPer * i * kPitch);
-    if (f < nf && row < row_end && col_ok) st16(out + static_cast<int64_t>(row) * ld + col, v);
-    if (i % 8 == 7) __builtin_amdgcn_sched_barrier(0);  // eight reads in flight at most
+    const int pr = pr0 + kPairsPer * i;
+    const int f = (kPairsPer * i) / 16;  // the A fragment these rows belong to
+    const int row = row0 + 32 * (2 * f + wm) + 2 * (pr % 16);
+    const u32x4 w0 = *reinterpret_cast<const u32x4*>(rd + kPairsPer * i * kPairPitch);
+    const u32x4 w1 = *reinterpret_cast<const u32x4*>(rd + kPairsPer * i * kPairPitch + 16);
+    const u32x4 even = {lo_halves(w0[0], w0[1]), lo_halves(w0[2], w0[3]),
+                        lo_halves(w1[0], w1[1]), lo_halves(w1[2], w1[3])};
+    const u32x4 odd = {hi_halves(w0[0], w0[1]), hi_halves(w0[2], w0[3]),
+                       hi_halves(w1[0], w1[1]), hi_halves(w1[2], w1[3])};
+    if (f < nf && col_ok) {
+      if (row < row_end) st16(out + static_cast<int64_t>(row) * ld + col, even);
+      if (row + 1 < row_end) st16(out + static_cast<int64_t>(row + 1) * ld + col, odd);
+    }
+    if (i % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // eight reads in flight at most
   }
 }
 

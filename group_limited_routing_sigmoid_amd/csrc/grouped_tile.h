@@ -20,8 +20,8 @@ constexpr int kTileBytes = BM * kRowBytes;  // 32 KiB per operand tile
 constexpr int kXcds = 8;
 constexpr int kXcdRun = 32;                 // consecutive logical tiles per XCD per round
 constexpr int kRound = kXcds * kXcdRun;     // logical tiles per round
-constexpr int kBandM = 8;                   // M tiles per band of the logical order
-constexpr int kQuadN = 4;                   // N tiles per quad
+constexpr int kBandM = 4;                   // M tiles per band of the logical order
+constexpr int kQuadN = 8;                   // N tiles per quad
 constexpr int kLoads = kTileBytes / (16 * kThreads);  // DMA regions per wave per operand
 
 // Two stages of (A tile, B tile).
@@ -54,23 +54,28 @@ struct Coords {
 // start roughly in order.  The logical tiles form two sequences: those of
 // hot experts (several M tiles, weights reused) and those of cold experts
 // (one tile, weights streamed once from HBM); inside a sequence the order is
-// expert, then bands of 8 M tiles, then quads of 4 N tiles, the M tile
-// moving fastest inside a quad.  The sequences are cut into chunks of 32
-// tiles, and chunk g = 8 (b / 256) + b % 8 goes to workgroups b of one
+// expert, then bands of band_m M tiles (default 4), then quads of quad_n N
+// tiles (default 8), the M tile moving fastest inside a quad.  The
+// sequences are cut into chunks of 32 tiles, and chunk
+// g = 8 (b / 256) + b % 8 goes to workgroups b of one
 // round of 256 (one tile per compute unit) on one XCD: chunk g is cold when
 // floor((g + 1) C / N) > floor(g C / N) (C cold chunks of N), so cold chunks
 // are spread evenly over the rounds.  Then
 // - the hot chunks of a round are consecutive: the XCDs on them share one
 //   window of one expert's weights and token rows in the last-level cache,
-//   and each XCD's 32 tiles (about 8 M x 4 N) share operand slices in its L2
+//   and each XCD's 32 tiles (about 4 M x 8 N) share operand slices in its L2
 //   (measured on the 16K-token layer: gate/up 8.20 -> 7.53 ms against XCDs
-//   walking separate eighths of an expert-major order);
+//   walking separate eighths of an expert-major order; with the four-wave
+//   bf16 kernels 4 M x 8 N measured about 1% faster than 8 M x 4 N, gate/up
+//   and down, on the 16K-token and expert-parallel layers, while 16 x 2,
+//   2 x 16 and 2 x 10 were slower; the 4-bit path keeps 8 M x 4 N);
 // - the cold chunks stream weights from HBM while the hot ones keep the
 //   matrix cores busy, instead of the chip alternating between the two.
 // Returns false for workgroups past the last tile.
 __device__ __forceinline__ bool tile_coords(const int32_t* counts, const int32_t* offsets,
                                             const int32_t* tt, const int32_t* meta,
-                                            int E, int n_nt, Coords& c, int bm = BM) {
+                                            int E, int n_nt, Coords& c, int bm = BM,
+                                            int band_m = kBandM, int quad_n = kQuadN) {
   const int nm = meta[kMetaTiles], nmh = meta[kMetaHot];
   const int nh = nmh * n_nt, nc = (nm - nmh) * n_nt;  // logical tiles per sequence
   const int chh = (nh + kXcdRun - 1) / kXcdRun, chc = (nc + kXcdRun - 1) / kXcdRun;
@@ -87,14 +92,14 @@ __device__ __forceinline__ bool tile_coords(const int32_t* counts, const int32_t
   const int e = tt[tt_expert(E) + mbase + L / n_nt];
   const int t0 = tt[e] - mbase, nt_e = tt[tt_count(E) + e];
   const int j = L - t0 * n_nt;
-  const int band = j / (kBandM * n_nt);
-  const int gm = min(kBandM, nt_e - band * kBandM);
-  const int jj = j - band * kBandM * n_nt;
-  const int q = jj / (gm * kQuadN);
-  const int rem = jj - q * gm * kQuadN;  // the last quad may be narrower
+  const int band = j / (band_m * n_nt);
+  const int gm = min(band_m, nt_e - band * band_m);
+  const int jj = j - band * band_m * n_nt;
+  const int q = jj / (gm * quad_n);
+  const int rem = jj - q * gm * quad_n;  // the last quad may be narrower
   c.e = e;
-  c.nt = q * kQuadN + rem / gm;
-  c.row0 = offsets[e] + (band * kBandM + rem % gm) * bm;
+  c.nt = q * quad_n + rem / gm;
+  c.row0 = offsets[e] + (band * band_m + rem % gm) * bm;
   c.row_end = offsets[e] + counts[e];
   return true;
 }

@@ -344,7 +344,7 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx(
   __shared__ __attribute__((aligned(16))) unsigned char lds[S * G::kStage + G::kPerBytes];
   constexpr int kPerOff = S * G::kStage;
   Coords tc;
-  if (!tile_coords(counts, offsets, tile_off, meta, E, n_nt, tc, BMS)) return;
+  if (!tile_coords(counts, offsets, tile_off, meta, E, n_nt, tc, BMS, 8, 4)) return;
   const int e = tc.e, nt = tc.nt, row0 = tc.row0, row_end = tc.row_end;
   const int K = (MODE == kGateUp) ? H : I;
   const int nk = K / 128;
@@ -632,7 +632,7 @@ __global__ __launch_bounds__(tile::kThreads) void grouped_gemm_mx_wide(
     int n_nt, int n_slots) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
   Coords tc;
-  if (!tile_coords(counts, offsets, tile_off, meta, E, n_nt, tc, BMS)) return;
+  if (!tile_coords(counts, offsets, tile_off, meta, E, n_nt, tc, BMS, 8, 4)) return;
   const int e = tc.e, nt = tc.nt, row0 = tc.row0, row_end = tc.row_end;
   const int K = (MODE == kGateUp) ? H : I;
   const int nk = K / 256, nper = nk / 2;

@@ -178,7 +178,122 @@ __device__ __forceinline__ void scale_rows_x(f32x16& accx, const float* v, const
   }
 }
 
-// One 128-deep stage for the wave's first NF fragments: rescale the
+// Keeps the compiler from moving instructions, LDS reads included, across
+// this point (a scheduling fence alone lets it hoist every read of the stage
+// to the top, and the registers holding them then spill).
+__device__ __forceinline__ void fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Ties the value to this point of the instruction stream (the matrix
+// products are pure computations the compiler would otherwise move freely).
+__device__ __forceinline__ void pin(f32x16& v) { asm volatile("" : "+v"(v)); }
+
+// acc[i][n] *= t[row of element] for the 16 rows fragment i holds in this
+// lane, t: those rows' factors (four 16-byte reads of the factor table).
+__device__ __forceinline__ void read_factors(f32x4 (&t)[4], int i, const float* v,
+                                             const FragAddr& fa) {
+  const unsigned char* base = reinterpret_cast<const unsigned char*>(v) + fa.r_row;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) t[q] = *reinterpret_cast<const f32x4*>(base + (i * 32 + 8 * q) * 4);
+}
+__device__ __forceinline__ void mul_factors(f32x16& a, const f32x4 (&t)[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[4 * q + j] *= t[q][j];
+}
+
+// One 128-deep stage for the wave's first NF fragments: add the stage's
+// exact products, one 64-deep half at a time (B fragments of the half held,
+// A fragments read one ahead), then rescale the accumulators to the next
+// stage's scale (factors `next`, 1 after the last stage).  The rescale of
+// fragment i goes between the products of fragment i+1 (one multiply
+// group beside each product), so the multiplies overlap the matrix-core
+// work instead of holding up the products that need them; each sum still
+// sees the same operations in the same order (products of stage kb, then
+// the factor of kb+1, then products of kb+1).
+// XT: the tile also holds extension rows (tile rows 256..287, their own
+// 4 KiB tile xt); wave (wm, wn) adds their products with its B fragment wm,
+// i.e. columns wn*64 + wm*32 .. +32, into accx.
+template <int NF, bool XT, typename Copy>
+__device__ __forceinline__ void fp8_stage(const unsigned char* at, const unsigned char* bt,
+                                          const unsigned char* xt, const float* next,
+                                          f32x16 (&acc)[4][2], f32x16& accx, int wm,
+                                          const FragAddr& fa, Copy&& copy) {
+  {  // first 64-deep half: products, the next stage's copies between them
+    const i32x8 b0 = frag8(bt, fa.b_row, fa, 0, 0);
+    const i32x8 b1 = frag8(bt, fa.b_row, fa, 1, 0);
+    if (XT) {
+      const i32x8 ax = frag8(xt, fa.x_row, fa, 0, 0);
+      accx = mfma_fp8_32x32x64(ax, wm ? b1 : b0, accx);
+      pin(accx);
+    }
+    i32x8 a = frag8(at, fa.a_row, fa, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      i32x8 an = a;
+      if (i + 1 < NF) an = frag8(at, fa.a_row, fa, i + 1, 0);
+      acc[i][0] = mfma_fp8_32x32x64(a, b0, acc[i][0]);
+      pin(acc[i][0]);
+      copy(2 * i);
+      acc[i][1] = mfma_fp8_32x32x64(a, b1, acc[i][1]);
+      pin(acc[i][1]);
+      copy(2 * i + 1);
+      a = an;
+    }
+#pragma unroll
+    for (int c = 2 * NF; c < 9; ++c) copy(c);
+  }
+  fence();
+  {  // second half: products, fragment i-1's rescale beside fragment i's
+    const i32x8 b0 = frag8(bt, fa.b_row, fa, 0, 1);
+    const i32x8 b1 = frag8(bt, fa.b_row, fa, 1, 1);
+    if (XT) {
+      const i32x8 ax = frag8(xt, fa.x_row, fa, 0, 1);
+      accx = mfma_fp8_32x32x64(ax, wm ? b1 : b0, accx);
+      pin(accx);
+    }
+    i32x8 a = frag8(at, fa.a_row, fa, 0, 1);
+    f32x4 t[4];
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      i32x8 an = a;
+      if (i + 1 < NF) an = frag8(at, fa.a_row, fa, i + 1, 1);
+      acc[i][0] = mfma_fp8_32x32x64(a, b0, acc[i][0]);
+      pin(acc[i][0]);
+      if (i > 0) {
+        mul_factors(acc[i - 1][0], t);
+        pin(acc[i - 1][0]);
+      }
+      acc[i][1] = mfma_fp8_32x32x64(a, b1, acc[i][1]);
+      pin(acc[i][1]);
+      if (i > 0) {
+        mul_factors(acc[i - 1][1], t);
+        pin(acc[i - 1][1]);
+      }
+      fence();
+      read_factors(t, i, next, fa);
+      fence();
+      a = an;
+    }
+    if (NF > 0) {
+      mul_factors(acc[NF - 1][0], t);
+      pin(acc[NF - 1][0]);
+      mul_factors(acc[NF - 1][1], t);
+      pin(acc[NF - 1][1]);
+    }
+    if (XT) {
+      fence();
+      scale_rows_x(accx, next, fa);
+      pin(accx);
+    }
+  }
+}
+
+// The 128-row tiles' stage (factors of the stage itself, applied first):
+// for the wave's first NF fragments rescale the
 // accumulators to this stage's scale and add the stage's exact products, one
 // 64-deep half at a time (B fragments of the half held, A fragments read one
 // ahead).  Fragment i is rescaled just before its first product of the
@@ -187,7 +302,7 @@ __device__ __forceinline__ void scale_rows_x(f32x16& accx, const float* v, const
 // 4 KiB tile xt); wave (wm, wn) adds their products with its B fragment wm,
 // i.e. columns wn*64 + wm*32 .. +32, into accx.
 template <int NF, bool XT>
-__device__ __forceinline__ void fp8_stage(const unsigned char* at, const unsigned char* bt,
+__device__ __forceinline__ void fp8_stage_pre(const unsigned char* at, const unsigned char* bt,
                                           const unsigned char* xt, const float* ratio,
                                           f32x16 (&acc)[4][2], f32x16& accx, int wm,
                                           const FragAddr& fa) {
@@ -216,10 +331,11 @@ __device__ __forceinline__ void fp8_stage(const unsigned char* at, const unsigne
 // Main loop over the K/128 stages.  Block scales: the exact product of a
 // 128-deep stage kb is P_kb (unit scales); the result is sum_kb s_kb * P_kb
 // with s_kb = s_a[row, kb] * s_w[block, kb].  The accumulator is kept in units
-// of the current stage's s: before adding P_kb it is multiplied by
-// s_{kb-1} / s_kb, and the epilogue multiplies by the last s.  Each thread
-// computes the factors of its (weight block, tile row) items one stage ahead
-// into rsc: (tid / 256, tid % 256), and, in a tile with extension rows (XT),
+// of the current stage's s: between P_{kb-1} and P_kb it is multiplied by
+// s_{kb-1} / s_kb (at the end of stage kb-1), and the epilogue multiplies by
+// the last s.  Each thread computes the factors of its (weight block, tile
+// row) items two stages ahead into rsc[stage % 2]: (tid / 256, tid % 256),
+// and, in a tile with extension rows (XT),
 // for threads 0..63 also an extension row (tid / 32, 256 + tid % 32) (the
 // others repeat their first item).  s_last receives the items' last s.
 struct ScaleItems {
@@ -247,46 +363,73 @@ __device__ __forceinline__ void fp8_mainloop(
   };
   constexpr int NI = XT ? 2 : 1;  // scale items per thread
   dma(0, 0);
+  // factors of stage 1 (1 if there is none), applied after stage 0's
+  // products; words of stage 2, for the factors of stage 2
   float s_prev[NI], sa_n[NI], sw_n[NI];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
-    s_prev[j] = it.sa[j][0] * it.sw[j][0];
-    // factors of stage 1, loaded a stage ahead of their use
-    sa_n[j] = it.sa[j][min(1, nkb - 1) * it.S];
-    sw_n[j] = it.sw[j][min(1, nkb - 1)];
-    rsc[0][it.blk[j]][it.row[j]] = 1.0f;
+    const float s0 = it.sa[j][0] * it.sw[j][0];
+    const float s1 = it.sa[j][min(1, nkb - 1) * it.S] * it.sw[j][min(1, nkb - 1)];
+    rsc[1][it.blk[j]][it.row[j]] = (nkb > 1) ? s0 / s1 : 1.0f;
+    s_prev[j] = (nkb > 1) ? s1 : s0;
+    sa_n[j] = it.sa[j][min(2, nkb - 1) * it.S];
+    sw_n[j] = it.sw[j][min(2, nkb - 1)];
   }
   __syncthreads();
   for (int kt = 0; kt < nkb; ++kt) {
     const int buf = kt & 1;
-    // buffer buf^1 and rsc[buf^1] were last read before the barrier that
-    // ended step kt-1
-    if (kt + 1 < nkb) dma(buf ^ 1, kt + 1);
-    // scale factors of stage kt+2 (consumed after the next barrier)
-    const int k2 = min(kt + 2, nkb - 1);
-    float sa2[NI], sw2[NI];
+    // buffer buf^1 was last read before the barrier that ended step kt-1;
+    // rsc[buf^1] holds the factors of stage kt+1, rsc[buf] (those of stage
+    // kt, read in step kt-1) takes those of stage kt+2 below
+    // copies of stage kt+1, spread between the products of the stage's first
+    // half (copy c: A region c/2 for even c, B region c/2 for odd c, the
+    // extension rows' region last): a compute unit's texture path takes
+    // about 64 bytes a cycle, and eight waves issuing all their copies at
+    // the top of the stage stall at issue
+    const bool more = kt + 1 < nkb;
+    auto copy = [&](int c) {
+      if (!more) return;
+      unsigned char* nb = &lds[buf ^ 1][0];
+      const int kb = kt + 1;
+      if (c < 2 * kLoads) {
+        const int i = c / 2, region = wave + 8 * i;
+        if (c % 2 == 0) {
+          if (a_ok[i]) dma16(a_src + (a_off[i] + kb * 128), nb + region * 1024);
+        } else {
+          dma16(wb + (b_off[i] + kb * 128), nb + kTileBytes + region * 1024);
+        }
+      } else if (x_ok) {
+        dma16(a_src + (x_off + kb * 128), nb + 2 * kTileBytes + wave * 1024);
+      }
+    };
+    // scale words of stage kt+3 (for the factors of kt+3, formed in step kt+1)
+    const int k3 = min(kt + 3, nkb - 1);
+    float sa3[NI], sw3[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      sa2[j] = it.sa[j][k2 * it.S];
-      sw2[j] = it.sw[j][k2];
+      sa3[j] = it.sa[j][k3 * it.S];
+      sw3[j] = it.sw[j][k3];
     }
     // no branch from here to the barrier, so the compiler keeps the
     // stage's reads next to the products that use them
     if (NF > 0)
       fp8_stage<NF, XT>(&lds[buf][0], &lds[buf][kTileBytes], &lds[buf][2 * kTileBytes],
-                        &rsc[buf][wn / 2][0], acc, accx, wm, fa);
+                        &rsc[buf ^ 1][wn / 2][0], acc, accx, wm, fa, copy);
+    else
+      for (int c = 0; c < 9; ++c) copy(c);
     // The factor arithmetic waits for its inputs with the wave's whole
     // vector-memory count, stage kt+1's copies included: keep it after the
     // products (the barrier below waits for those copies anyway).
     __builtin_amdgcn_sched_barrier(0);
-    // factors of stage kt+1 (after the last stage they land in an unused buffer)
+    // factors of stage kt+2 (1 past the last stage)
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const float s = sa_n[j] * sw_n[j];
-      rsc[buf ^ 1][it.blk[j]][it.row[j]] = s_prev[j] / s;
-      s_prev[j] = (kt + 1 < nkb) ? s : s_prev[j];
-      sa_n[j] = sa2[j];
-      sw_n[j] = sw2[j];
+      const bool real = kt + 2 < nkb;
+      rsc[buf][it.blk[j]][it.row[j]] = real ? s_prev[j] / s : 1.0f;
+      s_prev[j] = real ? s : s_prev[j];
+      sa_n[j] = sa3[j];
+      sw_n[j] = sw3[j];
     }
     __syncthreads();  // waits for this wave's loads, then for every wave
   }
@@ -582,7 +725,7 @@ __device__ __forceinline__ float mainloop(
     const int kn = kt + 2;
     if (kn < nkb) dma(st == 0 ? 2 : st - 1, kn);  // the buffer read in step kt-1
     if (NF > 0)
-      fp8_stage<NF, false>(&ring[st][0], &ring[st][kABytes], nullptr, &rsc[kt & 1][wn / 2][0],
+      fp8_stage_pre<NF, false>(&ring[st][0], &ring[st][kABytes], nullptr, &rsc[kt & 1][wn / 2][0],
                            acc, accx, 0, fa);
     __builtin_amdgcn_sched_barrier(0);
     // factors of block kt+1 from this stage's scale words; rsc[(kt+1) & 1]

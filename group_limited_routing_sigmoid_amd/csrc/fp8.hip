@@ -222,7 +222,7 @@ __device__ __forceinline__ void fp8_stage(const unsigned char* at, const unsigne
                                           const unsigned char* xt, const float* next,
                                           f32x16 (&acc)[4][2], f32x16& accx, int wm,
                                           const FragAddr& fa, Copy&& copy) {
-  {  // first 64-deep half: products, the next stage's copies between them
+  {  // first 64-deep half: products, the next stage's weight copies between them
     const i32x8 b0 = frag8(bt, fa.b_row, fa, 0, 0);
     const i32x8 b1 = frag8(bt, fa.b_row, fa, 1, 0);
     if (XT) {
@@ -237,17 +237,17 @@ __device__ __forceinline__ void fp8_stage(const unsigned char* at, const unsigne
       if (i + 1 < NF) an = frag8(at, fa.a_row, fa, i + 1, 0);
       acc[i][0] = mfma_fp8_32x32x64(a, b0, acc[i][0]);
       pin(acc[i][0]);
-      copy(2 * i);
+      copy(i);
       acc[i][1] = mfma_fp8_32x32x64(a, b1, acc[i][1]);
       pin(acc[i][1]);
-      copy(2 * i + 1);
       a = an;
     }
 #pragma unroll
-    for (int c = 2 * NF; c < 9; ++c) copy(c);
+    for (int c = NF; c < 4; ++c) copy(c);
   }
   fence();
-  {  // second half: products, fragment i-1's rescale beside fragment i's
+  {  // second half: products, fragment i-1's rescale and the next stage's
+     // token-row copies beside fragment i's
     const i32x8 b0 = frag8(bt, fa.b_row, fa, 0, 1);
     const i32x8 b1 = frag8(bt, fa.b_row, fa, 1, 1);
     if (XT) {
@@ -269,6 +269,7 @@ __device__ __forceinline__ void fp8_stage(const unsigned char* at, const unsigne
       }
       acc[i][1] = mfma_fp8_32x32x64(a, b1, acc[i][1]);
       pin(acc[i][1]);
+      copy(4 + i);
       if (i > 0) {
         mul_factors(acc[i - 1][1], t);
         pin(acc[i - 1][1]);
@@ -278,6 +279,8 @@ __device__ __forceinline__ void fp8_stage(const unsigned char* at, const unsigne
       fence();
       a = an;
     }
+#pragma unroll
+    for (int c = 4 + NF; c < 9; ++c) copy(c);
     if (NF > 0) {
       mul_factors(acc[NF - 1][0], t);
       pin(acc[NF - 1][0]);
@@ -381,23 +384,24 @@ __device__ __forceinline__ void fp8_mainloop(
     // buffer buf^1 was last read before the barrier that ended step kt-1;
     // rsc[buf^1] holds the factors of stage kt+1, rsc[buf] (those of stage
     // kt, read in step kt-1) takes those of stage kt+2 below
-    // copies of stage kt+1, spread between the products of the stage's first
-    // half (copy c: A region c/2 for even c, B region c/2 for odd c, the
-    // extension rows' region last): a compute unit's texture path takes
-    // about 64 bytes a cycle, and eight waves issuing all their copies at
-    // the top of the stage stall at issue
+    // copies of stage kt+1, spread over the stage's products (copies 0-3:
+    // the wave's weight regions, one beside every other product of the first
+    // half, so the bytes from HBM get the longest lead; 4-7: its token-row
+    // regions, which the L2 mostly holds, beside the second half's; 8: the
+    // extension rows' region): a compute unit's texture path takes about 64
+    // bytes a cycle, and eight waves issuing all their copies at the top of
+    // the stage stall at issue (measured at 8K tokens, gate/up: 2.56 ms with
+    // the burst, 2.43 with every copy in the first half, 2.37 split so)
     const bool more = kt + 1 < nkb;
     auto copy = [&](int c) {
       if (!more) return;
       unsigned char* nb = &lds[buf ^ 1][0];
       const int kb = kt + 1;
-      if (c < 2 * kLoads) {
-        const int i = c / 2, region = wave + 8 * i;
-        if (c % 2 == 0) {
-          if (a_ok[i]) dma16(a_src + (a_off[i] + kb * 128), nb + region * 1024);
-        } else {
-          dma16(wb + (b_off[i] + kb * 128), nb + kTileBytes + region * 1024);
-        }
+      if (c < kLoads) {
+        dma16(wb + (b_off[c] + kb * 128), nb + kTileBytes + (wave + 8 * c) * 1024);
+      } else if (c < 2 * kLoads) {
+        const int i = c - kLoads;
+        if (a_ok[i]) dma16(a_src + (a_off[i] + kb * 128), nb + (wave + 8 * i) * 1024);
       } else if (x_ok) {
         dma16(a_src + (x_off + kb * 128), nb + 2 * kTileBytes + wave * 1024);
       }

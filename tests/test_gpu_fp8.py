@@ -133,6 +133,22 @@ def test_fp8_128_row_tiles(T, hidden, skew):
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("hidden,intermediate", [(128, 128), (256, 128), (128, 256)])
+def test_fp8_one_and_two_blocks(hidden, intermediate):
+    # products only one or two 128-deep blocks deep (gate/up K = hidden, down
+    # K = intermediate): the rescale pipeline's first and last stages meet;
+    # 256-row tiles (with extended last tiles) and 128-row tiles against the
+    # oracle, and bit-identical to each other
+    sh = small_shape(hidden=hidden, intermediate=intermediate)
+    T = 2100
+    inp = make_inputs(WORKLOADS["fp8_8k"], device=device(), tokens=T, shape=sh,
+                      seed=90 + hidden + intermediate)
+    rows = np.arange(0, T, 7)
+    a, _ = _check(inp, sh, rows, f"fp8 256-row tiles H={hidden} I={intermediate}", gl.TILE_160)
+    b, _ = _check(inp, sh, rows, f"fp8 128-row tiles H={hidden} I={intermediate}", gl.TILE_128)
+    assert torch.equal(a, b)
+
+
 def test_fp8_max_tokens_sampled():
     # the largest batch the boundary accepts for the Beam layer (T = 52,428:
     # 419,424 slots, the slot-major scale words up to block 39), sampled rows

@@ -190,14 +190,15 @@ __device__ __forceinline__ void fence() {
 // products are pure computations the compiler would otherwise move freely).
 __device__ __forceinline__ void pin(f32x16& v) { asm volatile("" : "+v"(v)); }
 
-// acc[i][n] *= t[row of element] for the 16 rows fragment i holds in this
-// lane, t: those rows' factors (four 16-byte reads of the factor table).
+// t: the factors (per-row rescale ratios) of the 16 rows fragment i holds
+// in this lane, four 16-byte reads of the factor table v.
 __device__ __forceinline__ void read_factors(f32x4 (&t)[4], int i, const float* v,
                                              const FragAddr& fa) {
   const unsigned char* base = reinterpret_cast<const unsigned char*>(v) + fa.r_row;
 #pragma unroll
   for (int q = 0; q < 4; ++q) t[q] = *reinterpret_cast<const f32x4*>(base + (i * 32 + 8 * q) * 4);
 }
+// a *= t[row of element] for one 32x32 accumulator of that fragment.
 __device__ __forceinline__ void mul_factors(f32x16& a, const f32x4 (&t)[4]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q)
@@ -306,9 +307,9 @@ __device__ __forceinline__ void fp8_stage(const unsigned char* at, const unsigne
 // i.e. columns wn*64 + wm*32 .. +32, into accx.
 template <int NF, bool XT>
 __device__ __forceinline__ void fp8_stage_pre(const unsigned char* at, const unsigned char* bt,
-                                          const unsigned char* xt, const float* ratio,
-                                          f32x16 (&acc)[4][2], f32x16& accx, int wm,
-                                          const FragAddr& fa) {
+                                              const unsigned char* xt, const float* ratio,
+                                              f32x16 (&acc)[4][2], f32x16& accx, int wm,
+                                              const FragAddr& fa) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const i32x8 b0 = frag8(bt, fa.b_row, fa, 0, h);
@@ -383,8 +384,9 @@ __device__ __forceinline__ void fp8_mainloop(
     const int buf = kt & 1;
     // buffer buf^1 was last read before the barrier that ended step kt-1;
     // rsc[buf^1] holds the factors of stage kt+1, rsc[buf] (those of stage
-    // kt, read in step kt-1) takes those of stage kt+2 below
-    // copies of stage kt+1, spread over the stage's products (copies 0-3:
+    // kt, read in step kt-1) takes those of stage kt+2 below.
+    //
+    // Copies of stage kt+1, spread over the stage's products (copies 0-3:
     // the wave's weight regions, one beside every other product of the first
     // half, so the bytes from HBM get the longest lead; 4-7: its token-row
     // regions, which the L2 mostly holds, beside the second half's; 8: the
@@ -729,8 +731,8 @@ __device__ __forceinline__ float mainloop(
     const int kn = kt + 2;
     if (kn < nkb) dma(st == 0 ? 2 : st - 1, kn);  // the buffer read in step kt-1
     if (NF > 0)
-      fp8_stage_pre<NF, false>(&ring[st][0], &ring[st][kABytes], nullptr, &rsc[kt & 1][wn / 2][0],
-                           acc, accx, 0, fa);
+      fp8_stage_pre<NF, false>(&ring[st][0], &ring[st][kABytes], nullptr,
+                               &rsc[kt & 1][wn / 2][0], acc, accx, 0, fa);
     __builtin_amdgcn_sched_barrier(0);
     // factors of block kt+1 from this stage's scale words; rsc[(kt+1) & 1]
     // was last read in step kt-1
